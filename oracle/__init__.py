@@ -1,0 +1,174 @@
+"""CPU oracle for causal grouped-query attention — test infrastructure only.
+
+Only the tests, the smoke check and the benchmark's CPU-baseline leg may import this package.
+It wraps liboracle.so (plain C, fa_oracle.c), which computes the plain definition
+O = softmax(scale * Q K^T + causal mask) V as an explicit f32 matmul + softmax + matmul
+(mlxcel PR #2306, commit message 2; mi210-llm-stack build guide, Verification). It shares no
+code with the HIP path and never calls it.
+
+Argument conventions: q is [B, Sq, Hq, D] as numpy float16 (f16) or uint16 bit patterns
+(bf16); k and v are [B, Sk, Hkv, D] in the same way, or uint8 [B, Sk, Hkv, D/32*18] q4_0
+blocks. Results are float32.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import numpy as np
+
+from . import build as _build
+
+F16, BF16, Q4_0 = 0, 1, 2
+_CODES = {"f16": F16, "bf16": BF16, "q4_0": Q4_0}
+
+
+def _code(dtype) -> int:
+    return _CODES[dtype] if isinstance(dtype, str) else int(dtype)
+
+
+def _ptr(a: np.ndarray) -> int:
+    return a.ctypes.data
+
+
+def _c(a: np.ndarray) -> np.ndarray:
+    return np.ascontiguousarray(a)
+
+
+def _shapes(q, k, kv_dtype):
+    B, Sq, Hq, D = q.shape
+    Bk, Sk, Hkv = k.shape[:3]
+    if Bk != B:
+        raise ValueError("q and k batch sizes disagree")
+    if _code(kv_dtype) == Q4_0:
+        if D % 32 or k.shape[3] != D // 32 * 18:
+            raise ValueError("q4_0 rows must hold D/32 blocks of 18 bytes")
+    elif k.shape[3] != D:
+        raise ValueError("k head dim disagrees with q")
+    return B, Sq, Hq, Sk, Hkv, D
+
+
+class Oracle:
+    """The oracle functions bound to one build of fa_oracle.c."""
+
+    def __init__(self, path: str):
+        lib = ctypes.CDLL(path)
+        i64, i32, f32, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_float, ctypes.c_void_p
+        lib.orc_attention.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, i32,
+                                      i64, f32, vp, i64, vp, i32]
+        lib.orc_probs.argtypes = [vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, i32, i64,
+                                  f32, i64, vp]
+        lib.orc_dequant_q4_0.argtypes = [vp, i64, vp, vp]
+        lib.orc_half_to_float.argtypes = [vp, i64, vp]
+        lib.orc_float_to_half.argtypes = [vp, i64, vp]
+        for fn in (lib.orc_attention, lib.orc_probs, lib.orc_dequant_q4_0,
+                   lib.orc_half_to_float, lib.orc_float_to_half):
+            fn.restype = i32
+        self.path = path
+        self.lib = lib
+
+    def attention(self, q: np.ndarray, k: np.ndarray, v: np.ndarray, *, q_dtype, kv_dtype,
+                  causal: bool = True, offset: Optional[int] = None,
+                  scale: Optional[float] = None, rows: Optional[Sequence[int]] = None,
+                  threads: int = 0) -> np.ndarray:
+        """Attention output in float32.
+
+        Without `rows` the result has q's [B, Sq, Hq, D] shape. With `rows` (flattened indices
+        (b * Sq + i) * Hq + h) the result is [len(rows), D]. offset defaults to Sk - Sq and
+        scale to 1/sqrt(D).
+        """
+        q, k, v = _c(q), _c(k), _c(v)
+        B, Sq, Hq, Sk, Hkv, D = _shapes(q, k, kv_dtype)
+        if v.shape != k.shape:
+            raise ValueError("k and v shapes differ")
+        offset = Sk - Sq if offset is None else int(offset)
+        scale = 1.0 / np.sqrt(D) if scale is None else float(scale)
+        if rows is None:
+            out = np.empty((B, Sq, Hq, D), np.float32)
+            n_rows, rptr = B * Sq * Hq, None
+        else:
+            rows_arr = np.ascontiguousarray(np.asarray(rows, dtype=np.int64).reshape(-1))
+            n_rows = rows_arr.size
+            out = np.empty((n_rows, D), np.float32)
+            rptr = _ptr(rows_arr)
+        rc = self.lib.orc_attention(_ptr(q), _ptr(k), _ptr(v), _code(q_dtype), _code(kv_dtype),
+                                    B, Hq, Hkv, Sq, Sk, D, int(bool(causal)), offset, scale,
+                                    rptr, n_rows, _ptr(out), int(threads))
+        if rc:
+            raise ValueError(f"oracle rejected the arguments (code {rc})")
+        return out
+
+    def probs(self, q: np.ndarray, k: np.ndarray, *, q_dtype, kv_dtype, row: int,
+              causal: bool = True, offset: Optional[int] = None,
+              scale: Optional[float] = None) -> np.ndarray:
+        """Softmax probabilities of one flattened query row over all Sk keys (float32 [Sk])."""
+        q, k = _c(q), _c(k)
+        B, Sq, Hq, Sk, Hkv, D = _shapes(q, k, kv_dtype)
+        offset = Sk - Sq if offset is None else int(offset)
+        scale = 1.0 / np.sqrt(D) if scale is None else float(scale)
+        out = np.empty(Sk, np.float32)
+        rc = self.lib.orc_probs(_ptr(q), _ptr(k), _code(q_dtype), _code(kv_dtype), B, Hq, Hkv,
+                                Sq, Sk, D, int(bool(causal)), offset, scale, int(row), _ptr(out))
+        if rc:
+            raise ValueError(f"oracle rejected the arguments (code {rc})")
+        return out
+
+    def dequant_q4_0(self, blocks: np.ndarray):
+        """q4_0 blocks (uint8, 18 bytes each) -> (float32 values, f16 bit patterns)."""
+        blocks = _c(np.asarray(blocks, dtype=np.uint8))
+        if blocks.size % 18:
+            raise ValueError("q4_0 data must be whole 18-byte blocks")
+        n = blocks.size // 18
+        f32 = np.empty(n * 32, np.float32)
+        f16 = np.empty(n * 32, np.uint16)
+        if self.lib.orc_dequant_q4_0(_ptr(blocks), n, _ptr(f32), _ptr(f16)):
+            raise ValueError("oracle rejected the arguments")
+        return f32, f16
+
+    def half_to_float(self, bits: np.ndarray) -> np.ndarray:
+        bits = _c(np.asarray(bits, dtype=np.uint16))
+        out = np.empty(bits.shape, np.float32)
+        if self.lib.orc_half_to_float(_ptr(bits), bits.size, _ptr(out)):
+            raise ValueError("bad arguments")
+        return out
+
+    def float_to_half(self, x: np.ndarray) -> np.ndarray:
+        x = _c(np.asarray(x, dtype=np.float32))
+        out = np.empty(x.shape, np.uint16)
+        if self.lib.orc_float_to_half(_ptr(x), x.size, _ptr(out)):
+            raise ValueError("bad arguments")
+        return out
+
+
+_default: Optional[Oracle] = None
+
+
+def default() -> Oracle:
+    """The oracle built from fa_oracle.c (built on first use if no build exists)."""
+    global _default
+    if _default is None:
+        if not os.path.exists(_build.LIB):
+            _build.build()
+        _default = Oracle(_build.LIB)
+    return _default
+
+
+def attention(*a, **kw):
+    return default().attention(*a, **kw)
+
+
+def probs(*a, **kw):
+    return default().probs(*a, **kw)
+
+
+def dequant_q4_0(*a, **kw):
+    return default().dequant_q4_0(*a, **kw)
+
+
+def half_to_float(*a, **kw):
+    return default().half_to_float(*a, **kw)
+
+
+def float_to_half(*a, **kw):
+    return default().float_to_half(*a, **kw)
