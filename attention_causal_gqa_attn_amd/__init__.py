@@ -1,0 +1,200 @@
+"""Causal grouped-query flash attention for AMD Instinct MI355X (gfx950).
+
+Thin Python binding of libfa.so, whose C ABI is include/fa.h. This module only marshals
+arguments: torch tensors become device pointers and sizes, torch's current HIP stream becomes
+the stream argument, and a non-zero status becomes an FAError. Every step of the attention
+runs in the HIP kernels of libfa.so; there is no Python or CPU fallback, and if the library is
+missing every call raises.
+
+Raw entry points with the C names (pointers and ints): fa_prefill, fa_decode,
+fa_decode_workspace_bytes, fa_dequant_q4_0, fa_strerror, fa_version.
+Tensor helpers: prefill, decode, decode_workspace_bytes, dequant_q4_0.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
+
+FA_KV_F16, FA_KV_BF16, FA_KV_Q4_0 = 0, 1, 2
+Q4_0_BYTES = 18
+
+FA_OK = 0
+FA_ERR_NULL = -1
+FA_ERR_SHAPE = -2
+FA_ERR_DTYPE = -3
+FA_ERR_UNSUPPORTED = -4
+FA_ERR_WORKSPACE = -5
+FA_ERR_ALIGN = -6
+FA_ERR_HIP = -7
+FA_ERR_VALUE = -8
+
+EXPORTS = ("fa_prefill", "fa_decode", "fa_decode_workspace_bytes", "fa_dequant_q4_0",
+           "fa_strerror", "fa_version")
+
+
+class FAError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where}: {fa_strerror(code)} (status {code})")
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load libfa.so (once). Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run "
+                               "`python -m attention_causal_gqa_attn_amd.build` first")
+        lib = ctypes.CDLL(LIB_PATH)
+        i32, i64, f32, vp, sz = (ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p,
+                                 ctypes.c_size_t)
+        attn = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i64, f32, i32]
+        lib.fa_prefill.argtypes = attn + [vp]
+        lib.fa_prefill.restype = i32
+        lib.fa_decode.argtypes = attn + [vp, sz, vp]
+        lib.fa_decode.restype = i32
+        lib.fa_decode_workspace_bytes.argtypes = [i32] * 6
+        lib.fa_decode_workspace_bytes.restype = sz
+        lib.fa_dequant_q4_0.argtypes = [vp, i64, vp, vp, vp]
+        lib.fa_dequant_q4_0.restype = i32
+        lib.fa_strerror.argtypes = [i32]
+        lib.fa_strerror.restype = ctypes.c_char_p
+        lib.fa_version.argtypes = []
+        lib.fa_version.restype = i32
+        _lib = lib
+    return _lib
+
+
+# ---- raw C entry points ---------------------------------------------------------------------
+
+def fa_prefill(q, k, v, o, B, Hq, Hkv, Sq, Sk, D, causal, causal_offset, scale, kv_dtype,
+               stream) -> int:
+    return load().fa_prefill(q, k, v, o, B, Hq, Hkv, Sq, Sk, D, causal, causal_offset, scale,
+                             kv_dtype, stream)
+
+
+def fa_decode(q, k, v, o, B, Hq, Hkv, Sq, Sk, D, causal, causal_offset, scale, kv_dtype,
+              workspace, workspace_bytes, stream) -> int:
+    return load().fa_decode(q, k, v, o, B, Hq, Hkv, Sq, Sk, D, causal, causal_offset, scale,
+                            kv_dtype, workspace, workspace_bytes, stream)
+
+
+def fa_decode_workspace_bytes(B, Hq, Hkv, Sq, Sk, D) -> int:
+    return load().fa_decode_workspace_bytes(B, Hq, Hkv, Sq, Sk, D)
+
+
+def fa_dequant_q4_0(blocks, n_blocks, out_f32, out_f16, stream) -> int:
+    return load().fa_dequant_q4_0(blocks, n_blocks, out_f32, out_f16, stream)
+
+
+def fa_strerror(code: int) -> str:
+    return load().fa_strerror(code).decode()
+
+
+def fa_version() -> int:
+    return load().fa_version()
+
+
+# ---- tensor helpers -------------------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _kv_code(k) -> int:
+    torch = _torch()
+    if k.dtype == torch.float16:
+        return FA_KV_F16
+    if k.dtype == torch.bfloat16:
+        return FA_KV_BF16
+    if k.dtype == torch.uint8:
+        return FA_KV_Q4_0
+    raise TypeError(f"unsupported K/V dtype {k.dtype}")
+
+
+def _stream(t, stream) -> int:
+    if stream is not None:
+        return int(stream.cuda_stream if hasattr(stream, "cuda_stream") else stream)
+    return int(_torch().cuda.current_stream(t.device).cuda_stream)
+
+
+def _sizes(q, k, v, kv):
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be 4-d: [B, S, H, D] (q4_0: [B, S, H, D/32*18] bytes)")
+    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
+        raise ValueError("q, k, v must be contiguous")
+    if k.shape != v.shape:
+        raise ValueError("k and v shapes differ")
+    B, Sq, Hq, D = q.shape
+    Bk, Sk, Hkv, Dk = k.shape
+    if Bk != B:
+        raise ValueError("batch sizes differ")
+    want = D // 32 * Q4_0_BYTES if kv == FA_KV_Q4_0 else D
+    if Dk != want:
+        raise ValueError(f"k/v last dim {Dk}, expected {want}")
+    return B, Hq, Hkv, Sq, Sk, D
+
+
+def prefill(q, k, v, *, causal: bool = True, offset: Optional[int] = None,
+            scale: Optional[float] = None, out=None, stream=None):
+    """O = softmax(scale * Q K^T + causal mask) V via fa_prefill. K/V dtype selects the cache
+    type (float16, bfloat16, or uint8 q4_0 blocks). offset defaults to Sk - Sq."""
+    kv = _kv_code(k)
+    B, Hq, Hkv, Sq, Sk, D = _sizes(q, k, v, kv)
+    offset = Sk - Sq if offset is None else int(offset)
+    scale = D ** -0.5 if scale is None else float(scale)
+    if out is None:
+        out = _torch().empty_like(q)
+    rc = fa_prefill(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, Hq, Hkv, Sq,
+                    Sk, D, int(bool(causal)), offset, scale, kv, _stream(q, stream))
+    if rc != FA_OK:
+        raise FAError(rc, "fa_prefill")
+    return out
+
+
+def decode_workspace_bytes(B, Hq, Hkv, Sq, Sk, D) -> int:
+    return fa_decode_workspace_bytes(B, Hq, Hkv, Sq, Sk, D)
+
+
+def decode(q, k, v, *, causal: bool = True, offset: Optional[int] = None,
+           scale: Optional[float] = None, out=None, workspace=None, stream=None):
+    """Split-K decode via fa_decode (Sq * Hq / Hkv <= 16). A workspace tensor of
+    decode_workspace_bytes(...) bytes is allocated when none is given."""
+    torch = _torch()
+    kv = _kv_code(k)
+    B, Hq, Hkv, Sq, Sk, D = _sizes(q, k, v, kv)
+    offset = Sk - Sq if offset is None else int(offset)
+    scale = D ** -0.5 if scale is None else float(scale)
+    if out is None:
+        out = torch.empty_like(q)
+    if workspace is None:
+        nbytes = decode_workspace_bytes(B, Hq, Hkv, Sq, Sk, D)
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    rc = fa_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, Hq, Hkv, Sq, Sk,
+                   D, int(bool(causal)), offset, scale, kv, workspace.data_ptr(),
+                   workspace.numel() * workspace.element_size(), _stream(q, stream))
+    if rc != FA_OK:
+        raise FAError(rc, "fa_decode")
+    return out
+
+
+def dequant_q4_0(blocks, stream=None):
+    """q4_0 blocks (uint8 device tensor, 18 bytes each) -> (float32 values, float16 values)."""
+    torch = _torch()
+    if blocks.dtype != torch.uint8 or not blocks.is_contiguous() or blocks.numel() % 18:
+        raise ValueError("blocks must be a contiguous uint8 tensor of whole 18-byte blocks")
+    n = blocks.numel() // 18
+    f32 = torch.empty(n * 32, dtype=torch.float32, device=blocks.device)
+    f16 = torch.empty(n * 32, dtype=torch.float16, device=blocks.device)
+    rc = fa_dequant_q4_0(blocks.data_ptr(), n, f32.data_ptr(), f16.data_ptr(),
+                         _stream(blocks, stream))
+    if rc != FA_OK:
+        raise FAError(rc, "fa_dequant_q4_0")
+    return f32, f16

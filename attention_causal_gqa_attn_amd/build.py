@@ -1,0 +1,73 @@
+"""Build libfa.so (the HIP kernels and the C ABI of include/fa.h) for gfx950, in-tree.
+
+    python -m attention_causal_gqa_attn_amd.build          # or build() from Python
+
+Every source is compiled with hipcc --offload-arch=gfx950 -O3, with the packed-FP32 VALU
+forms disabled (-Xclang -target-feature -Xclang -packed-fp32-ops); the objects are linked into
+attention_causal_gqa_attn_amd/libfa.so next to this file.
+"""
+from __future__ import annotations
+
+import concurrent.futures
+import os
+import shutil
+import subprocess
+import sys
+import tempfile
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+LIB = os.path.join(HERE, "libfa.so")
+SOURCES = ["fa_api.cpp", "fa_prefill.hip", "fa_decode.hip", "fa_dequant.hip"]
+ARCH = "gfx950"
+
+COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
+          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-Wall", "-Wno-unused-function"]
+
+
+def _hipcc() -> str:
+    path = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(path):
+        raise RuntimeError("hipcc not found (ROCm is required to build libfa.so)")
+    return path
+
+
+def _quiet(out: str) -> str:
+    # the host pass does not know the packed-fp32 feature and says so: harmless
+    return "\n".join(l for l in out.splitlines() if "packed-fp32-ops" not in l)
+
+
+def build(verbose: bool = False, extra_flags=()) -> str:
+    hipcc = _hipcc()
+    with tempfile.TemporaryDirectory(prefix="fa_build_") as tmp:
+        def compile_one(src):
+            obj = os.path.join(tmp, os.path.splitext(src)[0] + ".o")
+            cmd = [hipcc, *COMMON, *extra_flags, "-c", os.path.join(CSRC, src), "-o", obj]
+            if src.endswith(".cpp"):
+                cmd[1:1] = ["-x", "hip"]
+            r = subprocess.run(cmd, capture_output=True, text=True)
+            msg = _quiet(r.stdout + r.stderr)
+            if r.returncode != 0:
+                raise RuntimeError(f"hipcc failed on {src}:\n{' '.join(cmd)}\n{msg}")
+            if verbose and msg.strip():
+                print(msg, flush=True)
+            return obj
+
+        with concurrent.futures.ThreadPoolExecutor(max_workers=min(4, len(SOURCES))) as ex:
+            objs = list(ex.map(compile_one, SOURCES))
+        out = os.path.join(tmp, "libfa.so")
+        cmd = [hipcc, "-shared", f"--offload-arch={ARCH}", *objs, "-o", out]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{_quiet(r.stdout + r.stderr)}")
+        shutil.copyfile(out, LIB + ".tmp")
+        os.replace(LIB + ".tmp", LIB)
+    if verbose:
+        print(f"built {LIB}", flush=True)
+    return LIB
+
+
+if __name__ == "__main__":
+    build(verbose=True)
+    sys.exit(0)

@@ -1,0 +1,189 @@
+// C ABI of libfa.so (declared in include/fa.h): argument validation, then one kernel launch
+// (prefill) or two (decode: split + merge) on the caller's stream. Every check runs before
+// the first HIP call, so a rejected call has launched nothing; the library allocates nothing.
+#include <cmath>
+#include <cstdint>
+
+#include "../../include/fa.h"
+#include "fa_kernels.h"
+
+namespace {
+
+constexpr int kVersion = 1 * 10000 + 0 * 100 + 0;
+constexpr int64_t kMaxWorkgroups = (int64_t)UINT32_MAX / 256;   // 256-thread workgroups
+
+bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+// a * b * c * d without int64 overflow (all >= 0); -1 on overflow.
+int64_t mul4(int64_t a, int64_t b, int64_t c, int64_t d)
+{
+    const int64_t lim = INT64_MAX / 4;
+    int64_t r = a;
+    for (int64_t x : {b, c, d}) {
+        if (x != 0 && r > lim / x)
+            return -1;
+        r *= x;
+    }
+    return r;
+}
+
+// Shared checks of fa_prefill / fa_decode. Fills `a` on success.
+int check_attention(const void *q, const void *k, const void *v, void *o, int B, int Hq, int Hkv,
+                    int Sq, int Sk, int D, int causal, int64_t offset, float scale, int kv_dtype,
+                    fa::AttnArgs &a)
+{
+    if (kv_dtype != FA_KV_F16 && kv_dtype != FA_KV_BF16 && kv_dtype != FA_KV_Q4_0)
+        return FA_ERR_DTYPE;
+    if (B < 0 || Sq < 0 || Sk < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || Hq % Hkv != 0)
+        return FA_ERR_SHAPE;
+    if (D != 64 && D != 128)
+        return FA_ERR_UNSUPPORTED;
+    if (!(std::isfinite(scale) && scale > 0.0f))
+        return FA_ERR_VALUE;
+    const int64_t nq = mul4(B, Sq, Hq, D);
+    const int64_t nk = mul4(B, Sk, Hkv, D);
+    if (nq < 0 || nk < 0 || Sk > INT32_MAX - 2 * 64)
+        return FA_ERR_SHAPE;
+    if ((nq > 0 && (!q || !o)) || (nk > 0 && (!k || !v)))
+        return FA_ERR_NULL;
+    const uintptr_t kv_align = kv_dtype == FA_KV_Q4_0 ? 4 : 16;
+    if (!aligned(q, 16) || !aligned(o, 16) || !aligned(k, kv_align) || !aligned(v, kv_align))
+        return FA_ERR_ALIGN;
+
+    // offsets beyond these bounds change nothing: every key visible, or none
+    if (offset > (int64_t)Sk)
+        offset = Sk;
+    if (offset < -(int64_t)Sq - 1)
+        offset = -(int64_t)Sq - 1;
+
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.o = o;
+    a.B = B;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.Sq = Sq;
+    a.Sk = Sk;
+    a.D = D;
+    a.G = Hq / Hkv;
+    a.kv = kv_dtype;
+    a.causal = causal ? 1 : 0;
+    a.offset = offset;
+    a.c = scale * 1.4426950408889634f;
+    return FA_OK;
+}
+
+int64_t visible_end(int Sq, int Sk, int causal, int64_t offset)
+{
+    if (!causal)
+        return Sk;
+    int64_t e = (int64_t)Sq - 1 + offset + 1;
+    if (e > Sk)
+        e = Sk;
+    return e < 0 ? 0 : e;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int fa_prefill(const void *q, const void *k, const void *v, void *o, int B, int Hq, int Hkv,
+               int Sq, int Sk, int D, int causal, int64_t causal_offset, float scale,
+               int kv_dtype, fa_stream_t stream)
+{
+    fa::AttnArgs a;
+    const int rc = check_attention(q, k, v, o, B, Hq, Hkv, Sq, Sk, D, causal, causal_offset,
+                                   scale, kv_dtype, a);
+    if (rc != FA_OK)
+        return rc;
+    if ((int64_t)B * Sq == 0)
+        return FA_OK;
+    if (fa::prefill_grid(a).n_wg > kMaxWorkgroups)
+        return FA_ERR_UNSUPPORTED;
+    return hip_status(fa::launch_prefill(a, (hipStream_t)stream));
+}
+
+size_t fa_decode_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Sk, int D)
+{
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || Sq <= 0 || Sk < 0 || Hq % Hkv != 0 ||
+        (D != 64 && D != 128))
+        return 0;
+    // the largest split count any causal offset can produce for these sizes
+    return fa::decode_grid(B, Hq, Hkv, Sq, Sk, D, /*kend=*/Sk, /*bound=*/true).workspace_bytes;
+}
+
+int fa_decode(const void *q, const void *k, const void *v, void *o, int B, int Hq, int Hkv,
+              int Sq, int Sk, int D, int causal, int64_t causal_offset, float scale, int kv_dtype,
+              void *workspace, size_t workspace_bytes, fa_stream_t stream)
+{
+    fa::AttnArgs a;
+    const int rc = check_attention(q, k, v, o, B, Hq, Hkv, Sq, Sk, D, causal, causal_offset,
+                                   scale, kv_dtype, a);
+    if (rc != FA_OK)
+        return rc;
+    if ((int64_t)(Hq / Hkv) * Sq > 16)
+        return FA_ERR_UNSUPPORTED;
+    if ((int64_t)B * Sq == 0)
+        return FA_OK;
+    const fa::DecodeGrid g = fa::decode_grid(B, Hq, Hkv, Sq, Sk, D,
+                                             visible_end(Sq, Sk, a.causal, a.offset), false);
+    if (g.n_wg > kMaxWorkgroups)
+        return FA_ERR_UNSUPPORTED;
+    if (g.workspace_bytes > 0) {
+        if (!workspace || workspace_bytes < g.workspace_bytes)
+            return FA_ERR_WORKSPACE;
+        if (!aligned(workspace, 16))
+            return FA_ERR_ALIGN;
+    }
+    return hip_status(fa::launch_decode(a, g, workspace, (hipStream_t)stream));
+}
+
+int fa_dequant_q4_0(const void *blocks, int64_t n_blocks, float *out_f32, void *out_f16,
+                    fa_stream_t stream)
+{
+    if (n_blocks < 0 || n_blocks > INT64_MAX / 64)
+        return FA_ERR_SHAPE;
+    if (n_blocks == 0)
+        return FA_OK;
+    if (!blocks || (!out_f32 && !out_f16))
+        return FA_ERR_NULL;
+    if (!aligned(blocks, 2) || !aligned(out_f32, 4) || !aligned(out_f16, 4))
+        return FA_ERR_ALIGN;
+    if ((n_blocks + 255) / 256 > kMaxWorkgroups)
+        return FA_ERR_UNSUPPORTED;
+    return hip_status(fa::launch_dequant_q4_0(blocks, n_blocks, out_f32, out_f16,
+                                              (hipStream_t)stream));
+}
+
+const char *fa_strerror(int code)
+{
+    switch (code) {
+    case FA_OK:
+        return "ok";
+    case FA_ERR_NULL:
+        return "a required pointer is NULL";
+    case FA_ERR_SHAPE:
+        return "invalid sizes (negative, Hq not a multiple of Hkv, or too large)";
+    case FA_ERR_DTYPE:
+        return "unknown kv_dtype";
+    case FA_ERR_UNSUPPORTED:
+        return "unsupported combination (head dim not 64 or 128, decode rows > 16, grid too large)";
+    case FA_ERR_WORKSPACE:
+        return "decode workspace missing or too small";
+    case FA_ERR_ALIGN:
+        return "misaligned pointer (16 bytes; q4_0 K/V 4 bytes)";
+    case FA_ERR_HIP:
+        return "HIP runtime error at launch";
+    case FA_ERR_VALUE:
+        return "scale must be finite and positive";
+    default:
+        return "unknown status code";
+    }
+}
+
+int fa_version(void) { return kVersion; }
+
+}  // extern "C"

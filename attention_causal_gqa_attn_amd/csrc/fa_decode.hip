@@ -1,0 +1,298 @@
+// Decode kernels: split-K attention for few query rows per KV head, then a log-sum-exp merge.
+//
+// The rows of one KV head (its G query heads times Sq query tokens, at most 16) share every
+// K/V element, so a workgroup streams one range of keys ("split") of one (b, KV head) through
+// LDS once and computes all rows against it. Many splits run at once to keep HBM busy; each
+// writes its partial softmax state (frame f, sum l, unnormalised output row) and a second
+// kernel combines the splits of a row:
+//     F = max_s f_s,   L = sum_s l_s 2^(f_s - F),   O = sum_s O_s 2^(f_s - F) / L
+// (log2 units). A q4_0 cache is dequantized on the way into LDS by the same tile loader as
+// the prefill kernel.
+//
+// Inside a workgroup the 4 waves take 16 keys each of every 64-key tile:
+//   S^T[16 keys][16 rows] = v_mfma_f32_16x16x32 (K from LDS, Q^T in registers);
+//   the C layout puts 4 consecutive keys of one row in a lane, which is exactly the B operand
+//   of v_mfma_f32_16x16x16 for O^T[16 d][16 rows] += V^T[16 d][16 keys] P^T;
+//   each wave keeps its own deferred softmax frame per row (rescale only past the margin),
+//   and the 4 waves' states are combined through LDS at the end of the split.
+#include "fa_kernels.h"
+#include "fa_tiles.h"
+
+namespace fa {
+
+namespace {
+
+struct DecodeParams {
+    AttnArgs a;
+    int rows, n_split, split_len;
+    int64_t kend;          // keys any row can see: [0, kend)
+    float *part;           // [B][Hkv][n_split][rows][D + 2]
+};
+
+template <int D, int KV>
+__global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeParams p)
+{
+    constexpr bool BF = (KV == KV_BF16);
+    using Geo = TileGeom<D>;
+    constexpr int kLdsElems = 2 * Geo::stage > 4 * 16 * D * 2 + 256 ? 2 * Geo::stage
+                                                                      : 4 * 16 * D * 2 + 256;
+    __shared__ __attribute__((aligned(16))) uint16_t lds[kLdsElems];
+
+    const AttnArgs &a = p.a;
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int quad = lane >> 4, r = lane & 15;     // C layout: keys 4*quad + i, row r
+
+    int rest = xcd_remap(blockIdx.x, gridDim.x);
+    const int s = rest % p.n_split;
+    rest /= p.n_split;
+    const int kvh = rest % a.Hkv;
+    const int b = rest / a.Hkv;
+
+    const int64_t ks = (int64_t)s * p.split_len;
+    const int64_t ke = min(ks + p.split_len, p.kend);
+    const int nb = ke > ks ? (int)((ke - ks + kBN - 1) / kBN) : 0;
+
+    // row r = qi * G + hl; rows >= p.rows are padding
+    const bool row_on = r < p.rows;
+    const int qi = row_on ? r / a.G : 0;
+    const int hl = row_on ? r % a.G : 0;
+    const int h = kvh * a.G + hl;
+    int64_t rowlim = ke - 1;                        // last key this row may see in the split
+    if (a.causal)
+        rowlim = min(rowlim, (int64_t)qi + a.offset);
+    if (!row_on)
+        rowlim = -1;
+
+    // Q^T as B operands: lane holds row r, d = 32*kk + 8*quad .. +7
+    u32x4 qf[D / 32];
+    {
+        const uint16_t *qp = (const uint16_t *)a.q + (((int64_t)b * a.Sq + qi) * a.Hq + h) * D;
+#pragma unroll
+        for (int kk = 0; kk < D / 32; ++kk)
+            qf[kk] = row_on ? *(const u32x4 *)(qp + 32 * kk + 8 * quad) : (u32x4){};
+    }
+
+    f32x4 acc[D / 16];
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt)
+        acc[dt] = (f32x4){};
+    float frame = -INFINITY, lsum = 0.0f;
+
+    TileLoader<D, KV> ld;
+    ld.init(a.k, a.v, (int64_t)b * a.Sk * a.Hkv + kvh, a.Hkv, a.Sk, t);
+    if (nb > 0) {
+        ld.load((int)ks);
+        ld.store(lds, lds + Geo::kElems);
+    }
+    __syncthreads();
+
+    for (int kb = 0; kb < nb; ++kb) {
+        const int k0 = (int)ks + kb * kBN;
+        if (kb + 1 < nb)
+            ld.load(k0 + kBN);
+        const uint16_t *lk = lds + (kb & 1) * Geo::stage;
+        const uint16_t *lv = lk + Geo::kElems;
+        const int kw = k0 + 16 * wave;              // this wave's first key
+
+        if (__any(kw <= rowlim)) {          // wave-uniform: some row sees a key here
+            f32x4 sc = (f32x4){};
+            const uint16_t *kr = lk + (16 * wave + r) * Geo::kStride + 8 * quad;
+#pragma unroll
+            for (int kk = 0; kk < D / 32; ++kk)
+                sc = mfma16<BF>(*(const u32x4 *)(kr + 32 * kk), qf[kk], sc);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (kw + 4 * quad + i > rowlim)
+                    sc[i] = -INFINITY;
+            float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+            mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+            mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+            const float m2 = mx * a.c;
+            const bool need = m2 > frame + kRescaleMarginLog2;
+            if (__any(need)) {
+                const float alpha = need ? exp2_fast(frame - m2) : 1.0f;
+#pragma unroll
+                for (int dt = 0; dt < D / 16; ++dt)
+                    acc[dt] *= alpha;
+                lsum *= alpha;
+                frame = need ? m2 : frame;
+            }
+            const float fr = (frame == -INFINITY) ? 0.0f : frame;
+            u32x2 pf;
+            {
+                const float p0 = exp2_fast(__builtin_fmaf(sc[0], a.c, -fr));
+                const float p1 = exp2_fast(__builtin_fmaf(sc[1], a.c, -fr));
+                const float p2 = exp2_fast(__builtin_fmaf(sc[2], a.c, -fr));
+                const float p3 = exp2_fast(__builtin_fmaf(sc[3], a.c, -fr));
+                pf[0] = pack2<BF>(p0, p1);
+                pf[1] = pack2<BF>(p2, p3);
+                lsum = sum2<BF>(pf[1], sum2<BF>(pf[0], lsum));
+            }
+            const uint16_t *vr = lv + r * Geo::vStride + 16 * wave + 4 * quad;
+#pragma unroll
+            for (int dt = 0; dt < D / 16; ++dt)
+                acc[dt] = mfma16k16<BF>(*(const u32x2 *)(vr + 16 * dt * Geo::vStride), pf, acc[dt]);
+        }
+        if (kb + 1 < nb)
+            ld.store(lds + ((kb + 1) & 1) * Geo::stage,
+                     lds + ((kb + 1) & 1) * Geo::stage + Geo::kElems);
+        __syncthreads();
+    }
+
+    // ---- combine the 4 waves' states of each row, write the split's partial ---------------
+    lsum += __shfl_xor(lsum, 16, 64);
+    lsum += __shfl_xor(lsum, 32, 64);
+    float *cmb_o = (float *)lds;                    // [4 waves][16 rows][D]
+    float *cmb_f = cmb_o + 4 * 16 * D;              // [4][16]
+    float *cmb_l = cmb_f + 64;                      // [4][16]
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            cmb_o[(wave * 16 + r) * D + 16 * dt + 4 * quad + i] = acc[dt][i];
+    if (quad == 0) {
+        cmb_f[wave * 16 + r] = frame;
+        cmb_l[wave * 16 + r] = lsum;
+    }
+    __syncthreads();
+
+    float *out = p.part + (((int64_t)b * a.Hkv + kvh) * p.n_split + s) * p.rows * (D + 2);
+    for (int e = t; e < p.rows * D; e += kThreads) {
+        const int rr = e / D, d = e % D;
+        float F = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+            F = fmaxf(F, cmb_f[w * 16 + rr]);
+        float o = 0.0f, l = 0.0f;
+        if (F != -INFINITY) {
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const float sw = exp2_fast(cmb_f[w * 16 + rr] - F);   // 0 for an empty wave
+                o += sw * cmb_o[(w * 16 + rr) * D + d];
+                l += sw * cmb_l[w * 16 + rr];
+            }
+        }
+        out[rr * (D + 2) + d] = o;
+        if (d == 0) {
+            out[rr * (D + 2) + D] = F;
+            out[rr * (D + 2) + D + 1] = l;
+        }
+    }
+}
+
+// One wave per (b, KV head, row): log-sum-exp merge of the row's n_split partials.
+template <int D, bool BF>
+__global__ __launch_bounds__(64) void decode_merge_kernel(DecodeParams p)
+{
+    __shared__ float wts[1024];
+    const AttnArgs &a = p.a;
+    const int lane = threadIdx.x;
+    int rest = blockIdx.x;
+    const int rr = rest % p.rows;
+    rest /= p.rows;
+    const int kvh = rest % a.Hkv;
+    const int b = rest / a.Hkv;
+    const int stride = p.rows * (D + 2);
+    const float *base = p.part + ((int64_t)b * a.Hkv + kvh) * p.n_split * stride + rr * (D + 2);
+
+    float F = -INFINITY;
+    for (int s = lane; s < p.n_split; s += 64)
+        F = fmaxf(F, base[(int64_t)s * stride + D]);
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1)
+        F = fmaxf(F, __shfl_xor(F, m, 64));
+    float L = 0.0f;
+    for (int s = lane; s < p.n_split; s += 64) {
+        const float w = F == -INFINITY ? 0.0f : exp2_fast(base[(int64_t)s * stride + D] - F);
+        wts[s] = w;
+        L += w * base[(int64_t)s * stride + D + 1];
+    }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1)
+        L += __shfl_xor(L, m, 64);
+    __syncthreads();
+    const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+
+    const int qi = rr / a.G, hl = rr % a.G;
+    uint16_t *op = (uint16_t *)a.o + (((int64_t)b * a.Sq + qi) * a.Hq + kvh * a.G + hl) * D;
+    for (int d2 = lane; d2 < D / 2; d2 += 64) {
+        float o0 = 0.0f, o1 = 0.0f;
+        for (int s = 0; s < p.n_split; ++s) {
+            const float w = wts[s];
+            o0 += w * base[(int64_t)s * stride + 2 * d2];
+            o1 += w * base[(int64_t)s * stride + 2 * d2 + 1];
+        }
+        *(uint32_t *)(op + 2 * d2) = pack2<BF>(o0 * inv, o1 * inv);
+    }
+}
+
+template <int D, int KV>
+hipError_t launch(const DecodeParams &p, int64_t n_wg, hipStream_t stream)
+{
+    hipLaunchKernelGGL((decode_split_kernel<D, KV>), dim3((unsigned)n_wg), dim3(kThreads), 0,
+                       stream, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    const int64_t n_rows = (int64_t)p.a.B * p.a.Hkv * p.rows;
+    hipLaunchKernelGGL((decode_merge_kernel<D, KV == KV_BF16>), dim3((unsigned)n_rows), dim3(64),
+                       0, stream, p);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+// Split choice: about 1024 workgroups in all (several per CU), each split a whole number of
+// 64-key tiles and at least one tile.
+constexpr int64_t kTargetWorkgroups = 1024;
+
+DecodeGrid decode_grid(int B, int Hq, int Hkv, int Sq, int Sk, int D, int64_t kend, bool bound)
+{
+    DecodeGrid g;
+    g.rows = (Hq / Hkv) * Sq;
+    const int64_t heads = (int64_t)B * Hkv;
+    int64_t want = heads > 0 ? (kTargetWorkgroups + heads - 1) / heads : 1;
+    if (want > 1024)
+        want = 1024;     // the merge kernel keeps one weight per split in LDS
+    const int64_t tiles = (kend + kBN - 1) / kBN;
+    const int64_t tiles_per = tiles > 0 ? (tiles + want - 1) / want : 1;
+    g.split_len = (int)(tiles_per * kBN);
+    g.n_split = tiles > 0 ? (int)((tiles + tiles_per - 1) / tiles_per) : 1;
+    if (bound) {
+        const int64_t all_tiles = ((int64_t)Sk + kBN - 1) / kBN;
+        g.n_split = (int)(all_tiles < want ? (all_tiles > 0 ? all_tiles : 1) : want);
+    }
+    g.n_wg = heads * g.n_split;
+    g.workspace_bytes = (size_t)heads * g.n_split * g.rows * (D + 2) * sizeof(float);
+    return g;
+}
+
+hipError_t launch_decode(const AttnArgs &a, const DecodeGrid &g, void *workspace,
+                         hipStream_t stream)
+{
+    if (g.n_wg == 0)
+        return hipSuccess;
+    DecodeParams p;
+    p.a = a;
+    p.rows = g.rows;
+    p.n_split = g.n_split;
+    p.split_len = g.split_len;
+    p.kend = a.causal ? min((int64_t)a.Sk, (int64_t)a.Sq - 1 + a.offset + 1) : (int64_t)a.Sk;
+    if (p.kend < 0)
+        p.kend = 0;
+    p.part = (float *)workspace;
+    if (a.D == 128) {
+        if (a.kv == KV_F16)
+            return launch<128, KV_F16>(p, g.n_wg, stream);
+        if (a.kv == KV_BF16)
+            return launch<128, KV_BF16>(p, g.n_wg, stream);
+        return launch<128, KV_Q4_0>(p, g.n_wg, stream);
+    }
+    if (a.kv == KV_F16)
+        return launch<64, KV_F16>(p, g.n_wg, stream);
+    if (a.kv == KV_BF16)
+        return launch<64, KV_BF16>(p, g.n_wg, stream);
+    return launch<64, KV_Q4_0>(p, g.n_wg, stream);
+}
+
+}  // namespace fa

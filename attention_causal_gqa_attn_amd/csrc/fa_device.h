@@ -1,0 +1,184 @@
+// Device building blocks shared by the prefill, decode and dequant kernels (gfx950 only).
+//
+// Element values travel as raw 16-bit patterns (uint32 pairs, 16-byte quads) and are
+// reinterpreted as f16 or bf16 vectors only at the MFMA and conversion instructions, so one
+// code path serves both 16-bit types.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+enum { KV_F16 = 0, KV_BF16 = 1, KV_Q4_0 = 2 };
+
+// Softmax works in base 2: scores are multiplied by scale*log2(e) and exponentiated with
+// v_exp_f32. The rescale margin of 10 natural-log units becomes 10*log2(e).
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kRescaleMargin = 10.0f;
+constexpr float kRescaleMarginLog2 = kRescaleMargin * kLog2e;
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ---------------------------------------------------------------------------------------
+// MFMA: D = A * B + C with 8 16-bit elements of A and of B per lane.
+//   32x32x16: lane l holds A[m = l%32][k = 8*(l/32) .. +7], B[k = 8*(l/32) .. +7][n = l%32];
+//             C reg i holds C[m = 8*(i/4) + 4*(l/32) + i%4][n = l%32].
+//   16x16x32: lane l holds A[m = l%16][k = 8*(l/16) .. +7], B[k = 8*(l/16) .. +7][n = l%16];
+//             C reg i holds C[m = 4*(l/16) + i][n = l%16].
+// Only the C layout matters for correctness here: the k order inside A and B is the same
+// function of (lane, slot) for both operands, so any k permutation cancels in the sum.
+// ---------------------------------------------------------------------------------------
+template <bool BF>
+__device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c)
+{
+    if constexpr (BF)
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                      __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
+template <bool BF>
+__device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c)
+{
+    if constexpr (BF)
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                      __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
+// 16x16x16 with 4 elements per lane: A[m = l%16][k = 4*(l/16) .. +3], B likewise.
+template <bool BF>
+__device__ __forceinline__ f32x4 mfma16k16(u32x2 a, u32x2 b, f32x4 c)
+{
+    if constexpr (BF)
+        return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4, a) ,
+                                                        __builtin_bit_cast(bf16x4, b), c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a),
+                                                     __builtin_bit_cast(f16x4, b), c, 0, 0, 0);
+}
+
+// Two f32 -> packed 16-bit pair, round to nearest even.
+template <bool BF>
+__device__ __forceinline__ uint32_t pack2(float lo, float hi)
+{
+    if constexpr (BF) {
+        bf16x2 v = __builtin_convertvector((f32x2){lo, hi}, bf16x2);
+        return __builtin_bit_cast(uint32_t, v);
+    } else {
+        f16x2 v = __builtin_convertvector((f32x2){lo, hi}, f16x2);
+        return __builtin_bit_cast(uint32_t, v);
+    }
+}
+
+// Sum of a packed 16-bit pair, accumulated in f32 (v_dot2 with ones).
+template <bool BF>
+__device__ __forceinline__ float sum2(uint32_t pair, float acc)
+{
+    if constexpr (BF) {
+        const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+        return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pair), one, acc, false);
+    } else {
+        const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
+        return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pair), one, acc, false);
+    }
+}
+
+// Value held by lane l ^ 32.
+__device__ __forceinline__ float swap_halves(float x) { return __shfl_xor(x, 32, 64); }
+
+// Byte permute: result byte i = byte sel_i of {hi:lo} (0..3 lo, 4..7 hi, 0x0C -> 0).
+__device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel)
+{
+    return __builtin_amdgcn_perm(hi, lo, sel);
+}
+
+// ---------------------------------------------------------------------------------------
+// q4_0 unpacking. A code byte holds element t (low nibble) and element t+16 (high nibble)
+// of its 32-element block; value (c - 8) * d with the block's f16 scale d.
+//
+// A nibble c placed in the low mantissa bits of the f16 pattern 0x6400 (= 1024) gives the
+// f16 value 1024 + c; subtracting 1032 is exact and leaves c - 8; one f16 multiply by d
+// then rounds the exact product (c - 8) * d to nearest even — the same value as the
+// correctly rounded f16 of the exact product.
+// ---------------------------------------------------------------------------------------
+// Two nibbles at bits 0..3 and 16..19 of `nib` -> packed f16 pair (c0 - 8) * d0, (c1 - 8) * d1.
+__device__ __forceinline__ uint32_t q4_pair(uint32_t nib, uint32_t d2)
+{
+    const f16x2 x = __builtin_bit_cast(f16x2, (nib & 0x000F000Fu) | 0x64006400u);
+    const f16x2 c = x - (f16x2){(_Float16)1032.0f, (_Float16)1032.0f};
+    return __builtin_bit_cast(uint32_t, c * __builtin_bit_cast(f16x2, d2));
+}
+
+// Four code bytes of one block (bytes 4g .. 4g+3) -> natural-order element pairs:
+//   lo[0] = (e[4g], e[4g+1]), lo[1] = (e[4g+2], e[4g+3]),
+//   hi[0] = (e[16+4g], e[16+4g+1]), hi[1] = (e[16+4g+2], e[16+4g+3]).
+// d2 = the block scale in both halves.
+__device__ __forceinline__ void q4_unpack_row(uint32_t codes, uint32_t d2, uint32_t lo[2],
+                                              uint32_t hi[2])
+{
+    const uint32_t u0 = perm(0u, codes, 0x0C010C00u);   // [B0, 0, B1, 0]
+    const uint32_t u1 = perm(0u, codes, 0x0C030C02u);   // [B2, 0, B3, 0]
+    lo[0] = q4_pair(u0, d2);
+    hi[0] = q4_pair(u0 >> 4, d2);
+    lo[1] = q4_pair(u1, d2);
+    hi[1] = q4_pair(u1 >> 4, d2);
+}
+
+// Code byte j of two keys' blocks (c0 for key 0, c1 for key 1) -> key-pairs of one element:
+//   lo = (x0[t], x1[t]) and hi = (x0[t+16], x1[t+16]) with t = 4g + j;
+// d2 = (d of key 0, d of key 1).
+template <int J>
+__device__ __forceinline__ void q4_unpack_cols(uint32_t c0, uint32_t c1, uint32_t d2,
+                                               uint32_t &lo, uint32_t &hi)
+{
+    constexpr uint32_t sel = 0x0C000C00u | ((4u + J) << 16) | (uint32_t)J;
+    const uint32_t u = perm(c1, c0, sel);                 // [c0.Bj, 0, c1.Bj, 0]
+    lo = q4_pair(u, d2);
+    hi = q4_pair(u >> 4, d2);
+}
+
+// Read the 18-byte block starting `misalign` (0 or 2) bytes into five aligned dwords w[0..4]:
+// returns its scale (f16 bits in the low half) and its 16 code bytes as 4 dwords.
+__device__ __forceinline__ void q4_split_block(const uint32_t w[5], uint32_t misalign,
+                                               uint32_t &d_bits, uint32_t codes[4])
+{
+    // misalign == 0: scale = w0[15:0], codes start at byte 2 (straddling dwords);
+    // misalign == 2: scale = w0[31:16], codes are w1..w4.
+    const uint32_t sh = misalign ? 0u : 16u;
+    d_bits = (misalign ? (w[0] >> 16) : w[0]) & 0xFFFFu;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+        const uint32_t lo = misalign ? w[g + 1] : w[g];
+        codes[g] = __builtin_amdgcn_alignbit(w[g + 1], lo, sh);
+    }
+}
+
+// Grid remap so that consecutive logical workgroups run on the same XCD: the hardware deals
+// workgroup ids round-robin over the 8 XCDs, so id -> (id % 8) * (n / 8) + id / 8 hands each
+// XCD one contiguous slice of the logical order (and so of K/V heads, which share its L2).
+__device__ __forceinline__ int xcd_remap(int id, int n)
+{
+    if (n % 8)
+        return id;
+    return (id % 8) * (n / 8) + id / 8;
+}
+
+}  // namespace fa

@@ -1,0 +1,45 @@
+// Internal interface between the C ABI (fa_api.cpp) and the kernel translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+// Everything a prefill or decode launch needs; filled and validated by the C ABI layer.
+struct AttnArgs {
+    const void *q, *k, *v;
+    void *o;
+    int B, Hq, Hkv, Sq, Sk, D;
+    int G;              // query heads per KV head
+    int kv;             // KV_F16, KV_BF16 or KV_Q4_0
+    int causal;
+    int64_t offset;     // query i sits at absolute position i + offset
+    float c;            // scale * log2(e)
+};
+
+// Prefill workgroup decomposition: 4 waves of 32 query rows; hpw heads of one KV group by
+// qsub 32-row sub-blocks (hpw * qsub <= 4); heads beyond 4 of a group go to further chunks.
+struct PrefillGrid {
+    int hpw, qsub, n_qblk, n_hchunk;
+    int64_t n_wg;
+};
+PrefillGrid prefill_grid(const AttnArgs &a);
+hipError_t launch_prefill(const AttnArgs &a, hipStream_t stream);
+
+// Decode: n_split key ranges per (b, KV head); rows = G * Sq query rows per KV head (<= 16).
+struct DecodeGrid {
+    int rows, n_split, split_len;   // split_len: keys per split, a multiple of 64
+    int64_t n_wg;
+    size_t workspace_bytes;
+};
+// kend: keys any row can see, [0, kend). With bound = true the result's workspace_bytes is
+// the largest any kend <= Sk can need (the split count is not monotone in kend).
+DecodeGrid decode_grid(int B, int Hq, int Hkv, int Sq, int Sk, int D, int64_t kend, bool bound);
+hipError_t launch_decode(const AttnArgs &a, const DecodeGrid &g, void *workspace,
+                         hipStream_t stream);
+
+hipError_t launch_dequant_q4_0(const void *blocks, int64_t n_blocks, float *out_f32,
+                               void *out_f16, hipStream_t stream);
+
+}  // namespace fa

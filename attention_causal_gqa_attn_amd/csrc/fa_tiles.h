@@ -1,0 +1,190 @@
+// K/V tile staging: global memory -> registers -> LDS, shared by the prefill and decode
+// kernels. A tile is kBN = 64 consecutive keys of one KV head:
+//   K tile  [64 keys][D]      row stride D + 8 elements (16 B pad: conflict-free row reads)
+//   V^T tile [D][64 keys]     row stride 64 + 8 elements (transposed at store time, so the
+//                             P.V MFMA reads 8 consecutive keys of one d as one 16-byte load)
+// Both hold f16 or bf16 values; a q4_0 cache is dequantized on the way into LDS, so the
+// MFMA loop is the same for every cache type.
+//
+// Work split over the 256 threads of a workgroup:
+//   16-bit K: 16-byte chunks, id = pass * 256 + t -> key id / (D/8), chunk id % (D/8).
+//   16-bit V: KPT = D/32 consecutive keys x one 16-byte chunk per thread; the KPT rows are
+//             transposed in registers with byte permutes and written as KPT-key runs.
+//   q4_0:     one item = 2 consecutive keys x 1 block; threads [0, D) take K, [D, 2D) take V.
+// Key indices past the end of the sequence are clamped to the last key: those slots are
+// masked out of the softmax, and clamping keeps every load in bounds and every value finite.
+#pragma once
+
+#include "fa_device.h"
+
+namespace fa {
+
+constexpr int kBN = 64;          // keys per tile
+constexpr int kThreads = 256;    // threads per workgroup
+
+template <int D>
+struct TileGeom {
+    static constexpr int kStride = D + 8;
+    static constexpr int vStride = kBN + 8;
+    static constexpr int kElems = kBN * kStride;
+    static constexpr int vElems = D * vStride;
+    static constexpr int stage = kElems + vElems;     // 16-bit elements per K+V buffer
+};
+
+template <int D, int KV>
+struct TileLoader;
+
+// f16 / bf16 caches ----------------------------------------------------------------------
+template <int D, int KV>
+struct TileLoader {
+    static_assert(D == 64 || D == 128, "head dim");
+    using G = TileGeom<D>;
+    static constexpr int KC = D / 32;     // K chunks per thread
+    static constexpr int KPT = D / 32;    // V keys per thread
+    static constexpr int VCOLS = kBN / KPT;
+
+    const uint16_t *kbase, *vbase;        // first element of (b, key 0, kvh)
+    int64_t row;                          // elements between consecutive keys
+    int Sk, t;
+    u32x4 kr[KC], vr[KPT];
+
+    // head_off_rows: key-row index of (b, key 0, kvh); row_rows: key rows between keys (Hkv)
+    __device__ void init(const void *k, const void *v, int64_t head_off_rows, int64_t row_rows,
+                         int Sk_, int t_)
+    {
+        kbase = (const uint16_t *)k + head_off_rows * D;
+        vbase = (const uint16_t *)v + head_off_rows * D;
+        row = row_rows * D;
+        Sk = Sk_;
+        t = t_;
+    }
+
+    __device__ void load(int k0)
+    {
+#pragma unroll
+        for (int p = 0; p < KC; ++p) {
+            const int id = p * kThreads + t;
+            const int key = id / (D / 8), dc = id % (D / 8);
+            const int64_t j = min(k0 + key, Sk - 1);
+            kr[p] = *(const u32x4 *)(kbase + j * row + dc * 8);
+        }
+        const int key0 = KPT * (t % VCOLS), dc = t / VCOLS;
+#pragma unroll
+        for (int r = 0; r < KPT; ++r) {
+            const int64_t j = min(k0 + key0 + r, Sk - 1);
+            vr[r] = *(const u32x4 *)(vbase + j * row + dc * 8);
+        }
+    }
+
+    __device__ void store(uint16_t *lk, uint16_t *lv) const
+    {
+#pragma unroll
+        for (int p = 0; p < KC; ++p) {
+            const int id = p * kThreads + t;
+            const int key = id / (D / 8), dc = id % (D / 8);
+            *(u32x4 *)(lk + key * G::kStride + dc * 8) = kr[p];
+        }
+        const int key0 = KPT * (t % VCOLS), dc = t / VCOLS;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+            uint16_t *dst = lv + (dc * 8 + e) * G::vStride + key0;
+            if constexpr (KPT == 4) {
+                u32x2 w;
+                w[0] = perm(vr[1][e / 2], vr[0][e / 2], sel);
+                w[1] = perm(vr[3][e / 2], vr[2][e / 2], sel);
+                *(u32x2 *)dst = w;
+            } else {
+                *(uint32_t *)dst = perm(vr[1][e / 2], vr[0][e / 2], sel);
+            }
+        }
+    }
+};
+
+// q4_0 cache -----------------------------------------------------------------------------
+template <int D>
+struct TileLoader<D, KV_Q4_0> {
+    static_assert(D == 64 || D == 128, "head dim");
+    using G = TileGeom<D>;
+    static constexpr int NB = D / 32;           // blocks per key row
+    static constexpr int ROWB = NB * 18;        // bytes per key row
+
+    const uint8_t *base;                        // K or V, first byte of (b, key 0, kvh)
+    int64_t row;                                // bytes between consecutive keys
+    int Sk, tensor, kp, blk, aligned, mis;
+    uint32_t w[2][5];
+
+    __device__ void init(const void *k, const void *v, int64_t head_off_rows, int64_t row_rows,
+                         int Sk_, int t)
+    {
+        tensor = t / D;                         // 0: K, 1: V, >= 2: idle
+        const int u = t % D;
+        kp = u % 32;
+        blk = u / 32;
+        const int off = 18 * blk;
+        aligned = off & ~3;
+        mis = off & 3;
+        base = (const uint8_t *)(tensor ? v : k) + head_off_rows * ROWB;
+        row = row_rows * ROWB;
+        Sk = Sk_;
+    }
+
+    __device__ void load(int k0)
+    {
+        if (tensor >= 2)
+            return;
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            const int64_t j = min(k0 + 2 * kp + r, Sk - 1);
+            const uint32_t *p = (const uint32_t *)(base + j * row + aligned);
+#pragma unroll
+            for (int i = 0; i < 5; ++i)
+                w[r][i] = p[i];
+        }
+    }
+
+    __device__ void store(uint16_t *lk, uint16_t *lv) const
+    {
+        if (tensor >= 2)
+            return;
+        uint32_t dbits[2], codes[2][4];
+        q4_split_block(w[0], mis, dbits[0], codes[0]);
+        q4_split_block(w[1], mis, dbits[1], codes[1]);
+        if (tensor == 0) {
+#pragma unroll
+            for (int r = 0; r < 2; ++r) {
+                const uint32_t d2 = dbits[r] * 0x10001u;
+                uint32_t lo[4][2], hi[4][2];
+#pragma unroll
+                for (int g = 0; g < 4; ++g)
+                    q4_unpack_row(codes[r][g], d2, lo[g], hi[g]);
+                uint16_t *dst = lk + (2 * kp + r) * G::kStride + 32 * blk;
+                *(u32x4 *)(dst + 0) = (u32x4){lo[0][0], lo[0][1], lo[1][0], lo[1][1]};
+                *(u32x4 *)(dst + 8) = (u32x4){lo[2][0], lo[2][1], lo[3][0], lo[3][1]};
+                *(u32x4 *)(dst + 16) = (u32x4){hi[0][0], hi[0][1], hi[1][0], hi[1][1]};
+                *(u32x4 *)(dst + 24) = (u32x4){hi[2][0], hi[2][1], hi[3][0], hi[3][1]};
+            }
+        } else {
+            const uint32_t d2 = dbits[0] | (dbits[1] << 16);
+            uint16_t *col = lv + (32 * blk) * G::vStride + 2 * kp;
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                uint32_t lo, hi;
+                q4_unpack_cols<0>(codes[0][g], codes[1][g], d2, lo, hi);
+                *(uint32_t *)(col + (4 * g + 0) * G::vStride) = lo;
+                *(uint32_t *)(col + (4 * g + 16) * G::vStride) = hi;
+                q4_unpack_cols<1>(codes[0][g], codes[1][g], d2, lo, hi);
+                *(uint32_t *)(col + (4 * g + 1) * G::vStride) = lo;
+                *(uint32_t *)(col + (4 * g + 17) * G::vStride) = hi;
+                q4_unpack_cols<2>(codes[0][g], codes[1][g], d2, lo, hi);
+                *(uint32_t *)(col + (4 * g + 2) * G::vStride) = lo;
+                *(uint32_t *)(col + (4 * g + 18) * G::vStride) = hi;
+                q4_unpack_cols<3>(codes[0][g], codes[1][g], d2, lo, hi);
+                *(uint32_t *)(col + (4 * g + 3) * G::vStride) = lo;
+                *(uint32_t *)(col + (4 * g + 19) * G::vStride) = hi;
+            }
+        }
+    }
+};
+
+}  // namespace fa

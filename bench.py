@@ -1,0 +1,237 @@
+"""Benchmark of the causal GQA flash-attention hot path on one MI355X.
+
+One step = one pass of the whole path over resident inputs:
+  * prefill: 2048 f16 queries as the last positions of 16384 keys, GQA 32/8, D=128, causal
+    (fa_prefill, one MFMA kernel);
+  * decode:  4 sequences x 1 query against 32768 q4_0-cached keys, GQA 32/8, D=128
+    (fa_decode, split kernel + merge kernel).
+Before each call a 1 GiB buffer is overwritten so that neither call finds its inputs in the
+256 MB last-level cache (the decode working set, 151 MB, would otherwise stay resident).
+
+Prints one JSON line. `value` is prefill TFLOP/s (algorithmic FLOPs / mean kernel time from
+HIP events on the launch stream); the decode HBM GB/s figure sits in `decode`. `roofline` is
+for the prefill kernel, `roofline_decode` for the decode pair. `cpu_baseline` times the CPU
+oracle on a bounded sample of the prefill workload's rows.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+    python bench.py --calibrate-copy     # a plain 256 MiB device copy, for HBM counter scaling
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attention TFLOP/s at 2K-query×16K-key GQA32/8 D=128 f16; q4_0 decode HBM GB/s"
+PEAK_MFMA_F16_TFLOPS = 2500.0      # MI355X dense f16/bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0              # MI355X HBM3E, published
+PAGES_PREFILL_16K_TFLOPS = 1.20    # the pages' fixed kernel at 16K keys (Radeon 8060S, gfx1151)
+FLUSH_BYTES = 1 << 30
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_16k_f16_traffic.txt")
+
+
+def source_hash() -> str:
+    """Hash of the kernel sources, to tell whether stored counter readings still apply."""
+    csrc = os.path.join(ROOT, "attention_causal_gqa_attn_amd", "csrc")
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic():
+    """HBM bytes per prefill launch from the committed counter summary, if it was taken on the
+    current kernel sources."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    for line in open(TRAFFIC_FILE):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("source_hash") != source_hash():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def calibrate_copy(torch):
+    n = 256 << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate_copy_bytes_read": n, "calibrate_copy_bytes_written": n}), flush=True)
+
+
+def cpu_baseline(w, x, seconds: float):
+    """The oracle, as it stands, on a random sample of the prefill workload's rows."""
+    import numpy as np
+    import oracle
+    import workloads as W
+
+    threads = len(os.sched_getaffinity(0))
+    rng = np.random.default_rng(0)
+    total = w.B * w.Sq * w.Hq
+
+    def run(n):
+        rows = np.sort(rng.choice(total, size=n, replace=False))
+        t0 = time.perf_counter()
+        oracle.attention(x.q, x.k, x.v, q_dtype=w.q_dtype, kv_dtype=w.kv, causal=w.causal,
+                         offset=w.causal_offset, scale=w.scale, rows=rows, threads=threads)
+        dt = time.perf_counter() - t0
+        i = (rows // w.Hq) % w.Sq
+        keys = np.clip(i + w.causal_offset + 1, 0, w.Sk)
+        return dt, int(4 * w.D * keys.sum()), n
+
+    dt, _, n = run(max(threads, 16))
+    n_big = int(min(total, max(threads, n * seconds / max(dt, 1e-3))))
+    dt, flops, n = run(n_big)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n} of {total} query rows of the 2Kx16K f16 prefill (uniform random), "
+                      f"{flops / 1e9:.1f} GFLOP in {dt:.1f} s, {threads} OpenMP threads",
+            "seconds": dt}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--calibrate-copy", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for "
+              f"--gpus {args.gpus}); run with --gpus 1", file=sys.stderr, flush=True)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    if args.calibrate_copy:
+        calibrate_copy(torch)
+        return
+
+    import attention_causal_gqa_attn_amd as fa
+    import workloads as W
+
+    fa.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def to_dev(a, dtype):
+        if dtype == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    wp = W.WORKLOADS["prefill_16k_f16"]
+    wd = W.WORKLOADS["decode_q4_0"]
+    xp = W.generate(wp)
+    xd = W.generate(wd)
+    pq, pk, pv = to_dev(xp.q, "f16"), to_dev(xp.k, "f16"), to_dev(xp.v, "f16")
+    dq, dk, dv = to_dev(xd.q, "f16"), to_dev(xd.k, "q4_0"), to_dev(xd.v, "q4_0")
+    po = torch.empty_like(pq)
+    do = torch.empty_like(dq)
+    ws = torch.empty(max(16, fa.decode_workspace_bytes(wd.B, wd.Hq, wd.Hkv, wd.Sq, wd.Sk, wd.D)),
+                     dtype=torch.uint8, device=dev)
+    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def prefill():
+        fa.prefill(pq, pk, pv, causal=True, offset=wp.causal_offset, scale=wp.scale, out=po,
+                   stream=stream)
+
+    def decode():
+        fa.decode(dq, dk, dv, causal=True, offset=wd.causal_offset, scale=wd.scale, out=do,
+                  workspace=ws, stream=stream)
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+
+    def step(i=None, k=0):
+        flush.fill_(k & 255)
+        if i is not None:
+            ev[i][0].record(stream)
+        prefill()
+        if i is not None:
+            ev[i][1].record(stream)
+        flush.fill_((k + 1) & 255)
+        if i is not None:
+            ev[i][2].record(stream)
+        decode()
+        if i is not None:
+            ev[i][3].record(stream)
+
+    for k in range(args.warmup):
+        step(None, k)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    p_ms = np.array([e[0].elapsed_time(e[1]) for e in ev])
+    d_ms = np.array([e[2].elapsed_time(e[3]) for e in ev])
+    flops = W.attention_flops(wp)
+    dbytes = W.algorithmic_bytes(wd)
+    p_s = float(p_ms.mean()) * 1e-3
+    d_s = float(d_ms.mean()) * 1e-3
+    tflops = flops / p_s / 1e12
+    gbs = dbytes / d_s / 1e9
+
+    traffic = stored_traffic()
+    line = {
+        "metric": METRIC,
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": round(tflops / PAGES_PREFILL_16K_TFLOPS, 2),
+        "vs_baseline_note": "ratio to the pages' 1.20 TFLOP/s (429.2 ms) at 16K keys, measured on "
+                            "a Radeon 8060S (gfx1151): context from other hardware, not a target",
+        "dtype": "f16",
+        "data": "synthetic: seeded N(0,1) Q/K/V; q4_0 K/V quantized from N(0,1)",
+        "config": {"workload": "prefill_16k_f16 (B=1 Sq=2048 Sk=16384 Hq=32 Hkv=8 D=128 causal, "
+                               "offset Sk-Sq) + decode_q4_0 (B=4 Sq=1 Sk=32768 Hq=32 Hkv=8 D=128)",
+                   "global_batch": wp.B, "seq_len": wp.Sk, "parallelism": "none (1 GPU)",
+                   "cache_flush_bytes_before_each_call": FLUSH_BYTES},
+        "prefill": {"tflops": round(tflops, 3), "ms_mean": round(float(p_ms.mean()), 5),
+                    "ms_median": round(float(np.median(p_ms)), 5),
+                    "ms_min": round(float(p_ms.min()), 5), "gflop": round(flops / 1e9, 3)},
+        "decode": {"value": round(gbs, 1), "unit": "GB/s", "ms_mean": round(float(d_ms.mean()), 5),
+                   "ms_median": round(float(np.median(d_ms)), 5),
+                   "ms_min": round(float(d_ms.min()), 5), "algorithmic_bytes": dbytes,
+                   "kernels": "decode_split_kernel + decode_merge_kernel"},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 3), "peak": PEAK_MFMA_F16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_MFMA_F16_TFLOPS, 4),
+                     "traffic": traffic, "kernel": "prefill_kernel<128, f16>",
+                     "algorithmic_flops_per_launch": flops},
+        "roofline_decode": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                            "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                            "algorithmic_bytes_per_call": dbytes},
+        "source_hash": source_hash(),
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(wp, xp, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

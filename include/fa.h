@@ -1,0 +1,124 @@
+/*
+ * fa.h — C ABI of libfa.so: causal grouped-query flash attention on AMD Instinct MI355X
+ * (gfx950), with f16, bf16 or 4-bit block-quantized (q4_0) K/V.
+ *
+ * What every call computes (the fused scaled-dot-product attention forward pass that the
+ * mlxcel PR #2306 "defer SDPA accumulator rescale, stage Q once per block" optimises and
+ * that the mi210-llm-stack guide "Build FlashAttention (CK backend) on gfx90a" verifies
+ * against torch's scaled_dot_product_attention):
+ *
+ *     O[b,i,h,:] = sum_j softmax_j(scale * Q[b,i,h,:] . K[b,j,g,:]) * V[b,j,g,:]
+ *
+ * over the keys j that query i may see, with g = h / (Hq / Hkv) (consecutive grouping of
+ * "GQA 32/8"). When causal != 0, query i sits at absolute position i + causal_offset and
+ * sees key j iff j <= i + causal_offset ("maskless" causal: the mask comes from indices; a
+ * chunk of Sq queries placed at the end of Sk keys uses causal_offset = Sk - Sq). A query
+ * that sees no key gets a zero output row.
+ *
+ * Layouts (all contiguous, row-major, no padding):
+ *   Q, O : [B, Sq, Hq, D]  elements of the Q type
+ *   K, V : [B, Sk, Hkv, D] elements of the K/V type, or for FA_KV_Q4_0
+ *          [B, Sk, Hkv, D/32] blocks of 18 bytes
+ * The Q/O type is bf16 when kv_dtype is FA_KV_BF16 and f16 otherwise (f16 and q4_0 caches).
+ *
+ * q4_0 block (the KV-cache type "-ctk q4_0 -ctv q4_0" of the mi210-llm-stack page
+ * "FlashAttention on gfx90a"; the page names it but does not define it, so this is the
+ * common GGML arrangement): 32 consecutive head-dim elements, stored as a little-endian f16
+ * scale d followed by 16 bytes; byte t holds the 4-bit code c of element t in its low nibble
+ * and of element t+16 in its high nibble. Element value: (c - 8) * d.
+ *
+ * Ownership: every pointer is caller-owned device memory (hipMalloc or a framework's
+ * allocator); the library allocates nothing, keeps no device state and never frees.
+ * Calls are asynchronous on `stream` (0 = the null stream). A return of FA_OK means the
+ * work was enqueued; all argument checks happen before any HIP call, so an error return
+ * means nothing was launched. No C++ exception crosses this interface. The library never
+ * falls back to a slower path: an unsupported combination is an error.
+ */
+#ifndef FA_H
+#define FA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Same type as HIP's hipStream_t. */
+typedef struct ihipStream_t *fa_stream_t;
+
+enum fa_kv_dtype {
+    FA_KV_F16 = 0,   /* K/V f16,  Q/O f16  */
+    FA_KV_BF16 = 1,  /* K/V bf16, Q/O bf16 */
+    FA_KV_Q4_0 = 2,  /* K/V q4_0, Q/O f16  */
+};
+
+enum fa_status {
+    FA_OK = 0,
+    FA_ERR_NULL = -1,         /* a required pointer is NULL */
+    FA_ERR_SHAPE = -2,        /* negative size, Hq % Hkv != 0, or an index that overflows */
+    FA_ERR_DTYPE = -3,        /* kv_dtype is not one of enum fa_kv_dtype */
+    FA_ERR_UNSUPPORTED = -4,  /* valid but not built: D not in {64, 128}; decode rows > 16 */
+    FA_ERR_WORKSPACE = -5,    /* decode workspace missing or smaller than required */
+    FA_ERR_ALIGN = -6,        /* Q/O/K/V not 16-byte aligned (q4_0 K/V: 4-byte aligned) */
+    FA_ERR_HIP = -7,          /* the HIP runtime reported an error at launch */
+    FA_ERR_VALUE = -8,        /* scale not finite and > 0 */
+};
+
+/*
+ * Chunked / causal prefill: any Sq, Sk. One MFMA kernel launch.
+ *   q, o      device pointers, [B, Sq, Hq, D]
+ *   k, v      device pointers, [B, Sk, Hkv, D] (q4_0: [B, Sk, Hkv, D/32] blocks)
+ *   B, Hq, Hkv, Sq, Sk, D   sizes; Hq % Hkv == 0; D in {64, 128}; B, Sq, Sk >= 0
+ *   causal    0 = every query sees every key; else the rule above with causal_offset
+ *   scale     softmax scale, finite and > 0 (typically 1/sqrt(D))
+ *   kv_dtype  enum fa_kv_dtype
+ * Per row the kernel keeps its O accumulators and sum in the softmax frame it was last
+ * rescaled to and rescales only when a block maximum exceeds that frame by more than 10
+ * (natural-log units), as the mlxcel PR describes; Q is staged once per workgroup.
+ */
+int fa_prefill(const void *q, const void *k, const void *v, void *o,
+               int B, int Hq, int Hkv, int Sq, int Sk, int D,
+               int causal, int64_t causal_offset, float scale, int kv_dtype,
+               fa_stream_t stream);
+
+/*
+ * Bytes of workspace fa_decode needs for these sizes (0 when nothing is needed).
+ * The workspace holds one partial (running max, sum, unnormalised output row) per query
+ * row and key split; it is scratch between the split kernel and the merge kernel of one
+ * call and need not be initialised.
+ */
+size_t fa_decode_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Sk, int D);
+
+/*
+ * Decode: few query rows per KV head (Sq * Hq / Hkv <= 16), long Sk. The keys are cut
+ * into splits that run in parallel; each split writes a partial softmax state to the
+ * workspace and a second kernel merges the splits with a log-sum-exp combine. Arguments
+ * as fa_prefill plus the caller-owned workspace (>= fa_decode_workspace_bytes(...) bytes,
+ * 16-byte aligned). Calls that share a workspace must be ordered on one stream.
+ */
+int fa_decode(const void *q, const void *k, const void *v, void *o,
+              int B, int Hq, int Hkv, int Sq, int Sk, int D,
+              int causal, int64_t causal_offset, float scale, int kv_dtype,
+              void *workspace, size_t workspace_bytes, fa_stream_t stream);
+
+/*
+ * Dequantize n_blocks q4_0 blocks (18 bytes each, 2-byte aligned) with the same device
+ * routine the attention kernels use. out_f32 receives the exact values (c - 8) * d as
+ * float (n_blocks * 32 floats); out_f16 receives their f16 forms, rounded to nearest even
+ * (n_blocks * 32 halves). Either output may be NULL, not both.
+ */
+int fa_dequant_q4_0(const void *blocks, int64_t n_blocks, float *out_f32, void *out_f16,
+                    fa_stream_t stream);
+
+/* Static text for a status code. */
+const char *fa_strerror(int code);
+
+/* Library version: major * 10000 + minor * 100 + patch. */
+int fa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H */

@@ -1,0 +1,71 @@
+"""Helpers for the GPU parity tests: move seeded inputs to the device, call the HIP path through
+the C ABI binding, and compare with the CPU oracle on the same rounded inputs."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import attention_causal_gqa_attn_amd as fa
+import oracle
+import workloads as W
+
+# max-abs tolerance on attention outputs (N(0,1) inputs): f16 and q4_0 caches 1e-2, bf16 2e-2
+TOL = {"f16": 1e-2, "q4_0": 1e-2, "bf16": 2e-2}
+
+
+def say(msg: str) -> None:
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def to_dev(arr: np.ndarray, dtype: str) -> torch.Tensor:
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(arr)).cuda()
+
+
+def to_host(t: torch.Tensor) -> np.ndarray:
+    return t.float().cpu().numpy()
+
+
+def device_inputs(w: W.Workload, x: W.Inputs):
+    return to_dev(x.q, w.q_dtype), to_dev(x.k, w.kv), to_dev(x.v, w.kv)
+
+
+def gpu_prefill(w: W.Workload, x: W.Inputs) -> np.ndarray:
+    q, k, v = device_inputs(w, x)
+    o = fa.prefill(q, k, v, causal=w.causal, offset=w.causal_offset, scale=w.scale)
+    torch.cuda.synchronize()
+    return to_host(o)
+
+
+def gpu_decode(w: W.Workload, x: W.Inputs) -> np.ndarray:
+    q, k, v = device_inputs(w, x)
+    o = fa.decode(q, k, v, causal=w.causal, offset=w.causal_offset, scale=w.scale)
+    torch.cuda.synchronize()
+    return to_host(o)
+
+
+def oracle_out(w: W.Workload, x: W.Inputs, rows=None) -> np.ndarray:
+    return oracle.attention(x.q, x.k, x.v, q_dtype=w.q_dtype, kv_dtype=w.kv, causal=w.causal,
+                            offset=w.causal_offset, scale=w.scale, rows=rows)
+
+
+def sample_rows(w: W.Workload, n: int, seed: int = 0) -> np.ndarray:
+    """Flattened (b, i, h) rows: first, last and tile-boundary queries of every head, plus
+    random ones."""
+    rng = np.random.default_rng(seed)
+    edge_i = sorted({0, 1, 31, 32, 63, 64, 127, 128, w.Sq // 2, w.Sq - 2, w.Sq - 1} & set(range(w.Sq)))
+    rows = [(b * w.Sq + i) * w.Hq + h for b in range(w.B) for i in edge_i for h in range(w.Hq)]
+    rows += list(rng.integers(0, w.B * w.Sq * w.Hq, size=max(0, n - len(rows))))
+    return np.unique(np.asarray(rows, dtype=np.int64))
+
+
+def compare(w: W.Workload, got: np.ndarray, ref: np.ndarray, label: str) -> float:
+    assert np.all(np.isfinite(got)), f"{label}: non-finite output"
+    err = float(np.max(np.abs(got - ref))) if got.size else 0.0
+    say(f"  {label}: max|err| = {err:.3e} (tol {TOL[w.kv]:.0e}, {got.shape[0]} rows)")
+    assert err <= TOL[w.kv], f"{label}: max abs error {err} > {TOL[w.kv]}"
+    return err

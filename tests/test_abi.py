@@ -1,0 +1,143 @@
+"""CPU checks of the C ABI: libfa.so loads, exports every function include/fa.h declares, and
+rejects invalid arguments with the documented status codes before any HIP call (so no GPU is
+needed). No call here passes arguments that would reach a kernel launch."""
+import os
+import re
+
+import pytest
+
+import attention_causal_gqa_attn_amd as fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+P = 0x10000          # a 64 KiB-aligned fake device address: never dereferenced here
+ODD = P + 2          # 2-byte aligned only
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(fa_\w+)\s*\(", text, flags=re.M)))
+
+
+def header_enums():
+    text = open(HEADER).read()
+    return {k: int(v) for k, v in re.findall(r"\b(FA_\w+)\s*=\s*(-?\d+)", text)}
+
+
+def test_library_exports_every_declared_function():
+    lib = fa.load()
+    declared = header_functions()
+    assert set(declared) == set(fa.EXPORTS), declared
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_binding_constants_match_header():
+    enums = header_enums()
+    for name, value in enums.items():
+        assert getattr(fa, name) == value, name
+
+
+def test_version_and_strerror():
+    assert fa.fa_version() == 10000
+    codes = [v for k, v in header_enums().items() if k.startswith("FA_OK") or k.startswith("FA_ERR")]
+    texts = {fa.fa_strerror(c) for c in codes}
+    assert len(texts) == len(codes)
+    assert fa.fa_strerror(12345) == "unknown status code"
+
+
+def prefill(**kw):
+    args = dict(q=P, k=P, v=P, o=P, B=1, Hq=32, Hkv=8, Sq=16, Sk=64, D=128, causal=1,
+                causal_offset=48, scale=0.088, kv_dtype=0, stream=None)
+    args.update(kw)
+    return fa.fa_prefill(*args.values())
+
+
+def decode(**kw):
+    args = dict(q=P, k=P, v=P, o=P, B=4, Hq=32, Hkv=8, Sq=1, Sk=4096, D=128, causal=1,
+                causal_offset=4095, scale=0.088, kv_dtype=2, workspace=P, workspace_bytes=0,
+                stream=None)
+    args.update(kw)
+    return fa.fa_decode(*args.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(kv_dtype=3), fa.FA_ERR_DTYPE),
+    (dict(kv_dtype=-1), fa.FA_ERR_DTYPE),
+    (dict(Hq=30), fa.FA_ERR_SHAPE),
+    (dict(Hkv=0), fa.FA_ERR_SHAPE),
+    (dict(B=-1), fa.FA_ERR_SHAPE),
+    (dict(Sq=-5), fa.FA_ERR_SHAPE),
+    (dict(Sk=-1), fa.FA_ERR_SHAPE),
+    (dict(D=0), fa.FA_ERR_SHAPE),
+    (dict(D=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(D=256), fa.FA_ERR_UNSUPPORTED),
+    (dict(scale=0.0), fa.FA_ERR_VALUE),
+    (dict(scale=-0.1), fa.FA_ERR_VALUE),
+    (dict(scale=float("nan")), fa.FA_ERR_VALUE),
+    (dict(scale=float("inf")), fa.FA_ERR_VALUE),
+    (dict(q=None), fa.FA_ERR_NULL),
+    (dict(o=None), fa.FA_ERR_NULL),
+    (dict(k=None), fa.FA_ERR_NULL),
+    (dict(v=None), fa.FA_ERR_NULL),
+    (dict(q=ODD), fa.FA_ERR_ALIGN),
+    (dict(o=P + 8), fa.FA_ERR_ALIGN),
+    (dict(k=P + 4), fa.FA_ERR_ALIGN),
+    (dict(v=P + 4, kv_dtype=1), fa.FA_ERR_ALIGN),
+    (dict(v=ODD, kv_dtype=2), fa.FA_ERR_ALIGN),
+    (dict(B=1 << 30, Sq=1 << 30, Hq=1 << 20, Hkv=1 << 20), fa.FA_ERR_SHAPE),
+])
+def test_prefill_rejects(kw, code):
+    assert prefill(**kw) == code
+
+
+def test_prefill_empty_is_a_no_op():
+    # nothing to compute: accepted without touching the device, even with NULL data
+    assert prefill(B=0, q=None, o=None, k=None, v=None) == fa.FA_OK
+    assert prefill(Sq=0, q=None, o=None) == fa.FA_OK
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(Sq=5), fa.FA_ERR_UNSUPPORTED),           # 5 * 4 rows > 16
+    (dict(Hq=64, Hkv=2), fa.FA_ERR_UNSUPPORTED),   # 32 rows
+    (dict(workspace=None, workspace_bytes=1 << 30), fa.FA_ERR_WORKSPACE),
+    (dict(workspace_bytes=100), fa.FA_ERR_WORKSPACE),
+    (dict(workspace=P + 4, workspace_bytes=1 << 30), fa.FA_ERR_ALIGN),
+    (dict(kv_dtype=7), fa.FA_ERR_DTYPE),
+    (dict(D=80), fa.FA_ERR_UNSUPPORTED),
+    (dict(k=P + 2), fa.FA_ERR_ALIGN),
+])
+def test_decode_rejects(kw, code):
+    assert decode(**kw) == code
+
+
+def test_decode_workspace_bound():
+    n = fa.fa_decode_workspace_bytes(4, 32, 8, 1, 32768, 128)
+    # about 1024 splits in all, each split a row of 4 heads x (128 outputs + frame + sum) f32
+    assert n == 4 * 8 * 32 * 4 * 130 * 4
+    assert fa.fa_decode_workspace_bytes(4, 32, 8, 1, 0, 128) == 4 * 8 * 1 * 4 * 130 * 4
+    assert fa.fa_decode_workspace_bytes(0, 32, 8, 1, 100, 128) == 0
+    assert fa.fa_decode_workspace_bytes(1, 32, 8, 1, 100, 96) == 0
+    # a workspace one byte short of the bound is refused for the largest causal offsets too
+    for off in (4095, 100000):
+        assert decode(workspace_bytes=fa.fa_decode_workspace_bytes(4, 32, 8, 1, 4096, 128) - 1,
+                      causal_offset=off) == fa.FA_ERR_WORKSPACE
+
+
+def test_dequant_rejects():
+    assert fa.fa_dequant_q4_0(P, -1, P, P, None) == fa.FA_ERR_SHAPE
+    assert fa.fa_dequant_q4_0(P, 0, None, None, None) == fa.FA_OK
+    assert fa.fa_dequant_q4_0(None, 4, P, P, None) == fa.FA_ERR_NULL
+    assert fa.fa_dequant_q4_0(P, 4, None, None, None) == fa.FA_ERR_NULL
+    assert fa.fa_dequant_q4_0(P + 1, 4, P, P, None) == fa.FA_ERR_ALIGN
+    assert fa.fa_dequant_q4_0(P, 4, P + 2, P, None) == fa.FA_ERR_ALIGN
+
+
+def test_binding_refuses_without_library(monkeypatch, tmp_path):
+    """The product path fails loudly when the HIP library is missing: no fallback."""
+    monkeypatch.setattr(fa, "_lib", None)
+    monkeypatch.setattr(fa, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        fa.load()

@@ -1,0 +1,171 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the same seeded,
+rounded inputs. Tolerances: max-abs 1e-2 (f16, q4_0) / 2e-2 (bf16) on attention outputs;
+q4_0 dequantized values bit-exact. Full-size workloads compare sampled rows."""
+import numpy as np
+import pytest
+import torch
+
+import attention_causal_gqa_attn_amd as fa
+import oracle
+import workloads as W
+from gpu_cases import (TOL, compare, gpu_decode, gpu_prefill, oracle_out, sample_rows, say,
+                       to_dev)
+
+pytestmark = pytest.mark.gpu
+
+
+def wl(name, B, Hq, Hkv, Sq, Sk, D, kv="f16", causal=True, offset=None, seed=0):
+    return W.Workload(name, B=B, Hq=Hq, Hkv=Hkv, Sq=Sq, Sk=Sk, D=D, kv=kv, causal=causal,
+                      offset=offset, seed=seed)
+
+
+# ---------------------------------------------------------------------------------------------
+# q4_0 dequantization: bit-exact against the oracle over every scale pattern and code
+# ---------------------------------------------------------------------------------------------
+
+def test_dequant_q4_0_exhaustive():
+    say("dequant q4_0: 65536 scale patterns x 16 codes")
+    d_bits = np.arange(65536, dtype=np.uint16)
+    lo = np.arange(16, dtype=np.uint8)
+    codes = np.tile(np.concatenate([lo, (lo * 7 + 3) % 16]), (65536, 1))
+    blocks = W.pack_q4_0_blocks(d_bits, codes)
+    ref32, ref16 = oracle.dequant_q4_0(blocks)
+    f32, f16 = fa.dequant_q4_0(torch.from_numpy(blocks.reshape(-1)).cuda())
+    torch.cuda.synchronize()
+    got32 = f32.cpu().numpy()
+    got16 = f16.cpu().numpy().view(np.uint16)
+    nan = np.isnan(ref32)
+    assert np.array_equal(np.isnan(got32), nan)
+    assert np.array_equal(got32[~nan].view(np.uint32), ref32[~nan].view(np.uint32))
+    nan16 = ((ref16 & 0x7C00) == 0x7C00) & ((ref16 & 0x3FF) != 0)
+    assert np.array_equal(got16[~nan16], ref16[~nan16])
+    assert np.all(((got16[nan16] & 0x7C00) == 0x7C00) & ((got16[nan16] & 0x3FF) != 0))
+
+
+# ---------------------------------------------------------------------------------------------
+# prefill: whole outputs on shapes that span several tiles and ragged tails
+# ---------------------------------------------------------------------------------------------
+
+PREFILL_SMALL = [
+    W.WORKLOADS["tiny"],
+    W.WORKLOADS["p2check"],
+    wl("gqa4_ragged_f16", 2, 8, 2, 100, 300, 128, "f16", True, 200, seed=21),
+    wl("gqa4_ragged_bf16", 2, 8, 2, 100, 300, 128, "bf16", True, 200, seed=22),
+    wl("gqa4_ragged_q4_0", 2, 8, 2, 100, 300, 128, "q4_0", True, 200, seed=23),
+    wl("d64_gqa4_f16", 1, 8, 2, 130, 130, 64, "f16", True, 0, seed=24),
+    wl("d64_q4_0", 1, 4, 1, 70, 200, 64, "q4_0", True, 130, seed=25),
+    wl("d64_bf16_g8_noncausal", 1, 8, 1, 33, 65, 64, "bf16", False, 0, seed=26),
+    wl("noncausal_f16", 2, 4, 4, 77, 123, 128, "f16", False, 0, seed=27),
+    wl("negative_offset", 1, 4, 2, 64, 64, 128, "f16", True, -20, seed=28),
+    wl("g3_bf16", 1, 6, 2, 50, 90, 128, "bf16", True, 40, seed=29),
+    wl("g8_f16", 1, 16, 2, 40, 100, 128, "f16", True, 60, seed=30),
+    wl("mqa32_d64", 1, 32, 1, 20, 50, 64, "f16", True, 30, seed=31),
+    wl("sq1_q4_0", 2, 32, 8, 1, 1000, 128, "q4_0", True, 999, seed=32),
+    wl("sk1", 1, 4, 1, 3, 1, 128, "f16", True, 0, seed=33),
+    wl("offset_past_end", 1, 4, 2, 16, 64, 128, "f16", True, 10 ** 6, seed=34),
+    wl("long_rows_q4_0", 1, 8, 2, 40, 1500, 128, "q4_0", True, 1460, seed=35),
+]
+
+
+@pytest.mark.parametrize("w", PREFILL_SMALL, ids=[w.name for w in PREFILL_SMALL])
+def test_prefill_matches_oracle(w):
+    say(f"prefill {w}")
+    x = W.generate(w)
+    compare(w, gpu_prefill(w, x).reshape(-1, w.D), oracle_out(w, x).reshape(-1, w.D), w.name)
+
+
+def test_prefill_no_keys_gives_zeros():
+    w = wl("sk0", 1, 4, 1, 3, 0, 128, "f16", True, 0, seed=36)
+    say(f"prefill {w}")
+    x = W.generate(w)
+    assert np.all(gpu_prefill(w, x) == 0)
+
+
+@pytest.mark.parametrize("kv", ["f16", "bf16", "q4_0"])
+def test_single_visible_key_is_exact(kv):
+    """A row that sees exactly one key returns that key's V row (as stored / dequantized to f16)
+    bit for bit: P = 1, l = 1. For q4_0 this checks the V-side dequant exactly."""
+    w = wl(f"one_key_{kv}", 1, 8, 2, 8, 40, 128, kv, True, 0, seed=37)
+    say(f"prefill {w}")
+    x = W.generate(w)
+    got = gpu_prefill(w, x)
+    ref = oracle_out(w, x)
+    for h in range(w.Hq):
+        row = ref[0, 0, h]       # = V[0, h // 4] exactly (f32)
+        if kv == "bf16":
+            exact = torch.from_numpy(row).to(torch.bfloat16).float().numpy()
+        else:
+            exact = row.astype(np.float16).astype(np.float32)
+        assert np.array_equal(got[0, 0, h], exact), h
+
+
+# ---------------------------------------------------------------------------------------------
+# prefill at the chunked-prefill sizes (2048 queries at the end of 2K/8K/16K keys, GQA 32/8,
+# D=128), with the launch configuration the benchmark times; sampled rows
+# ---------------------------------------------------------------------------------------------
+
+FULL = ["prefill_2k_f16", "prefill_8k_f16", "prefill_16k_f16", "prefill_2k_bf16",
+        "prefill_8k_bf16", "prefill_16k_bf16", "prefill_2k_f16_ramp", "prefill_16k_f16_ramp",
+        "prefill_2k_bf16_ramp", "prefill_16k_bf16_ramp", "prefill_16k_q4_0"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_prefill_full_size_sampled(name):
+    w = W.WORKLOADS[name]
+    say(f"prefill {w}")
+    x = W.generate(w)
+    got = gpu_prefill(w, x).reshape(-1, w.D)
+    rows = sample_rows(w, 512, seed=1)
+    compare(w, got[rows], oracle_out(w, x, rows=rows), name)
+
+
+def test_prefill_second_seeds():
+    for name, seed in [("prefill_2k_f16", 11), ("prefill_2k_bf16", 12)]:
+        w = W.WORKLOADS[name].with_(seed=seed)
+        say(f"prefill {w}")
+        x = W.generate(w)
+        got = gpu_prefill(w, x).reshape(-1, w.D)
+        rows = sample_rows(w, 256, seed=seed)
+        compare(w, got[rows], oracle_out(w, x, rows=rows), f"{name}/seed{seed}")
+
+
+# ---------------------------------------------------------------------------------------------
+# decode (split-K + log-sum-exp merge)
+# ---------------------------------------------------------------------------------------------
+
+DECODE = [
+    W.WORKLOADS["decode_q4_0"],
+    wl("decode_f16", 2, 32, 8, 1, 5000, 128, "f16", True, 4999, seed=41),
+    wl("decode_bf16_sq4", 1, 8, 2, 4, 3000, 128, "bf16", True, 2996, seed=42),
+    wl("decode_q4_0_d64_sq2", 3, 16, 4, 2, 777, 64, "q4_0", True, 775, seed=43),
+    wl("decode_short", 1, 4, 1, 1, 10, 128, "f16", True, 9, seed=44),
+    wl("decode_noncausal", 2, 4, 4, 3, 200, 128, "f16", False, 0, seed=45),
+    wl("decode_negative_offset", 1, 4, 1, 4, 100, 128, "f16", True, -2, seed=46),
+    wl("decode_mha_d64", 2, 8, 8, 16, 300, 64, "f16", True, 284, seed=47),
+    wl("decode_one_key", 1, 8, 2, 1, 1, 128, "q4_0", True, 0, seed=48),
+]
+
+
+@pytest.mark.parametrize("w", DECODE, ids=[w.name for w in DECODE])
+def test_decode_matches_oracle(w):
+    say(f"decode {w}")
+    x = W.generate(w)
+    compare(w, gpu_decode(w, x).reshape(-1, w.D), oracle_out(w, x).reshape(-1, w.D), w.name)
+
+
+def test_decode_no_keys_gives_zeros():
+    w = wl("decode_sk0", 2, 8, 2, 1, 0, 128, "f16", True, -1, seed=49)
+    say(f"decode {w}")
+    x = W.generate(w)
+    assert np.all(gpu_decode(w, x) == 0)
+
+
+def test_decode_equals_prefill_on_decode_shape():
+    """The two entry points compute the same function: on the decode workload they agree to
+    well within the parity tolerance of each."""
+    w = W.WORKLOADS["decode_q4_0"].with_(Sk=4096, offset=None)
+    say(f"decode vs prefill {w}")
+    x = W.generate(w)
+    a = gpu_decode(w, x)
+    b = gpu_prefill(w, x)
+    assert float(np.max(np.abs(a - b))) <= TOL[w.kv]
