@@ -94,8 +94,14 @@ def cpu_baseline(w, x, seconds: float):
         keys = np.clip(i + w.causal_offset + 1, 0, w.Sk)
         return dt, int(4 * w.D * keys.sum()), n
 
-    dt, _, n = run(max(threads, 16))
-    n_big = int(min(total, max(threads, n * seconds / max(dt, 1e-3))))
+    # the oracle widens all of K and V once per call, a fixed cost: grow the sample until the
+    # per-row work dominates, then size the timed sample to about `seconds`
+    n = max(threads, 16)
+    dt, _, _ = run(n)
+    while dt < seconds / 8 and n < total:
+        n = min(total, 4 * n)
+        dt, _, _ = run(n)
+    n_big = int(min(total, max(n, n * seconds / max(dt, 1e-3))))
     dt, flops, n = run(n_big)
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"{n} of {total} query rows of the 2Kx16K f16 prefill (uniform random), "
