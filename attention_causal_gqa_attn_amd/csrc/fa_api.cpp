@@ -44,6 +44,9 @@ int check_attention(const void *q, const void *k, const void *v, void *o, int B,
     const int64_t nk = mul4(B, Sk, Hkv, D);
     if (nq < 0 || nk < 0 || Sk > INT32_MAX - 2 * 64)
         return FA_ERR_SHAPE;
+    // per-thread tile offsets are 32-bit: 64 key rows of all KV heads must span < 4 GiB
+    if ((int64_t)Hkv * D * 2 * 64 > (int64_t)UINT32_MAX)
+        return FA_ERR_UNSUPPORTED;
     if ((nq > 0 && (!q || !o)) || (nk > 0 && (!k || !v)))
         return FA_ERR_NULL;
     const uintptr_t kv_align = kv_dtype == FA_KV_Q4_0 ? 4 : 16;

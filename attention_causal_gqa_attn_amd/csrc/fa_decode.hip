@@ -29,24 +29,84 @@ struct DecodeParams {
     float *part;           // [B][Hkv][n_split][rows][D + 2]
 };
 
+// One 64-key tile of the split: each wave takes 16 keys.
+template <int D, bool BF>
+__device__ __forceinline__ void decode_tile(const uint16_t *lk, const uint16_t *lv, int k0,
+                                            int wave, int quad, int r, int64_t rowlim, float c,
+                                            const u32x4 *qf, f32x4 *acc, float &frame,
+                                            float &lsum)
+{
+    using Geo = TileGeom<D>;
+    const int kw = k0 + 16 * wave;                  // this wave's first key
+    if (!__any(kw <= rowlim))                       // wave-uniform: no row sees these keys
+        return;
+    f32x4 sc = (f32x4){};
+    const uint16_t *kr = lk + (16 * wave + r) * Geo::kStride + 8 * quad;
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk)
+        sc = mfma16<BF>(*(const u32x4 *)(kr + 32 * kk), qf[kk], sc);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        if (kw + 4 * quad + i > rowlim)
+            sc[i] = -INFINITY;
+    float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float m2 = mx * c;
+    const bool need = m2 > frame + kRescaleMarginLog2;
+    if (__any(need)) {
+        const float alpha = need ? exp2_fast(frame - m2) : 1.0f;
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt)
+            acc[dt] *= alpha;
+        lsum *= alpha;
+        frame = need ? m2 : frame;
+    }
+    const float fr = (frame == -INFINITY) ? 0.0f : frame;
+    u32x2 pf;
+    {
+        const float p0 = exp2_fast(__builtin_fmaf(sc[0], c, -fr));
+        const float p1 = exp2_fast(__builtin_fmaf(sc[1], c, -fr));
+        const float p2 = exp2_fast(__builtin_fmaf(sc[2], c, -fr));
+        const float p3 = exp2_fast(__builtin_fmaf(sc[3], c, -fr));
+        pf[0] = pack2<BF>(p0, p1);
+        pf[1] = pack2<BF>(p2, p3);
+        lsum = sum2<BF>(pf[1], sum2<BF>(pf[0], lsum));
+    }
+    const uint16_t *vr = lv + r * Geo::vStride + 16 * wave + 4 * quad;
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt)
+        acc[dt] = mfma16k16<BF>(*(const u32x2 *)(vr + 16 * dt * Geo::vStride), pf, acc[dt]);
+}
+
+// Tiles whose global loads are in flight at once per workgroup: decode has little work per
+// byte, so keeping HBM busy needs several tiles outstanding. The q4_0 staging registers are
+// small (10 per thread per tile), the 16-bit ones are not.
+template <int KV>
+constexpr int kDecodeSets = KV == KV_Q4_0 ? 2 : 1;
+
 template <int D, int KV>
-__global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeParams p)
+__global__ __launch_bounds__(kThreads, 4) void decode_split_kernel(DecodeParams p)
 {
     constexpr bool BF = (KV == KV_BF16);
+    constexpr int NSETS = kDecodeSets<KV>;
     using Geo = TileGeom<D>;
-    constexpr int kLdsElems = 2 * Geo::stage > 4 * 16 * D * 2 + 256 ? 2 * Geo::stage
-                                                                      : 4 * 16 * D * 2 + 256;
+    // one K + V^T tile, reused afterwards for the cross-wave combine
+    constexpr int kLdsElems = Geo::stage > 4 * 16 * D * 2 + 256 ? Geo::stage
+                                                                : 4 * 16 * D * 2 + 256;
     __shared__ __attribute__((aligned(16))) uint16_t lds[kLdsElems];
 
     const AttnArgs &a = p.a;
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int quad = lane >> 4, r = lane & 15;     // C layout: keys 4*quad + i, row r
 
+    // KV head fastest: the Hkv workgroups of one key range go to one XCD together, and since
+    // a key's rows of all KV heads are contiguous they share that XCD's L2 lines
     int rest = xcd_remap(blockIdx.x, gridDim.x);
-    const int s = rest % p.n_split;
-    rest /= p.n_split;
     const int kvh = rest % a.Hkv;
-    const int b = rest / a.Hkv;
+    rest /= a.Hkv;
+    const int s = rest % p.n_split;
+    const int b = rest / p.n_split;
 
     const int64_t ks = (int64_t)s * p.split_len;
     const int64_t ke = min(ks + p.split_len, p.kend);
@@ -70,6 +130,9 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeParams 
 #pragma unroll
         for (int kk = 0; kk < D / 32; ++kk)
             qf[kk] = row_on ? *(const u32x4 *)(qp + 32 * kk + 8 * quad) : (u32x4){};
+#pragma unroll
+        for (int kk = 0; kk < D / 32; ++kk)
+            settle(qf[kk]);
     }
 
     f32x4 acc[D / 16];
@@ -78,65 +141,29 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeParams 
         acc[dt] = (f32x4){};
     float frame = -INFINITY, lsum = 0.0f;
 
-    TileLoader<D, KV> ld;
-    ld.init(a.k, a.v, (int64_t)b * a.Sk * a.Hkv + kvh, a.Hkv, a.Sk, t);
-    if (nb > 0) {
-        ld.load((int)ks);
-        ld.store(lds, lds + Geo::kElems);
+    // tile kb is staged by loader kb % NSETS; NSETS tiles are in flight ahead of the compute
+    TileLoader<D, KV> ld[NSETS];
+#pragma unroll
+    for (int u = 0; u < NSETS; ++u) {
+        ld[u].init(a.k, a.v, (int64_t)b * a.Sk * a.Hkv + kvh, a.Hkv, a.Sk, t);
+        if (u < nb)
+            ld[u].load((int)ks + u * kBN);
     }
-    __syncthreads();
-
-    for (int kb = 0; kb < nb; ++kb) {
-        const int k0 = (int)ks + kb * kBN;
-        if (kb + 1 < nb)
-            ld.load(k0 + kBN);
-        const uint16_t *lk = lds + (kb & 1) * Geo::stage;
-        const uint16_t *lv = lk + Geo::kElems;
-        const int kw = k0 + 16 * wave;              // this wave's first key
-
-        if (__any(kw <= rowlim)) {          // wave-uniform: some row sees a key here
-            f32x4 sc = (f32x4){};
-            const uint16_t *kr = lk + (16 * wave + r) * Geo::kStride + 8 * quad;
+    uint16_t *lk = lds, *lv = lds + Geo::kElems;
+    for (int kb0 = 0; kb0 < nb; kb0 += NSETS) {
 #pragma unroll
-            for (int kk = 0; kk < D / 32; ++kk)
-                sc = mfma16<BF>(*(const u32x4 *)(kr + 32 * kk), qf[kk], sc);
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                if (kw + 4 * quad + i > rowlim)
-                    sc[i] = -INFINITY;
-            float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
-            mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-            mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-            const float m2 = mx * a.c;
-            const bool need = m2 > frame + kRescaleMarginLog2;
-            if (__any(need)) {
-                const float alpha = need ? exp2_fast(frame - m2) : 1.0f;
-#pragma unroll
-                for (int dt = 0; dt < D / 16; ++dt)
-                    acc[dt] *= alpha;
-                lsum *= alpha;
-                frame = need ? m2 : frame;
+        for (int u = 0; u < NSETS; ++u) {
+            const int kb = kb0 + u;
+            if (kb < nb) {                          // uniform over the workgroup
+                ld[u].store(lk, lv);
+                __syncthreads();
+                if (kb + NSETS < nb)
+                    ld[u].load((int)ks + (kb + NSETS) * kBN);
+                decode_tile<D, BF>(lk, lv, (int)ks + kb * kBN, wave, quad, r, rowlim, a.c, qf,
+                                   acc, frame, lsum);
+                __syncthreads();
             }
-            const float fr = (frame == -INFINITY) ? 0.0f : frame;
-            u32x2 pf;
-            {
-                const float p0 = exp2_fast(__builtin_fmaf(sc[0], a.c, -fr));
-                const float p1 = exp2_fast(__builtin_fmaf(sc[1], a.c, -fr));
-                const float p2 = exp2_fast(__builtin_fmaf(sc[2], a.c, -fr));
-                const float p3 = exp2_fast(__builtin_fmaf(sc[3], a.c, -fr));
-                pf[0] = pack2<BF>(p0, p1);
-                pf[1] = pack2<BF>(p2, p3);
-                lsum = sum2<BF>(pf[1], sum2<BF>(pf[0], lsum));
-            }
-            const uint16_t *vr = lv + r * Geo::vStride + 16 * wave + 4 * quad;
-#pragma unroll
-            for (int dt = 0; dt < D / 16; ++dt)
-                acc[dt] = mfma16k16<BF>(*(const u32x2 *)(vr + 16 * dt * Geo::vStride), pf, acc[dt]);
         }
-        if (kb + 1 < nb)
-            ld.store(lds + ((kb + 1) & 1) * Geo::stage,
-                     lds + ((kb + 1) & 1) * Geo::stage + Geo::kElems);
-        __syncthreads();
     }
 
     // ---- combine the 4 waves' states of each row, write the split's partial ---------------

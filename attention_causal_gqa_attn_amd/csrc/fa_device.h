@@ -101,6 +101,11 @@ __device__ __forceinline__ float sum2(uint32_t pair, float acc)
     }
 }
 
+// Make the compiler treat `x` as read here, so that the wait for its global load is placed
+// here and not inside a later loop (where an in-order wait on it would also wait for every
+// load issued after it, e.g. the next tile's).
+__device__ __forceinline__ void settle(const u32x4 &x) { asm volatile("" ::"v"(x)); }
+
 // Value held by lane l ^ 32.
 __device__ __forceinline__ float swap_halves(float x) { return __shfl_xor(x, 32, 64); }
 

@@ -96,6 +96,9 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p)
 #pragma unroll
     for (int s = 0; s < D / 16; ++s)
         qf[s] = *(const u32x4 *)(qp + 16 * s + 8 * half);
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s)
+        settle(qf[s]);
 
     f32x16 acc[D / 32];
 #pragma unroll
@@ -131,16 +134,16 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p)
                 for (int st = 0; st < D / 16; ++st)
                     s[hf] = mfma32<BF>(*(const u32x4 *)(kr + 16 * st), qf[st], s[hf]);
             }
-            // causal / sequence-end mask, only where a key can exceed the row's limit
+            // causal / sequence-end mask, only where a key can exceed the row's limit; keys are
+            // compared relative to the tile start, in 32 bits
             if ((int64_t)k0 + kBN - 1 > klim_min) {
+                const int lim = (int)max(min(klim - k0, (int64_t)kBN), (int64_t)-1) - 8 * half;
 #pragma unroll
                 for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        const int64_t key = k0 + hf * 32 + 16 * (i / 8) + 8 * half + (i % 8);
-                        if (key > klim)
+                    for (int i = 0; i < 16; ++i)
+                        if (hf * 32 + 16 * (i / 8) + (i % 8) > lim)
                             s[hf][i] = -INFINITY;
-                    }
             }
             // block maximum of the row (this lane's 32 keys, then lane l^32's)
             float mx = s[0][0];

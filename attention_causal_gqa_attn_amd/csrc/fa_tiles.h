@@ -43,48 +43,70 @@ struct TileLoader {
     static constexpr int KPT = D / 32;    // V keys per thread
     static constexpr int VCOLS = kBN / KPT;
 
-    const uint16_t *kbase, *vbase;        // first element of (b, key 0, kvh)
-    int64_t row;                          // elements between consecutive keys
+    const uint8_t *kbase, *vbase;         // first byte of (b, key 0, kvh)
+    uint32_t row;                         // bytes between consecutive keys
     int Sk, t;
+    uint32_t koff[KC], voff[KPT];         // per-thread byte offsets inside a tile
     u32x4 kr[KC], vr[KPT];
+
+    __device__ __forceinline__ int k_key(int p) const { return (p * kThreads + t) / (D / 8); }
+    __device__ __forceinline__ int k_dc(int p) const { return (p * kThreads + t) % (D / 8); }
+    __device__ __forceinline__ int v_key0() const { return KPT * (t % VCOLS); }
+    __device__ __forceinline__ int v_dc() const { return t / VCOLS; }
 
     // head_off_rows: key-row index of (b, key 0, kvh); row_rows: key rows between keys (Hkv)
     __device__ void init(const void *k, const void *v, int64_t head_off_rows, int64_t row_rows,
                          int Sk_, int t_)
     {
-        kbase = (const uint16_t *)k + head_off_rows * D;
-        vbase = (const uint16_t *)v + head_off_rows * D;
-        row = row_rows * D;
+        kbase = (const uint8_t *)k + head_off_rows * D * 2;
+        vbase = (const uint8_t *)v + head_off_rows * D * 2;
+        row = (uint32_t)(row_rows * D * 2);
         Sk = Sk_;
         t = t_;
+#pragma unroll
+        for (int p = 0; p < KC; ++p)
+            koff[p] = (uint32_t)k_key(p) * row + (uint32_t)k_dc(p) * 16u;
+#pragma unroll
+        for (int r = 0; r < KPT; ++r)
+            voff[r] = (uint32_t)(v_key0() + r) * row + (uint32_t)v_dc() * 16u;
     }
 
-    __device__ void load(int k0)
+    // Global loads of the tile starting at key k0 (k0 < Sk). The tile base is uniform and the
+    // per-thread part a 32-bit offset; in the last, partial tile keys past the end repeat the
+    // last key.
+    __device__ __forceinline__ void load(int k0)
     {
+        const uint8_t *kt = kbase + (int64_t)k0 * row;
+        const uint8_t *vt = vbase + (int64_t)k0 * row;
+        if (k0 + kBN <= Sk) {
 #pragma unroll
-        for (int p = 0; p < KC; ++p) {
-            const int id = p * kThreads + t;
-            const int key = id / (D / 8), dc = id % (D / 8);
-            const int64_t j = min(k0 + key, Sk - 1);
-            kr[p] = *(const u32x4 *)(kbase + j * row + dc * 8);
-        }
-        const int key0 = KPT * (t % VCOLS), dc = t / VCOLS;
+            for (int p = 0; p < KC; ++p)
+                kr[p] = *(const u32x4 *)(kt + koff[p]);
 #pragma unroll
-        for (int r = 0; r < KPT; ++r) {
-            const int64_t j = min(k0 + key0 + r, Sk - 1);
-            vr[r] = *(const u32x4 *)(vbase + j * row + dc * 8);
+            for (int r = 0; r < KPT; ++r)
+                vr[r] = *(const u32x4 *)(vt + voff[r]);
+        } else {
+            const int last = Sk - 1 - k0;
+#pragma unroll
+            for (int p = 0; p < KC; ++p) {
+                const uint32_t off = (uint32_t)min(k_key(p), last) * row + (uint32_t)k_dc(p) * 16u;
+                kr[p] = *(const u32x4 *)(kt + off);
+            }
+#pragma unroll
+            for (int r = 0; r < KPT; ++r) {
+                const uint32_t off =
+                    (uint32_t)min(v_key0() + r, last) * row + (uint32_t)v_dc() * 16u;
+                vr[r] = *(const u32x4 *)(vt + off);
+            }
         }
     }
 
-    __device__ void store(uint16_t *lk, uint16_t *lv) const
+    __device__ __forceinline__ void store(uint16_t *lk, uint16_t *lv) const
     {
 #pragma unroll
-        for (int p = 0; p < KC; ++p) {
-            const int id = p * kThreads + t;
-            const int key = id / (D / 8), dc = id % (D / 8);
-            *(u32x4 *)(lk + key * G::kStride + dc * 8) = kr[p];
-        }
-        const int key0 = KPT * (t % VCOLS), dc = t / VCOLS;
+        for (int p = 0; p < KC; ++p)
+            *(u32x4 *)(lk + k_key(p) * G::kStride + k_dc(p) * 8) = kr[p];
+        const int key0 = v_key0(), dc = v_dc();
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
@@ -110,7 +132,7 @@ struct TileLoader<D, KV_Q4_0> {
     static constexpr int ROWB = NB * 18;        // bytes per key row
 
     const uint8_t *base;                        // K or V, first byte of (b, key 0, kvh)
-    int64_t row;                                // bytes between consecutive keys
+    uint32_t row;                               // bytes between consecutive keys
     int Sk, tensor, kp, blk, aligned, mis;
     uint32_t w[2][5];
 
@@ -125,18 +147,23 @@ struct TileLoader<D, KV_Q4_0> {
         aligned = off & ~3;
         mis = off & 3;
         base = (const uint8_t *)(tensor ? v : k) + head_off_rows * ROWB;
-        row = row_rows * ROWB;
+        row = (uint32_t)(row_rows * ROWB);
         Sk = Sk_;
     }
 
-    __device__ void load(int k0)
+    // Global loads of the tile starting at key k0 (k0 < Sk); in the last, partial tile keys
+    // past the end repeat the last key.
+    __device__ __forceinline__ void load(int k0)
     {
         if (tensor >= 2)
             return;
+        const uint8_t *tile = base + (int64_t)k0 * row;
+        const int last = Sk - 1 - k0;
+        const bool full = k0 + kBN <= Sk;
 #pragma unroll
         for (int r = 0; r < 2; ++r) {
-            const int64_t j = min(k0 + 2 * kp + r, Sk - 1);
-            const uint32_t *p = (const uint32_t *)(base + j * row + aligned);
+            const uint32_t key = full ? (uint32_t)(2 * kp + r) : (uint32_t)min(2 * kp + r, last);
+            const uint32_t *p = (const uint32_t *)(tile + key * row + (uint32_t)aligned);
 #pragma unroll
             for (int i = 0; i < 5; ++i)
                 w[r][i] = p[i];
