@@ -85,8 +85,13 @@ __device__ __forceinline__ void decode_tile(const uint16_t *lk, const uint16_t *
 template <int KV>
 constexpr int kDecodeSets = KV == KV_Q4_0 ? 2 : 1;
 
+// Waves per SIMD the register budget is sized for: 4 workgroups per CU for q4_0 (small
+// staging registers), 3 for the 16-bit caches (16 staging registers per thread).
+template <int KV>
+constexpr int kDecodeOccupancy = KV == KV_Q4_0 ? 4 : 3;
+
 template <int D, int KV>
-__global__ __launch_bounds__(kThreads, 4) void decode_split_kernel(DecodeParams p)
+__global__ __launch_bounds__(kThreads, kDecodeOccupancy<KV>) void decode_split_kernel(DecodeParams p)
 {
     constexpr bool BF = (KV == KV_BF16);
     constexpr int NSETS = kDecodeSets<KV>;
@@ -144,13 +149,36 @@ __global__ __launch_bounds__(kThreads, 4) void decode_split_kernel(DecodeParams 
     // tile kb is staged by loader kb % NSETS; NSETS tiles are in flight ahead of the compute
     TileLoader<D, KV> ld[NSETS];
 #pragma unroll
-    for (int u = 0; u < NSETS; ++u) {
+    for (int u = 0; u < NSETS; ++u)
         ld[u].init(a.k, a.v, (int64_t)b * a.Sk * a.Hkv + kvh, a.Hkv, a.Sk, t);
-        if (u < nb)
-            ld[u].load((int)ks + u * kBN);
-    }
     uint16_t *lk = lds, *lv = lds + Geo::kElems;
-    for (int kb0 = 0; kb0 < nb; kb0 += NSETS) {
+    int kb0 = 0;
+    if (nb >= 2 * NSETS) {
+        // Steady state: the prologue and every iteration issue the same loads in the same
+        // order, so the compiler's in-order load accounting stays exact and storing set u
+        // waits only for set u, not for the sets issued after it.
+#pragma unroll
+        for (int u = 0; u < NSETS; ++u)
+            ld[u].load((int)ks + u * kBN);
+        for (; kb0 + 2 * NSETS <= nb; kb0 += NSETS) {
+#pragma unroll
+            for (int u = 0; u < NSETS; ++u) {
+                ld[u].store(lk, lv);
+                __syncthreads();
+                ld[u].load((int)ks + (kb0 + u + NSETS) * kBN);
+                decode_tile<D, BF>(lk, lv, (int)ks + (kb0 + u) * kBN, wave, quad, r, rowlim,
+                                   a.c, qf, acc, frame, lsum);
+                __syncthreads();
+            }
+        }
+    } else {
+#pragma unroll
+        for (int u = 0; u < NSETS; ++u)
+            if (u < nb)
+                ld[u].load((int)ks + u * kBN);
+    }
+    // tail: the last tiles (their loads are already in flight), loading only what exists
+    for (; kb0 < nb; kb0 += NSETS) {
 #pragma unroll
         for (int u = 0; u < NSETS; ++u) {
             const int kb = kb0 + u;

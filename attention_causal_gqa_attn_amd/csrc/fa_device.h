@@ -125,9 +125,18 @@ __device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel)
 // correctly rounded f16 of the exact product.
 // ---------------------------------------------------------------------------------------
 // Two nibbles at bits 0..3 and 16..19 of `nib` -> packed f16 pair (c0 - 8) * d0, (c1 - 8) * d1.
+__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t mask, uint32_t bits)
+{
+    // (x & mask) | bits in one instruction (the compiler otherwise emits an AND and an OR);
+    // one scalar operand at most, so `bits` sits in a VGPR
+    uint32_t r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "s"(mask), "v"(bits));
+    return r;
+}
+
 __device__ __forceinline__ uint32_t q4_pair(uint32_t nib, uint32_t d2)
 {
-    const f16x2 x = __builtin_bit_cast(f16x2, (nib & 0x000F000Fu) | 0x64006400u);
+    const f16x2 x = __builtin_bit_cast(f16x2, and_or(nib, 0x000F000Fu, 0x64006400u));
     const f16x2 c = x - (f16x2){(_Float16)1032.0f, (_Float16)1032.0f};
     return __builtin_bit_cast(uint32_t, c * __builtin_bit_cast(f16x2, d2));
 }

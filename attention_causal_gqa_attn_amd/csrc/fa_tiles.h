@@ -131,10 +131,16 @@ struct TileLoader<D, KV_Q4_0> {
     static constexpr int NB = D / 32;           // blocks per key row
     static constexpr int ROWB = NB * 18;        // bytes per key row
 
+    // D = 128: all 256 threads stage (128 for K, 128 for V); D = 64: threads >= 128 idle
+    static constexpr bool kAllBusy = (2 * D == kThreads);
+
     const uint8_t *base;                        // K or V, first byte of (b, key 0, kvh)
     uint32_t row;                               // bytes between consecutive keys
-    int Sk, tensor, kp, blk, aligned, mis;
+    int Sk, tensor, kp, blk, mis;
+    uint32_t off[2];                            // byte offsets of this thread's 2 key rows
     uint32_t w[2][5];
+
+    __device__ __forceinline__ bool busy() const { return kAllBusy || tensor < 2; }
 
     __device__ void init(const void *k, const void *v, int64_t head_off_rows, int64_t row_rows,
                          int Sk_, int t)
@@ -143,36 +149,48 @@ struct TileLoader<D, KV_Q4_0> {
         const int u = t % D;
         kp = u % 32;
         blk = u / 32;
-        const int off = 18 * blk;
-        aligned = off & ~3;
-        mis = off & 3;
+        const int boff = 18 * blk;
+        mis = boff & 3;
         base = (const uint8_t *)(tensor ? v : k) + head_off_rows * ROWB;
         row = (uint32_t)(row_rows * ROWB);
         Sk = Sk_;
+#pragma unroll
+        for (int r = 0; r < 2; ++r)
+            off[r] = (uint32_t)(2 * kp + r) * row + (uint32_t)(boff & ~3);
     }
 
     // Global loads of the tile starting at key k0 (k0 < Sk); in the last, partial tile keys
     // past the end repeat the last key.
     __device__ __forceinline__ void load(int k0)
     {
-        if (tensor >= 2)
+        if (!busy())
             return;
         const uint8_t *tile = base + (int64_t)k0 * row;
-        const int last = Sk - 1 - k0;
-        const bool full = k0 + kBN <= Sk;
+        if (k0 + kBN <= Sk) {
 #pragma unroll
-        for (int r = 0; r < 2; ++r) {
-            const uint32_t key = full ? (uint32_t)(2 * kp + r) : (uint32_t)min(2 * kp + r, last);
-            const uint32_t *p = (const uint32_t *)(tile + key * row + (uint32_t)aligned);
+            for (int r = 0; r < 2; ++r) {
+                const uint32_t *p = (const uint32_t *)(tile + off[r]);
 #pragma unroll
-            for (int i = 0; i < 5; ++i)
-                w[r][i] = p[i];
+                for (int i = 0; i < 5; ++i)
+                    w[r][i] = p[i];
+            }
+        } else {
+            const int last = Sk - 1 - k0;
+#pragma unroll
+            for (int r = 0; r < 2; ++r) {
+                const uint32_t key = (uint32_t)min(2 * kp + r, last);
+                const uint32_t *p =
+                    (const uint32_t *)(tile + key * row + (uint32_t)((18 * blk) & ~3));
+#pragma unroll
+                for (int i = 0; i < 5; ++i)
+                    w[r][i] = p[i];
+            }
         }
     }
 
     __device__ void store(uint16_t *lk, uint16_t *lv) const
     {
-        if (tensor >= 2)
+        if (!busy())
             return;
         uint32_t dbits[2], codes[2][4];
         q4_split_block(w[0], mis, dbits[0], codes[0]);
