@@ -51,7 +51,7 @@ __device__ __forceinline__ void decode_tile(const uint16_t *lk, const uint16_t *
             sc[i] = -INFINITY;
     float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
     mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    mx = pair_max(mx);
     const float m2 = mx * c;
     const bool need = m2 > frame + kRescaleMarginLog2;
     if (__any(need)) {
@@ -196,7 +196,7 @@ __global__ __launch_bounds__(kThreads, kDecodeOccupancy<KV>) void decode_split_k
 
     // ---- combine the 4 waves' states of each row, write the split's partial ---------------
     lsum += __shfl_xor(lsum, 16, 64);
-    lsum += __shfl_xor(lsum, 32, 64);
+    lsum = pair_sum(lsum);
     float *cmb_o = (float *)lds;                    // [4 waves][16 rows][D]
     float *cmb_f = cmb_o + 4 * 16 * D;              // [4][16]
     float *cmb_l = cmb_f + 64;                      // [4][16]

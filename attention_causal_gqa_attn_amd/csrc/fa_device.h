@@ -21,6 +21,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
 
 enum { KV_F16 = 0, KV_BF16 = 1, KV_Q4_0 = 2 };
 
@@ -106,8 +107,30 @@ __device__ __forceinline__ float sum2(uint32_t pair, float acc)
 // load issued after it, e.g. the next tile's).
 __device__ __forceinline__ void settle(const u32x4 &x) { asm volatile("" ::"v"(x)); }
 
-// Value held by lane l ^ 32.
-__device__ __forceinline__ float swap_halves(float x) { return __shfl_xor(x, 32, 64); }
+// max / sum of x over the lane pair {l, l ^ 32}. v_permlane32_swap on two copies of x leaves,
+// in every lane, the value of lane l % 32 in one and of lane l % 32 + 32 in the other — a VALU
+// exchange, no LDS trip. It is issued from asm: given one value for both operands, the
+// compiler's builtin treats its two results as equal and drops one of them. The s_nop covers
+// the two wait states the swap needs after a VALU write of its operands.
+__device__ __forceinline__ void lane_halves(float x, float &lo, float &hi)
+{
+    float a = x, b = x;
+    asm("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+    lo = a;
+    hi = b;
+}
+__device__ __forceinline__ float pair_max(float x)
+{
+    float lo, hi;
+    lane_halves(x, lo, hi);
+    return fmaxf(lo, hi);
+}
+__device__ __forceinline__ float pair_sum(float x)
+{
+    float lo, hi;
+    lane_halves(x, lo, hi);
+    return lo + hi;
+}
 
 // Byte permute: result byte i = byte sel_i of {hi:lo} (0..3 lo, 4..7 hi, 0x0C -> 0).
 __device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel)

@@ -18,14 +18,17 @@ struct AttnArgs {
     float c;            // scale * log2(e)
 };
 
-// Prefill workgroup decomposition: 4 waves of 32 query rows; hpw heads of one KV group by
-// qsub 32-row sub-blocks (hpw * qsub <= 4); heads beyond 4 of a group go to further chunks.
+// Prefill workgroup decomposition: `waves` waves (4 or 8) of 32 query rows; hpw heads of one
+// KV group by qsub 32-row sub-blocks (hpw * qsub <= waves); heads beyond `waves` of a group go
+// to further chunks.
 struct PrefillGrid {
-    int hpw, qsub, n_qblk, n_hchunk;
+    int waves, hpw, qsub, n_qblk, n_hchunk;
     int64_t n_wg;
 };
 PrefillGrid prefill_grid(const AttnArgs &a);
 hipError_t launch_prefill(const AttnArgs &a, hipStream_t stream);
+// f16 / bf16 caches: 8-wave workgroups, tiles moved by LDS DMA (fa_prefill16.hip)
+hipError_t launch_prefill16(const AttnArgs &a, const PrefillGrid &g, hipStream_t stream);
 
 // Decode: n_split key ranges per (b, KV head); rows = G * Sq query rows per KV head (<= 16).
 struct DecodeGrid {

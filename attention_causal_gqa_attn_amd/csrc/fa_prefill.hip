@@ -21,14 +21,14 @@
 //    are in flight while the current one is computed;
 //  * workgroups are ordered heaviest-first for causal work and mapped so that one XCD works
 //    through one KV head at a time (its L2 then serves all of that head's workgroups).
+#include <cstdlib>
+
 #include "fa_kernels.h"
 #include "fa_tiles.h"
 
 namespace fa {
 
 namespace {
-
-constexpr int kWaves = 4;
 
 struct PrefillParams {
     AttnArgs a;
@@ -43,10 +43,12 @@ __device__ __forceinline__ int k_row_perm(int m)
     return ((a >> 1) << 4) | (hh << 3) | ((a & 1) << 2) | bb;
 }
 
-template <int D, int KV>
-__global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p)
+// NW waves per workgroup (4 or 8), each 32 query rows; two workgroup-waves per SIMD.
+template <int D, int KV, int NW>
+__global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillParams p)
 {
     constexpr bool BF = (KV == KV_BF16);
+    constexpr int NT = 64 * NW;
     using Geo = TileGeom<D>;
     __shared__ __attribute__((aligned(16))) uint16_t lds[2 * Geo::stage];
 
@@ -107,33 +109,52 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p)
     float frame = -INFINITY;     // row's softmax frame, log2 units of the scaled score
     float lsum = 0.0f;           // this lane's share of the row sum, in the frame
 
-    TileLoader<D, KV> ld;
+    // LDS: two K tiles and two V^T tiles. K is staged one tile ahead of V, so that while a
+    // wave turns tile kb's scores into P (VALU), the MFMAs of tile kb+1's scores can run.
+    uint16_t *const kbuf0 = lds;
+    uint16_t *const vbuf0 = lds + 2 * Geo::kElems;
+    auto kbuf = [&](int i) { return kbuf0 + (i & 1) * Geo::kElems; };
+    auto vbuf = [&](int i) { return vbuf0 + (i & 1) * Geo::vElems; };
+
+    TileLoader<D, KV, NT> ld;
     ld.init(a.k, a.v, (int64_t)b * a.Sk * a.Hkv + kvh, a.Hkv, a.Sk, t);
     if (nb > 0) {
         ld.load(0);
-        ld.store(lds, lds + Geo::kElems);
+        ld.store(kbuf(0), vbuf(0));
+    }
+    if (nb > 1) {
+        ld.load_k(kBN);
+        ld.store_k(kbuf(1));
     }
     __syncthreads();
 
     const int krow0 = k_row_perm(col);
-    for (int kb = 0; kb < nb; ++kb) {
-        if (kb + 1 < nb)
-            ld.load((kb + 1) * kBN);
-        const uint16_t *lk = lds + (kb & 1) * Geo::stage;
-        const uint16_t *lv = lk + Geo::kElems;
-        const int k0 = kb * kBN;
+    // S^T of the K tile in `lk` for this wave's rows: two 32-key halves
+    auto scores = [&](const uint16_t *lk, f32x16 *s) {
+        const uint16_t *kr = lk + krow0 * Geo::kStride + 8 * half;
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+            s[hf] = (f32x16){};
+#pragma unroll
+            for (int st = 0; st < D / 16; ++st)
+                s[hf] = mfma32<BF>(*(const u32x4 *)(kr + hf * 32 * Geo::kStride + 16 * st),
+                                   qf[st], s[hf]);
+        }
+    };
 
-        if (wave_on && k0 < wkend) {
-            // S^T for the two 32-key halves of the tile
-            f32x16 s[2];
-#pragma unroll
-            for (int hf = 0; hf < 2; ++hf) {
-                s[hf] = (f32x16){};
-                const uint16_t *kr = lk + (hf * 32 + krow0) * Geo::kStride + 8 * half;
-#pragma unroll
-                for (int st = 0; st < D / 16; ++st)
-                    s[hf] = mfma32<BF>(*(const u32x4 *)(kr + 16 * st), qf[st], s[hf]);
-            }
+    // One key tile: s_cur holds this tile's scores, s_next receives the next tile's. The loop
+    // below is unrolled by two with the buffers swapping roles, so no scores are copied.
+    auto tile = [&](const int kb, f32x16 *s_cur, f32x16 *s_next) {
+        const int k0 = kb * kBN;
+        const bool load_k = kb + 2 < nb, load_v = kb + 1 < nb;
+        if (load_k)
+            ld.load_k(k0 + 2 * kBN);
+        if (load_v)
+            ld.load_v(k0 + kBN);
+        const bool do_cur = wave_on && k0 < wkend;
+        const bool do_next = wave_on && kb + 1 < nb && k0 + kBN < wkend;
+
+        if (do_cur) {
             // causal / sequence-end mask, only where a key can exceed the row's limit; keys are
             // compared relative to the tile start, in 32 bits
             if ((int64_t)k0 + kBN - 1 > klim_min) {
@@ -143,17 +164,17 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p)
 #pragma unroll
                     for (int i = 0; i < 16; ++i)
                         if (hf * 32 + 16 * (i / 8) + (i % 8) > lim)
-                            s[hf][i] = -INFINITY;
+                            s_cur[hf][i] = -INFINITY;
             }
             // block maximum of the row (this lane's 32 keys, then lane l^32's)
-            float mx = s[0][0];
+            float mx = s_cur[0][0];
 #pragma unroll
             for (int i = 1; i < 16; ++i)
-                mx = fmaxf(mx, s[0][i]);
+                mx = fmaxf(mx, s_cur[0][i]);
 #pragma unroll
             for (int i = 0; i < 16; ++i)
-                mx = fmaxf(mx, s[1][i]);
-            mx = fmaxf(mx, swap_halves(mx));
+                mx = fmaxf(mx, s_cur[1][i]);
+            mx = pair_max(mx);
             const float m2 = mx * a.c;
 
             // deferred rescale: only rows whose block max outgrows the frame by the margin
@@ -166,40 +187,93 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p)
                 lsum *= alpha;
                 frame = need ? m2 : frame;
             }
-            const float fr = (frame == -INFINITY) ? 0.0f : frame;
+        }
 
-            // P = 2^(S*c - f), packed straight into the B operands of the P.V MFMA
-            u32x4 pf[4];
+        // This tile's P = 2^(S*c - f) (VALU) and the next tile's scores (MFMA) are independent:
+        // in the common case both are written as one straight-line block, one MFMA of the
+        // next scores (the two 32-key halves alternate, so consecutive MFMAs do not depend on
+        // each other) between chunks of P, so the two instruction streams overlap.
+        const float fr = (frame == -INFINITY) ? 0.0f : frame;
+        u32x4 pf[4];
+        auto p_chunk = [&](int j) {      // P pair j of 16 -> pf[j / 4][j % 4]
+            const int t4 = j >> 2, e = j & 3;
+            const int i = 8 * (t4 & 1) + 2 * e;
+            const float p0 = exp2_fast(__builtin_fmaf(s_cur[t4 >> 1][i], a.c, -fr));
+            const float p1 = exp2_fast(__builtin_fmaf(s_cur[t4 >> 1][i + 1], a.c, -fr));
+            const uint32_t pk = pack2<BF>(p0, p1);
+            pf[t4][e] = pk;
+            lsum = sum2<BF>(pk, lsum);
+        };
+        // O^T += V^T P^T for the 16 keys of P fragment t4
+        const uint16_t *lv = vbuf(kb);
+        auto pv = [&](int t4) {
+            const uint16_t *vr = lv + col * Geo::vStride + 16 * t4 + 8 * half;
 #pragma unroll
-            for (int t4 = 0; t4 < 4; ++t4) {
+            for (int dt = 0; dt < D / 32; ++dt)
+                acc[dt] = mfma32<BF>(*(const u32x4 *)(vr + 32 * dt * Geo::vStride), pf[t4],
+                                     acc[dt]);
+        };
+        if (do_cur && do_next) {
+            // one straight-line block: per step one MFMA of the next scores, one P pair, and
+            // after every fourth pair the 4 P.V MFMAs of those 16 keys
+            constexpr int NMF = D / 8;                 // MFMAs of one tile's scores
+            constexpr int PER = 16 / NMF;              // P pairs per MFMA
+            const uint16_t *kr = kbuf(kb + 1) + krow0 * Geo::kStride + 8 * half;
+            s_next[0] = (f32x16){};
+            s_next[1] = (f32x16){};
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int i = 8 * (t4 & 1) + 2 * e;
-                    const float p0 = exp2_fast(__builtin_fmaf(s[t4 >> 1][i], a.c, -fr));
-                    const float p1 = exp2_fast(__builtin_fmaf(s[t4 >> 1][i + 1], a.c, -fr));
-                    const uint32_t pk = pack2<BF>(p0, p1);
-                    pf[t4][e] = pk;
-                    lsum = sum2<BF>(pk, lsum);
+            for (int j = 0; j < NMF; ++j) {
+                const int hf = j & 1, st = j >> 1;
+                s_next[hf] = mfma32<BF>(*(const u32x4 *)(kr + hf * 32 * Geo::kStride + 16 * st),
+                                        qf[st], s_next[hf]);
+#pragma unroll
+                for (int c = 0; c < PER; ++c) {
+                    const int jj = j * PER + c;
+                    p_chunk(jj);
+                    if ((jj & 3) == 3)
+                        pv(jj >> 2);
                 }
             }
-            // O^T += V^T P^T, 16 keys per step
+            // Instruction order for the block: 4 LDS fragment reads ahead, then repeatedly one
+            // MFMA, one LDS read and three VALU ops, so that each MFMA's operand was requested
+            // several MFMAs earlier and the VALU work issues while the MFMAs run.
+            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
-            for (int t4 = 0; t4 < 4; ++t4) {
-                const uint16_t *vr = lv + col * Geo::vStride + 16 * t4 + 8 * half;
+            for (int i = 0; i < NMF + 16; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+            }
+        } else {
+            if (do_next)
+                scores(kbuf(kb + 1), s_next);
+            if (do_cur) {
 #pragma unroll
-                for (int dt = 0; dt < D / 32; ++dt)
-                    acc[dt] = mfma32<BF>(*(const u32x4 *)(vr + 32 * dt * Geo::vStride), pf[t4],
-                                         acc[dt]);
+                for (int j = 0; j < 16; ++j) {
+                    p_chunk(j);
+                    if ((j & 3) == 3)
+                        pv(j >> 2);
+                }
             }
         }
-        if (kb + 1 < nb)
-            ld.store(lds + ((kb + 1) & 1) * Geo::stage,
-                     lds + ((kb + 1) & 1) * Geo::stage + Geo::kElems);
+        if (load_k)
+            ld.store_k(kbuf(kb));
+        if (load_v)
+            ld.store_v(vbuf(kb + 1));
         __syncthreads();
+    };
+
+    f32x16 s_a[2], s_b[2];
+    if (wave_on && nb > 0 && 0 < wkend)
+        scores(kbuf(0), s_a);
+    for (int kb = 0; kb < nb; kb += 2) {
+        tile(kb, s_a, s_b);
+        if (kb + 1 < nb)
+            tile(kb + 1, s_b, s_a);
     }
 
     // ---- epilogue: O / l, cast, store ----------------------------------------------------
-    const float ltot = lsum + swap_halves(lsum);
+    const float ltot = pair_sum(lsum);
     if (!wave_on || qi >= a.Sq)
         return;
     const float inv = ltot > 0.0f ? 1.0f / ltot : 0.0f;
@@ -215,24 +289,60 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams p)
         }
 }
 
-template <int D, int KV>
+template <int D, int KV, int NW>
 hipError_t launch(const PrefillParams &p, int64_t n_wg, hipStream_t stream)
 {
-    hipLaunchKernelGGL((prefill_kernel<D, KV>), dim3((unsigned)n_wg), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((prefill_kernel<D, KV, NW>), dim3((unsigned)n_wg), dim3(64 * NW), 0,
+                       stream, p);
     return hipGetLastError();
 }
 
-}  // namespace
+template <int NW>
+hipError_t launch_waves(const PrefillParams &p, int D, int kv, int64_t n_wg, hipStream_t stream)
+{
+    if (D == 128) {
+        if (kv == KV_F16)
+            return launch<128, KV_F16, NW>(p, n_wg, stream);
+        if (kv == KV_BF16)
+            return launch<128, KV_BF16, NW>(p, n_wg, stream);
+        return launch<128, KV_Q4_0, NW>(p, n_wg, stream);
+    }
+    if (kv == KV_F16)
+        return launch<64, KV_F16, NW>(p, n_wg, stream);
+    if (kv == KV_BF16)
+        return launch<64, KV_BF16, NW>(p, n_wg, stream);
+    return launch<64, KV_Q4_0, NW>(p, n_wg, stream);
+}
 
-PrefillGrid prefill_grid(const AttnArgs &a)
+PrefillGrid grid_for(const AttnArgs &a, int waves)
 {
     PrefillGrid g;
-    g.hpw = a.G < kWaves ? a.G : kWaves;
-    g.qsub = kWaves / g.hpw;
+    g.waves = waves;
+    g.hpw = a.G < waves ? a.G : waves;
+    g.qsub = waves / g.hpw;
     g.n_qblk = (a.Sq + 32 * g.qsub - 1) / (32 * g.qsub);
     g.n_hchunk = (a.G + g.hpw - 1) / g.hpw;
     g.n_wg = (int64_t)g.n_qblk * g.n_hchunk * a.Hkv * a.B;
     return g;
+}
+
+}  // namespace
+
+// Workgroup size: 8 waves (the K/V tiles in LDS serve twice as many query rows, halving the
+// tile traffic) when that still gives at least one workgroup per CU, else 4 waves.
+// FA_PREFILL_WAVES=4|8 overrides the choice (for tuning).
+PrefillGrid prefill_grid(const AttnArgs &a)
+{
+    if (a.kv != KV_Q4_0)
+        return grid_for(a, 8);      // the LDS-DMA kernel always runs 8 waves
+    static const int forced = [] {
+        const char *e = getenv("FA_PREFILL_WAVES");
+        return e ? atoi(e) : 0;
+    }();
+    if (forced == 4 || forced == 8)
+        return grid_for(a, forced);
+    const PrefillGrid g8 = grid_for(a, 8);
+    return g8.n_wg >= 256 ? g8 : grid_for(a, 4);
 }
 
 hipError_t launch_prefill(const AttnArgs &a, hipStream_t stream)
@@ -241,18 +351,11 @@ hipError_t launch_prefill(const AttnArgs &a, hipStream_t stream)
     const PrefillParams p{a, g.hpw, g.qsub, g.n_qblk, g.n_hchunk};
     if (g.n_wg == 0)
         return hipSuccess;
-    if (a.D == 128) {
-        if (a.kv == KV_F16)
-            return launch<128, KV_F16>(p, g.n_wg, stream);
-        if (a.kv == KV_BF16)
-            return launch<128, KV_BF16>(p, g.n_wg, stream);
-        return launch<128, KV_Q4_0>(p, g.n_wg, stream);
-    }
-    if (a.kv == KV_F16)
-        return launch<64, KV_F16>(p, g.n_wg, stream);
-    if (a.kv == KV_BF16)
-        return launch<64, KV_BF16>(p, g.n_wg, stream);
-    return launch<64, KV_Q4_0>(p, g.n_wg, stream);
+    if (a.kv != KV_Q4_0)
+        return launch_prefill16(a, g, stream);
+    if (g.waves == 8)
+        return launch_waves<8>(p, a.D, a.kv, g.n_wg, stream);
+    return launch_waves<4>(p, a.D, a.kv, g.n_wg, stream);
 }
 
 }  // namespace fa

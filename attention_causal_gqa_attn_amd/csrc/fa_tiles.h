@@ -31,26 +31,30 @@ struct TileGeom {
     static constexpr int stage = kElems + vElems;     // 16-bit elements per K+V buffer
 };
 
-template <int D, int KV>
+// NT: threads of the workgroup that stages the tiles (256 or 512).
+template <int D, int KV, int NT = kThreads>
 struct TileLoader;
 
 // f16 / bf16 caches ----------------------------------------------------------------------
-template <int D, int KV>
+template <int D, int KV, int NT>
 struct TileLoader {
     static_assert(D == 64 || D == 128, "head dim");
+    static_assert(NT == 256 || NT == 512, "threads");
     using G = TileGeom<D>;
-    static constexpr int KC = D / 32;     // K chunks per thread
-    static constexpr int KPT = D / 32;    // V keys per thread
+    static constexpr int KC = kBN * (D / 8) / NT;    // K chunks per thread
+    static constexpr int KPT = kBN * (D / 8) / NT;   // V keys per thread
     static constexpr int VCOLS = kBN / KPT;
 
     const uint8_t *kbase, *vbase;         // first byte of (b, key 0, kvh)
     uint32_t row;                         // bytes between consecutive keys
     int Sk, t;
-    uint32_t koff[KC], voff[KPT];         // per-thread byte offsets inside a tile
+    uint32_t koff, voff;                  // per-thread byte offsets of the first K chunk / V key
     u32x4 kr[KC], vr[KPT];
 
-    __device__ __forceinline__ int k_key(int p) const { return (p * kThreads + t) / (D / 8); }
-    __device__ __forceinline__ int k_dc(int p) const { return (p * kThreads + t) % (D / 8); }
+    // K chunk p of thread t: key p * kKeysPerPass + t / (D/8), 16-byte chunk t % (D/8)
+    static constexpr int kKeysPerPass = NT / (D / 8);
+    __device__ __forceinline__ int k_key(int p) const { return p * kKeysPerPass + t / (D / 8); }
+    __device__ __forceinline__ int k_dc() const { return t % (D / 8); }
     __device__ __forceinline__ int v_key0() const { return KPT * (t % VCOLS); }
     __device__ __forceinline__ int v_dc() const { return t / VCOLS; }
 
@@ -63,35 +67,40 @@ struct TileLoader {
         row = (uint32_t)(row_rows * D * 2);
         Sk = Sk_;
         t = t_;
-#pragma unroll
-        for (int p = 0; p < KC; ++p)
-            koff[p] = (uint32_t)k_key(p) * row + (uint32_t)k_dc(p) * 16u;
-#pragma unroll
-        for (int r = 0; r < KPT; ++r)
-            voff[r] = (uint32_t)(v_key0() + r) * row + (uint32_t)v_dc() * 16u;
+        koff = (uint32_t)k_key(0) * row + (uint32_t)k_dc() * 16u;
+        voff = (uint32_t)v_key0() * row + (uint32_t)v_dc() * 16u;
     }
 
-    // Global loads of the tile starting at key k0 (k0 < Sk). The tile base is uniform and the
-    // per-thread part a 32-bit offset; in the last, partial tile keys past the end repeat the
-    // last key.
-    __device__ __forceinline__ void load(int k0)
+    // Global loads of the K (V) tile starting at key k0 (k0 < Sk): a uniform tile base plus a
+    // 32-bit offset (the per-pass / per-key part of it is uniform, the per-thread part fixed),
+    // both branches in 32 bits so the loads keep the scalar-base form after the compiler merges
+    // them. In the last, partial tile keys past the end repeat the last key.
+    __device__ __forceinline__ void load_k(int k0)
     {
         const uint8_t *kt = kbase + (int64_t)k0 * row;
-        const uint8_t *vt = vbase + (int64_t)k0 * row;
         if (k0 + kBN <= Sk) {
 #pragma unroll
             for (int p = 0; p < KC; ++p)
-                kr[p] = *(const u32x4 *)(kt + koff[p]);
-#pragma unroll
-            for (int r = 0; r < KPT; ++r)
-                vr[r] = *(const u32x4 *)(vt + voff[r]);
+                kr[p] = *(const u32x4 *)(kt + ((uint32_t)(p * kKeysPerPass) * row + koff));
         } else {
             const int last = Sk - 1 - k0;
 #pragma unroll
             for (int p = 0; p < KC; ++p) {
-                const uint32_t off = (uint32_t)min(k_key(p), last) * row + (uint32_t)k_dc(p) * 16u;
+                const uint32_t off = (uint32_t)min(k_key(p), last) * row + (uint32_t)k_dc() * 16u;
                 kr[p] = *(const u32x4 *)(kt + off);
             }
+        }
+    }
+
+    __device__ __forceinline__ void load_v(int k0)
+    {
+        const uint8_t *vt = vbase + (int64_t)k0 * row;
+        if (k0 + kBN <= Sk) {
+#pragma unroll
+            for (int r = 0; r < KPT; ++r)
+                vr[r] = *(const u32x4 *)(vt + ((uint32_t)r * row + voff));
+        } else {
+            const int last = Sk - 1 - k0;
 #pragma unroll
             for (int r = 0; r < KPT; ++r) {
                 const uint32_t off =
@@ -101,11 +110,21 @@ struct TileLoader {
         }
     }
 
-    __device__ __forceinline__ void store(uint16_t *lk, uint16_t *lv) const
+    __device__ __forceinline__ void load(int k0)
+    {
+        load_k(k0);
+        load_v(k0);
+    }
+
+    __device__ __forceinline__ void store_k(uint16_t *lk) const
     {
 #pragma unroll
         for (int p = 0; p < KC; ++p)
-            *(u32x4 *)(lk + k_key(p) * G::kStride + k_dc(p) * 8) = kr[p];
+            *(u32x4 *)(lk + k_key(p) * G::kStride + k_dc() * 8) = kr[p];
+    }
+
+    __device__ __forceinline__ void store_v(uint16_t *lv) const
+    {
         const int key0 = v_key0(), dc = v_dc();
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -116,23 +135,31 @@ struct TileLoader {
                 w[0] = perm(vr[1][e / 2], vr[0][e / 2], sel);
                 w[1] = perm(vr[3][e / 2], vr[2][e / 2], sel);
                 *(u32x2 *)dst = w;
-            } else {
+            } else if constexpr (KPT == 2) {
                 *(uint32_t *)dst = perm(vr[1][e / 2], vr[0][e / 2], sel);
+            } else {
+                *dst = (uint16_t)(vr[0][e / 2] >> (16 * (e & 1)));
             }
         }
+    }
+
+    __device__ __forceinline__ void store(uint16_t *lk, uint16_t *lv) const
+    {
+        store_k(lk);
+        store_v(lv);
     }
 };
 
 // q4_0 cache -----------------------------------------------------------------------------
-template <int D>
-struct TileLoader<D, KV_Q4_0> {
+template <int D, int NT>
+struct TileLoader<D, KV_Q4_0, NT> {
     static_assert(D == 64 || D == 128, "head dim");
     using G = TileGeom<D>;
     static constexpr int NB = D / 32;           // blocks per key row
     static constexpr int ROWB = NB * 18;        // bytes per key row
 
-    // D = 128: all 256 threads stage (128 for K, 128 for V); D = 64: threads >= 128 idle
-    static constexpr bool kAllBusy = (2 * D == kThreads);
+    // threads [0, D) stage K, [D, 2D) stage V, the rest idle (none at D = 128 with 256 threads)
+    static constexpr bool kAllBusy = (2 * D == NT);
 
     const uint8_t *base;                        // K or V, first byte of (b, key 0, kvh)
     uint32_t row;                               // bytes between consecutive keys
@@ -186,6 +213,28 @@ struct TileLoader<D, KV_Q4_0> {
                     w[r][i] = p[i];
             }
         }
+    }
+
+    // K (V) halves: threads [0, D) stage K, [D, 2D) stage V; at D = 128 this is wave-uniform.
+    __device__ __forceinline__ void load_k(int k0)
+    {
+        if (tensor == 0)
+            load(k0);
+    }
+    __device__ __forceinline__ void load_v(int k0)
+    {
+        if (tensor == 1)
+            load(k0);
+    }
+    __device__ __forceinline__ void store_k(uint16_t *lk) const
+    {
+        if (tensor == 0)
+            store(lk, nullptr);
+    }
+    __device__ __forceinline__ void store_v(uint16_t *lv) const
+    {
+        if (tensor == 1)
+            store(nullptr, lv);
     }
 
     __device__ void store(uint16_t *lk, uint16_t *lv) const
