@@ -89,6 +89,16 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi)
     }
 }
 
+// Packed 16-bit pair -> two f32 (exact).
+template <bool BF>
+__device__ __forceinline__ f32x2 unpack2(uint32_t pair)
+{
+    if constexpr (BF)
+        return __builtin_convertvector(__builtin_bit_cast(bf16x2, pair), f32x2);
+    else
+        return __builtin_convertvector(__builtin_bit_cast(f16x2, pair), f32x2);
+}
+
 // Sum of a packed 16-bit pair, accumulated in f32 (v_dot2 with ones).
 template <bool BF>
 __device__ __forceinline__ float sum2(uint32_t pair, float acc)

@@ -27,7 +27,9 @@ struct PrefillGrid {
 };
 PrefillGrid prefill_grid(const AttnArgs &a);
 hipError_t launch_prefill(const AttnArgs &a, hipStream_t stream);
-// f16 / bf16 caches: 8-wave workgroups, tiles moved by LDS DMA (fa_prefill16.hip)
+// f16 / bf16 caches: 4-wave workgroups of 64-row waves, tiles moved by LDS DMA
+// (fa_prefill16.hip)
+PrefillGrid prefill16_grid(const AttnArgs &a);
 hipError_t launch_prefill16(const AttnArgs &a, const PrefillGrid &g, hipStream_t stream);
 
 // Decode: n_split key ranges per (b, KV head); rows = G * Sq query rows per KV head (<= 16).

@@ -334,7 +334,7 @@ PrefillGrid grid_for(const AttnArgs &a, int waves)
 PrefillGrid prefill_grid(const AttnArgs &a)
 {
     if (a.kv != KV_Q4_0)
-        return grid_for(a, 8);      // the LDS-DMA kernel always runs 8 waves
+        return prefill16_grid(a);
     static const int forced = [] {
         const char *e = getenv("FA_PREFILL_WAVES");
         return e ? atoi(e) : 0;

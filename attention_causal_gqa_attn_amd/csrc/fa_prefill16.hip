@@ -1,20 +1,24 @@
-// Prefill kernel for f16 / bf16 caches: the same flash organisation as the q4_0-capable
-// kernel in fa_prefill.hip (K-ahead software pipeline, deferred rescale, S^T layout with one
-// query row per lane), with the K/V tiles moved by the LDS DMA path of gfx950:
+// Prefill kernel for f16 / bf16 caches: flash attention with the S^T = K Q^T layout (one query
+// row per lane), the deferred O/l rescale, and K/V tiles moved into LDS by the LDS-DMA path of
+// gfx950. Organisation, chosen from measurement on the chip:
 //
-//  * `global_load_lds_dwordx4` writes each tile straight from global memory into LDS — no
-//    staging registers — so a ring of 4 tile stages keeps two tiles in flight while one is
-//    computed (the pipeline waits on explicit load counts; a bare s_barrier with a compiler
-//    memory fence replaces __syncthreads, whose full fence would wait for every load);
-//  * tiles keep their natural row-major [key][d] layout, with 16-byte chunks XOR-swizzled per
-//    row so that the fragment reads below are bank-conflict free;
-//  * K fragments (the A operand of S^T = K Q^T) are 16-byte row reads; the swizzle is chosen so
-//    that the address of K-step st is (base | X) ^ 32*st — one VALU op per step;
-//  * V^T fragments (the A operand of O^T += V^T P^T) come from `ds_read_b64_tr_b16`: within each
-//    16-lane group, if source lane i reads V[key0 + i/4][d0 + 4*(i%4) .. +3], result lane j holds
-//    V[key0 .. key0+3][d0 + j] — 4 consecutive keys of one d, two reads per MFMA operand;
-//  * 8 waves per workgroup (4 heads x 64 queries for GQA 4), one workgroup per CU.
+//  * 4 waves per workgroup, one per SIMD, 64 query rows per wave as two 32-row blocks (j = 0, 1)
+//    of one head: every K or V^T fragment read from LDS feeds two MFMAs, halving the LDS read
+//    traffic against 32 rows per wave (the 2-byte transpose read runs at half the LDS rate of
+//    a 16-byte read, and LDS bandwidth is what 32-row waves run out of);
+//  * one wave per SIMD has to overlap its own softmax VALU work with its MFMAs. A 32x32x16 MFMA
+//    keeps the issue port busy for half of its 32 cycles, so each one leaves room for a few
+//    VALU instructions; a steady-state tile is written as a fixed sequence of MFMA slots with
+//    the softmax work spread over them, and scheduling barriers keep that order:
+//        half 1 of tile n:  acc[j] += V(n-1)^T P(n-1, j)^T, both blocks    | softmax(n, j = 0)
+//        half 2 of tile n:  S(n+1, j) = K(n+1) Q(j)^T, both blocks          | softmax(n, j = 1)
+//    (block 1's scores are double-buffered: its softmax reads S(n) while S(n+1) is written);
+//  * tiles keep their row-major [key][d] layout in LDS with 16-byte chunks XOR-swizzled per
+//    row, so K fragment reads (16 bytes) and V^T transpose reads (ds_read_b64_tr_b16) are free
+//    of bank conflicts; K runs 4 tiles ahead of its use and V 2 tiles, through 4-stage rings,
+//    so every tile has three loop iterations to arrive.
 #include <cstdlib>
+#include <utility>
 
 #include "fa_kernels.h"
 #include "fa_tiles.h"
@@ -23,9 +27,14 @@ namespace fa {
 
 namespace {
 
-constexpr int kNW = 8;                 // waves per workgroup
+// every helper lambda of the kernel is inlined: the kernel relies on scalar (wave-uniform)
+// values staying scalar, and on register arrays staying registers
+#define INL __attribute__((always_inline))
+
+constexpr int kNW = 4;                 // waves per workgroup
 constexpr int kNT = 64 * kNW;          // threads per workgroup
-constexpr int kStages = 4;             // K/V tile stages in LDS
+constexpr int kQW = 64;                // query rows per wave
+constexpr int kStages = 4;             // tile stages per ring (K ring, V ring)
 
 struct Prefill16Params {
     AttnArgs a;
@@ -48,11 +57,53 @@ __device__ __forceinline__ void dma16(const uint8_t *gbase, uint32_t voff, uint3
                  :: "v"(voff), "s"(gbase), "s"(lds_base) : "memory");
 }
 
-// LDS byte address of a wave-uniform pointer into the kernel's shared array, as an SGPR value
+// Keeps a value's computation at this point of the instruction stream: the empty volatile asm
+// cannot move across the scheduling fences, so neither can the code that produces its input.
+template <typename T>
+__device__ __forceinline__ void pin(T &x)
+{
+    asm volatile("" : "+v"(x));
+}
+
+// Score MFMAs, issued from asm so that their results land in VGPRs (the compiler would put
+// every MFMA result of this kernel in AGPRs, and the softmax reads the scores with VALU
+// instructions, which cannot take AGPR operands). The compiler does not see these as MFMAs:
+// the kernel waits out the MFMA-to-VALU dependency itself (s_nop before the first VALU read
+// of a tile's scores), and the chains accumulate in place (srcC == vdst). The Q operand is
+// taken from AGPRs, where Q stays for the whole kernel.
+template <bool BF>
+__device__ __forceinline__ void smfma_first(f32x16 &d, const u32x4 &a, const u32x4 &b)
+{
+    if constexpr (BF)
+        asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "a"(b));
+    else
+        asm("v_mfma_f32_32x32x16_f16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "a"(b));
+}
+template <bool BF>
+__device__ __forceinline__ void smfma_acc(f32x16 &d, const u32x4 &a, const u32x4 &b)
+{
+    if constexpr (BF)
+        asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "a"(b));
+    else
+        asm("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "a"(b));
+}
+// Wait states between the score MFMAs and VALU reads of their results (a 16-pass XDL result
+// needs at most 19 before a VALU reads it); each s_nop 7 gives 8. Taking the score registers
+// as operands makes every later read of them depend on the wait.
+__device__ __forceinline__ void smfma_drain()
+{
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+}
+__device__ __forceinline__ void smfma_drain(f32x16 &a, f32x16 &b, f32x16 &c, f32x16 &d)
+{
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(a), "+v"(b), "+v"(c), "+v"(d));
+}
+
+// LDS byte address of a pointer into the kernel's shared array
 __device__ __forceinline__ uint32_t lds_addr(const uint8_t *p)
 {
     const auto lp = (const __attribute__((address_space(3))) uint8_t *)p;
-    return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lp);
+    return (uint32_t)(uintptr_t)lp;
 }
 
 __device__ __forceinline__ int k_row_perm16(int m)
@@ -66,22 +117,107 @@ struct Geom16 {
     static constexpr int ROW = D * 2;                  // bytes per key row
     static constexpr int CPR = D / 8;                  // 16-byte chunks per row
     static constexpr int TILE = kBN * ROW;             // bytes per K (or V) tile
-    static constexpr int NDMA = TILE / (kNT * 16);     // DMA instructions per thread per tile
+    static constexpr int NDMA = TILE / (kNT * 16);     // DMA transfers per thread per tile
     static constexpr int LDS = 2 * kStages * TILE;
     // chunk swizzles: slot = chunk ^ sw(row)
     __device__ static __forceinline__ int swk(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
     __device__ static __forceinline__ int swv(int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
 };
 
+// f(std::integral_constant<int, I>) for I = B .. E-1, expanded at compile time
+template <int B, typename F, int... Is>
+__device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, Is...>)
+{
+    (f(std::integral_constant<int, B + Is>{}), ...);
+}
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F &&f)
+{
+    if constexpr (E > B)
+        static_for_impl<B>(f, std::make_integer_sequence<int, E - B>{});
+}
+
+// ---- compile-time placement of the softmax work over the MFMA slots of a half --------------
+// The softmax of one block and tile is 25 units: 8 partial maxima (unit 0..7), the frame
+// update (8), and 16 exponential units (9..24; unit 9 + 4*t4 + e makes P chunk t4, pair e).
+// Units run in order; each goes into the first slot at or after its earliest slot with room
+// (room 2 per slot: a partial maximum weighs 1, any other unit 2). Units that do not fit run
+// after the last slot.
+constexpr int kUnits = 25;
+struct UnitList {
+    int n;
+    int earliest[2 * kUnits];
+    int weight[2 * kUnits];
+};
+struct UnitPlan {
+    int first[64 + 1];       // units [first[s], first[s+1]) run in slot s; first[NM]: leftovers
+};
+constexpr UnitPlan plan_units(int nslots, const UnitList &l)
+{
+    UnitPlan pl{};
+    int u = 0;
+    for (int s = 0; s < nslots; ++s) {
+        pl.first[s] = u;
+        int room = 2;
+        while (u < l.n && l.earliest[u] <= s && l.weight[u] <= room) {
+            room -= l.weight[u];
+            ++u;
+        }
+    }
+    pl.first[nslots] = u;
+    return pl;
+}
+
+template <int D>
+struct Plans {
+    static constexpr int NDT = D / 32;                 // 32-wide d blocks of O^T
+    static constexpr int NST = D / 16;                 // k-steps of a score chain
+    static constexpr int NM = 8 * NDT;                 // MFMA slots per half
+    static_assert(NM == 4 * NST && NM <= 64, "both halves have NM MFMA slots");
+    // half 1: the exponential units of chunk t4 overwrite pf[0][t4], which the block-0 MFMAs
+    // of chunk t4 read; the last of those is in slot 2 * (t4 * NDT + NDT - 1)
+    static constexpr UnitList list1()
+    {
+        UnitList l{};
+        l.n = kUnits;
+        for (int u = 0; u < kUnits; ++u) {
+            l.earliest[u] = u < 9 ? 0 : 2 * (((u - 9) / 4) * NDT + NDT - 1) + 1;
+            l.weight[u] = u < 8 ? 1 : 2;
+        }
+        return l;
+    }
+    static constexpr UnitPlan h1 = plan_units(NM, list1());
+    static constexpr int c0 = h1.first[NM];            // first unit of block 0 left to half 2
+    static constexpr int carry = kUnits - c0;
+    // half 2: block 0's leftover units first (they read block 0's hf = 1 scores, which the
+    // block-0 score MFMAs of hf = 1 overwrite from slot 2 * NST on), then block 1's 25 units
+    static constexpr UnitList list2()
+    {
+        UnitList l{};
+        l.n = carry + kUnits;
+        for (int u = 0; u < l.n; ++u) {
+            l.earliest[u] = 0;
+            l.weight[u] = (u >= carry && u - carry < 8) ? 1 : 2;
+        }
+        return l;
+    }
+    static constexpr UnitPlan h2 = plan_units(NM, list2());
+    static_assert(c0 >= 9 + 8, "only exponential units of chunks 2, 3 (hf = 1) are carried");
+    static_assert(h2.first[2 * NST] >= carry, "carried units run before the hf = 1 scores");
+};
+
 template <int D, bool BF>
-__global__ __launch_bounds__(kNT, 2) void prefill16_kernel(Prefill16Params p)
+__global__ __launch_bounds__(kNT, 1) void prefill16_kernel(Prefill16Params p)
 {
     using G = Geom16<D>;
+    using PL = Plans<D>;
+    constexpr int NDT = PL::NDT, NST = PL::NST, NM = PL::NM;
     __shared__ __attribute__((aligned(1024))) uint8_t lds[G::LDS];
     typedef __attribute__((address_space(3))) s16x4_t lds_s16x4;
 
     const AttnArgs &a = p.a;
-    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int t = threadIdx.x, lane = t & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);   // uniform: scalar branches
     const int half = lane >> 5, col = lane & 31;
 
     // ---- which (b, kv head, head chunk, query block) this workgroup owns -------------------
@@ -92,13 +228,13 @@ __global__ __launch_bounds__(kNT, 2) void prefill16_kernel(Prefill16Params p)
     rest /= p.n_hchunk;
     const int kvh = rest % a.Hkv;
     const int b = rest / a.Hkv;
-    const int qb = a.causal ? p.n_qblk - 1 - qbl : qbl;      // heaviest blocks first
+    const int qblk = a.causal ? p.n_qblk - 1 - qbl : qbl;    // heaviest blocks first
 
-    const int bmq = 32 * p.qsub;
-    const int qwg0 = qb * bmq;
+    const int bmq = kQW * p.qsub;
+    const int qwg0 = qblk * bmq;
     const int hs = wave % p.hpw, qs = wave / p.hpw;
     const int hl = hc * p.hpw + hs;
-    const int q0 = qwg0 + qs * 32;
+    const int q0 = qwg0 + qs * kQW;
     const bool wave_on = (wave < p.hpw * p.qsub) && (hl < a.G) && (q0 < a.Sq);
     const int h = kvh * a.G + min(hl, a.G - 1);
 
@@ -109,85 +245,107 @@ __global__ __launch_bounds__(kNT, 2) void prefill16_kernel(Prefill16Params p)
     kend = max(kend, (int64_t)0);
     const int nb = (int)((kend + kBN - 1) / kBN);
 
-    int64_t wkend = a.Sk;
-    if (a.causal)
-        wkend = min((int64_t)a.Sk, (int64_t)min(q0 + 31, a.Sq - 1) + a.offset + 1);
-    const int qi = q0 + col;
-    const int64_t klim = a.causal ? min((int64_t)a.Sk - 1, (int64_t)qi + a.offset)
-                                  : (int64_t)a.Sk - 1;
-    const int64_t klim_min = a.causal ? min((int64_t)a.Sk - 1, (int64_t)q0 + a.offset)
-                                      : (int64_t)a.Sk - 1;
-
-    // ---- Q once, as B operands ---------------------------------------------------------------
-    const int qrow = min(qi, a.Sq - 1);
-    const uint16_t *qp = (const uint16_t *)a.q + (((int64_t)b * a.Sq + qrow) * a.Hq + h) * D;
-    u32x4 qf[D / 16];
+    // per block: this lane's row, its last visible key, and the block's most limited row's
+    int qi[2];
+    int64_t klim[2], klim_min[2];
 #pragma unroll
-    for (int s = 0; s < D / 16; ++s)
-        qf[s] = *(const u32x4 *)(qp + 16 * s + 8 * half);
-#pragma unroll
-    for (int s = 0; s < D / 16; ++s)
-        settle(qf[s]);
+    for (int j = 0; j < 2; ++j) {
+        qi[j] = q0 + 32 * j + col;
+        klim[j] = a.causal ? min((int64_t)a.Sk - 1, (int64_t)qi[j] + a.offset) : (int64_t)a.Sk - 1;
+        klim_min[j] = a.causal ? min((int64_t)a.Sk - 1, (int64_t)(q0 + 32 * j) + a.offset)
+                               : (int64_t)a.Sk - 1;
+    }
 
-    f32x16 acc[D / 32];
+    // ---- Q once, as B operands: qf[j][st] = row qi[j], d = 16 st + 8 half .. + 7 -----------
+    u32x4 qf[2][NST];
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
-        acc[dt] = (f32x16){};
-    float frame = -INFINITY, lsum = 0.0f;
+    for (int j = 0; j < 2; ++j) {
+        const int qrow = min(qi[j], a.Sq - 1);
+        const uint16_t *qp = (const uint16_t *)a.q + (((int64_t)b * a.Sq + qrow) * a.Hq + h) * D;
+#pragma unroll
+        for (int s = 0; s < NST; ++s)
+            qf[j][s] = *(const u32x4 *)(qp + 16 * s + 8 * half);
+    }
+    // Q moves to AGPRs here, once, and stays there: the score MFMAs read it from asm, and the
+    // drain below separates the AGPR writes from the first MFMA that reads them
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int s = 0; s < NST; ++s)
+            asm volatile("" : "+a"(qf[j][s]));
+    smfma_drain();
 
-    // ---- DMA of tiles: thread t's chunk n = (i * kNW + wave) * 64 + lane of instruction i ----
+    f32x16 acc[2][NDT];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+            acc[j][dt] = (f32x16){};
+    float frame[2] = {-INFINITY, -INFINITY}, lsum[2] = {0.0f, 0.0f};
+    float fr[2] = {0.0f, 0.0f}, alpha[2] = {1.0f, 1.0f};
+    bool rescale[2] = {false, false};
+
+    // ---- tile DMA: transfer i of thread t moves 16-byte chunk n = (i*kNW + wave)*64 + lane ---
     const uint8_t *kg = (const uint8_t *)a.k + ((int64_t)b * a.Sk * a.Hkv + kvh) * G::ROW;
     const uint8_t *vg = (const uint8_t *)a.v + ((int64_t)b * a.Sk * a.Hkv + kvh) * G::ROW;
     const uint32_t grow = (uint32_t)a.Hkv * G::ROW;       // bytes between consecutive keys
-    int drow[G::NDMA];
-    uint32_t kcol[G::NDMA], vcol[G::NDMA];
+    const uint32_t lds0 = lds_addr(lds);
+    // chunk (row r, column chunk c) of transfer i; K and V chunks land swizzled
+    auto chunk_r = [&](int i) INL { return ((i * kNW + wave) * 64 + lane) / G::CPR; };
+    auto chunk_c = [&](int i) INL { return ((i * kNW + wave) * 64 + lane) % G::CPR; };
+    auto kcol = [&](int i) INL { return (uint32_t)((chunk_c(i) ^ G::swk(chunk_r(i))) * 16); };
+    auto vcol = [&](int i) INL { return (uint32_t)((chunk_c(i) ^ G::swv(chunk_r(i))) * 16); };
+    uint32_t rowg[G::NDMA], kc[G::NDMA], vc[G::NDMA], lwave[G::NDMA];
 #pragma unroll
     for (int i = 0; i < G::NDMA; ++i) {
-        const int n = (i * kNW + wave) * 64 + lane;
-        const int r = n / G::CPR, s = n % G::CPR;
-        drow[i] = r;
-        kcol[i] = (uint32_t)((s ^ G::swk(r)) * 16);
-        vcol[i] = (uint32_t)((s ^ G::swv(r)) * 16);
+        rowg[i] = (uint32_t)chunk_r(i) * grow;
+        kc[i] = kcol(i);
+        vc[i] = vcol(i);
+        lwave[i] = __builtin_amdgcn_readfirstlane(lds0 + (uint32_t)((i * kNW + wave) * 1024));
     }
-    auto kstage = [&](int tile) { return lds + (tile % kStages) * G::TILE; };
-    auto vstage = [&](int tile) { return lds + (kStages + tile % kStages) * G::TILE; };
-    auto dma_tile = [&](int tile) {
-        const int k0 = tile * kBN;
-        const int last = a.Sk - 1 - k0;
-        const uint8_t *kt = kg + (int64_t)k0 * grow;
-        const uint8_t *vt = vg + (int64_t)k0 * grow;
-        uint8_t *ks = kstage(tile), *vs = vstage(tile);
-#pragma unroll
-        for (int i = 0; i < G::NDMA; ++i) {
-            const uint32_t roff = (uint32_t)min(drow[i], last) * grow;
-            const int wofs = (i * kNW + wave) * 1024;        // this wave's 1 KB of the tile
-            dma16(kt, roff + kcol[i], lds_addr(ks + wofs));
-            dma16(vt, roff + vcol[i], lds_addr(vs + wofs));
-        }
+    // K stages [0, kStages), V stages [kStages, 2*kStages); tile j lives in stage j % kStages
+    auto kstage = [&](int tl) INL { return lds + (tl & (kStages - 1)) * G::TILE; };
+    auto vstage = [&](int tl) INL { return lds + (kStages + (tl & (kStages - 1))) * G::TILE; };
+    // Transfer i of tile tl of K (is_v false) or V into a stage. Tiles past the last one
+    // re-read the last tile (into a stage nobody reads any more), so every loop iteration
+    // issues the same transfers and the wait counts stay fixed; rows past the end of the
+    // sequence repeat the last key.
+    auto dma_one = [&](bool is_v, int stage, int tl, int i) INL {
+        tl = min(tl, nb - 1);
+        const int k0 = tl * kBN;
+        const uint8_t *gt = (is_v ? vg : kg) + (int64_t)k0 * grow;
+        const uint32_t lastg = (uint32_t)min(kBN - 1, a.Sk - 1 - k0) * grow;
+        dma16(gt, min(rowg[i], lastg) + (is_v ? vc[i] : kc[i]),
+              lwave[i] + (uint32_t)(stage * G::TILE));
     };
-    // wait until at most `pending` tiles of DMA are outstanding, then synchronise the waves
-    auto sync_tiles = [&](bool one_pending) {
-        if (one_pending)
-            __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(2 * G::NDMA));
+    // transfer i of the tiles issued in iteration n: i < NDMA: K(n+4), else V(n+2)
+    auto dma_part = [&](int n, int i) INL {
+        if (i < G::NDMA)
+            dma_one(false, (n + 4) & (kStages - 1), n + 4, i);
         else
-            __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
-        asm volatile("s_barrier" ::: "memory");
+            dma_one(true, kStages + ((n + 2) & (kStages - 1)), n + 2, i - G::NDMA);
     };
 
     // ---- fragment addressing -----------------------------------------------------------------
-    // K: row krow = hf*32 + perm(col); chunk 2*st + half; byte offset in the tile
-    //    krow*ROW + 16*((2*st + half) ^ swk(krow)) = (krow*ROW | X) ^ 32*st
+    // K fragment f (hf = f / NST, st = f % NST): row krow = hf*32 + perm(col), chunk 2*st + half;
+    // byte offset krow*ROW + 16*((2*st + half) ^ swk(krow)) = (krow*ROW | X) ^ 32*st
     const int krow0 = k_row_perm16(col);
     const uint32_t kfx = (uint32_t)(krow0 * G::ROW) | (uint32_t)(16 * (half ^ G::swk(krow0)));
-    // V^T via transpose reads: group g = lane/16, position j = lane%16 as a source lane reads
-    // V[16*t4 + 8*(g/2) + 4*sec + j/4][32*dt + 16*(g%2) + 4*(j%4) .. +3]
-    const int g = lane >> 4, j = lane & 15;
-    const int vr0 = 8 * (g >> 1) + (j >> 2);                  // row within a 16-key group
-    const int vchunk = 2 * (g & 1) + ((j & 3) >> 1);          // chunk within a 32-column block
+    auto kread = [&](const uint8_t *ks, int f) INL -> u32x4 {
+        const int hf = f / NST, st = f % NST;
+        return *(const u32x4 *)(ks + (kfx ^ (uint32_t)(32 * st)) + hf * 32 * G::ROW);
+    };
+    // V^T fragment f (t4 = f / NDT, dt = f % NDT) via transpose reads: group g = lane/16,
+    // position jl = lane%16 as a source lane reads
+    // V[16*t4 + 8*(g/2) + 4*sec + jl/4][32*dt + 16*(g%2) + 4*(jl%4) .. +3]
+    const int g = lane >> 4, jl = lane & 15;
+    const int vr0 = 8 * (g >> 1) + (jl >> 2);                 // row within a 16-key group
+    const int vchunk = 2 * (g & 1) + ((jl & 3) >> 1);         // chunk within a 32-column block
     const uint32_t vfx = (uint32_t)(vr0 * G::ROW) +
-                         (uint32_t)(16 * (vchunk ^ G::swv(vr0)) + 8 * (j & 1));
+                         (uint32_t)(16 * (vchunk ^ G::swv(vr0)) + 8 * (jl & 1));
     // for dt: chunk 4*dt + vchunk, swizzled: (4*dt) ^ swv only touches bits the dt term owns
-    auto vread = [&](const uint8_t *vs, int t4, int dt) -> u32x4 {
+    auto vread = [&](const uint8_t *vs, int f) INL -> u32x4 {
+        const int t4 = f / NDT, dt = f % NDT;
         const uint32_t o = (vfx ^ (uint32_t)(64 * dt)) + (uint32_t)(16 * t4 * G::ROW);
         const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(vs + o));
         const s16x4_t hi =
@@ -195,148 +353,223 @@ __global__ __launch_bounds__(kNT, 2) void prefill16_kernel(Prefill16Params p)
         const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
         return (u32x4){l2[0], l2[1], h2[0], h2[1]};
     };
-    auto scores = [&](const uint8_t *ks, f32x16 *s) {
-        s[0] = (f32x16){};
-        s[1] = (f32x16){};
+
+    // ---- softmax of block j over the scores s (S^T registers of tile n) ------------------------
+    u32x4 pf[2][4];
+    float m8[8];
+    auto mask = [&](int j, f32x16 *s, int n) INL {
+        const int k0 = n * kBN;
+        if ((int64_t)k0 + kBN - 1 > klim_min[j]) {
+            const int lim = (int)max(min(klim[j] - k0, (int64_t)kBN), (int64_t)-1) - 8 * half;
 #pragma unroll
-        for (int st = 0; st < D / 16; ++st) {
-            const uint8_t *kp = ks + (kfx ^ (uint32_t)(32 * st));
-            s[0] = mfma32<BF>(*(const u32x4 *)kp, qf[st], s[0]);
-            s[1] = mfma32<BF>(*(const u32x4 *)(kp + 32 * G::ROW), qf[st], s[1]);
+            for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    if (hf * 32 + 16 * (i / 8) + (i % 8) > lim)
+                        s[hf][i] = -INFINITY;
         }
     };
-
-    // ---- prologue: tiles 0, 1, 2 in flight; wait for 0 and 1 ----------------------------------
+    auto unit = [&](int j, f32x16 *s, int u) INL {
+        if (u < 8) {
+            m8[u] = fmaxf(fmaxf(s[0][2 * u], s[0][2 * u + 1]), fmaxf(s[1][2 * u], s[1][2 * u + 1]));
+            pin(m8[u]);
+        } else if (u == 8) {
 #pragma unroll
-    for (int i = 0; i < 3; ++i)
-        if (i < nb)
-            dma_tile(i);
-    sync_tiles(nb > 2);
-
-    f32x16 s_a[2], s_b[2];
-    if (wave_on && nb > 0 && 0 < wkend)
-        scores(kstage(0), s_a);
-
-    auto tile = [&](const int kb, f32x16 *s_cur, f32x16 *s_next) {
-        // tile kb+1 resident (tile kb+2 may still be in flight); every wave is past tile kb-1,
-        // so its stage can be refilled with tile kb+3
-        if (kb > 0)
-            sync_tiles(kb + 2 < nb);
-        if (kb + 3 < nb)
-            dma_tile(kb + 3);
-        const int k0 = kb * kBN;
-        const bool do_cur = wave_on && k0 < wkend;
-        const bool do_next = wave_on && kb + 1 < nb && k0 + kBN < wkend;
-
-        if (do_cur) {
-            if ((int64_t)k0 + kBN - 1 > klim_min) {
-                const int lim = (int)max(min(klim - k0, (int64_t)kBN), (int64_t)-1) - 8 * half;
+            for (int w = 4; w >= 1; w >>= 1)
 #pragma unroll
-                for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-                    for (int i = 0; i < 16; ++i)
-                        if (hf * 32 + 16 * (i / 8) + (i % 8) > lim)
-                            s_cur[hf][i] = -INFINITY;
-            }
-            float mx = s_cur[0][0];
-#pragma unroll
-            for (int i = 1; i < 16; ++i)
-                mx = fmaxf(mx, s_cur[0][i]);
-#pragma unroll
-            for (int i = 0; i < 16; ++i)
-                mx = fmaxf(mx, s_cur[1][i]);
-            mx = pair_max(mx);
-            const float m2 = mx * a.c;
-            const bool need = m2 > frame + kRescaleMarginLog2;
-            if (__any(need)) {
-                const float alpha = need ? exp2_fast(frame - m2) : 1.0f;
-#pragma unroll
-                for (int dt = 0; dt < D / 32; ++dt)
-                    acc[dt] *= alpha;
-                lsum *= alpha;
-                frame = need ? m2 : frame;
-            }
-        }
-
-        const float fr = (frame == -INFINITY) ? 0.0f : frame;
-        u32x4 pf[4];
-        auto p_chunk = [&](int jj) {
-            const int t4 = jj >> 2, e = jj & 3;
-            const int i = 8 * (t4 & 1) + 2 * e;
-            const float p0 = exp2_fast(__builtin_fmaf(s_cur[t4 >> 1][i], a.c, -fr));
-            const float p1 = exp2_fast(__builtin_fmaf(s_cur[t4 >> 1][i + 1], a.c, -fr));
-            const uint32_t pk = pack2<BF>(p0, p1);
-            pf[t4][e] = pk;
-            lsum = sum2<BF>(pk, lsum);
-        };
-        const uint8_t *vs = vstage(kb);
-        auto pv = [&](int t4) {
-#pragma unroll
-            for (int dt = 0; dt < D / 32; ++dt)
-                acc[dt] = mfma32<BF>(vread(vs, t4, dt), pf[t4], acc[dt]);
-        };
-        if (do_cur && do_next) {
-            constexpr int NMF = D / 8;
-            constexpr int PER = 16 / NMF;
-            const uint8_t *ks = kstage(kb + 1);
-            s_next[0] = (f32x16){};
-            s_next[1] = (f32x16){};
-#pragma unroll
-            for (int jm = 0; jm < NMF; ++jm) {
-                const int hf = jm & 1, st = jm >> 1;
-                const uint8_t *kp = ks + (kfx ^ (uint32_t)(32 * st)) + hf * 32 * G::ROW;
-                s_next[hf] = mfma32<BF>(*(const u32x4 *)kp, qf[st], s_next[hf]);
-#pragma unroll
-                for (int c = 0; c < PER; ++c) {
-                    const int jj = jm * PER + c;
-                    p_chunk(jj);
-                    if ((jj & 3) == 3)
-                        pv(jj >> 2);
-                }
-            }
-            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-            for (int i = 0; i < NMF + 16; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
-            }
+                for (int i = 0; i < w; ++i)
+                    m8[i] = fmaxf(m8[i], m8[i + w]);
+            const float m2 = pair_max(m8[0]) * a.c;
+            const bool need = m2 > frame[j] + kRescaleMarginLog2;
+            alpha[j] = need ? exp2_fast(frame[j] - m2) : 1.0f;
+            frame[j] = need ? m2 : frame[j];
+            fr[j] = (frame[j] == -INFINITY) ? 0.0f : frame[j];
+            lsum[j] *= alpha[j];
+            rescale[j] = __any(need);
+            pin(fr[j]);
         } else {
-            if (do_next)
-                scores(kstage(kb + 1), s_next);
-            if (do_cur) {
+            const int t4 = (u - 9) >> 2, e = (u - 9) & 3;
+            const int i = 8 * (t4 & 1) + 2 * e;
+            const float p0 = exp2_fast(__builtin_fmaf(s[t4 >> 1][i], a.c, -fr[j]));
+            const float p1 = exp2_fast(__builtin_fmaf(s[t4 >> 1][i + 1], a.c, -fr[j]));
+            uint32_t pk = pack2<BF>(p0, p1);
+            pin(pk);
+            pf[j][t4][e] = pk;
+            lsum[j] = sum2<BF>(pk, lsum[j]);
+        }
+    };
+    auto apply_rescale = [&](int j) INL {
+        if (rescale[j]) {
 #pragma unroll
-                for (int jj = 0; jj < 16; ++jj) {
-                    p_chunk(jj);
-                    if ((jj & 3) == 3)
-                        pv(jj >> 2);
-                }
-            }
+            for (int dt = 0; dt < NDT; ++dt)
+                acc[j][dt] *= alpha[j];
         }
     };
 
-    for (int kb = 0; kb < nb; kb += 2) {
-        tile(kb, s_a, s_b);
-        if (kb + 1 < nb)
-            tile(kb + 1, s_b, s_a);
+    // ---- MFMA slots ----------------------------------------------------------------------------
+    // P.V slot i: V^T fragment i/2 times P of block i%2; score slot i: K fragment i/2 times Q
+    // of block i%2 (fragments in hf-major order, so block 0's hf = 0 chain finishes first)
+    auto pv_slot = [&](int i, const u32x4 &vf) INL {
+        const int f = i >> 1, j = i & 1, t4 = f / NDT, dt = f % NDT;
+        acc[j][dt] = mfma32<BF>(vf, pf[j][t4], acc[j][dt]);
+    };
+    auto s_slot = [&](int i, const u32x4 &kf, f32x16 *s0, f32x16 *s1) INL {
+        const int f = i >> 1, j = i & 1, hf = f / NST, st = f % NST;
+        f32x16 *s = j == 0 ? s0 : s1;
+        if (st == 0)
+            smfma_first<BF>(s[hf], kf, qf[j][st]);
+        else
+            smfma_acc<BF>(s[hf], kf, qf[j][st]);
+    };
+    // Fragment reads run kRead fragments ahead of their MFMAs through a ring of kRead + 1
+    // registers; sched_barrier fences keep the compiler from hoisting every read at once.
+    constexpr int kRead = 3;
+    auto scores_all = [&](const uint8_t *ks, f32x16 *s0, f32x16 *s1) INL {
+        u32x4 fb[kRead + 1];
+        static_for<0, kRead>([&](auto fc) { fb[fc.value] = kread(ks, fc.value); });
+        static_for<0, 2 * NST>([&](auto fc) {
+            constexpr int f = decltype(fc)::value;
+            if constexpr (f + kRead < 2 * NST)
+                fb[(f + kRead) % (kRead + 1)] = kread(ks, f + kRead);
+            s_slot(2 * f, fb[f % (kRead + 1)], s0, s1);
+            s_slot(2 * f + 1, fb[f % (kRead + 1)], s0, s1);
+            __builtin_amdgcn_sched_barrier(0);
+        });
+    };
+    auto pv_all = [&](const uint8_t *vs) INL {
+        u32x4 fb[kRead + 1];
+        static_for<0, kRead>([&](auto fc) { fb[fc.value] = vread(vs, fc.value); });
+        static_for<0, 4 * NDT>([&](auto fc) {
+            constexpr int f = decltype(fc)::value;
+            if constexpr (f + kRead < 4 * NDT)
+                fb[(f + kRead) % (kRead + 1)] = vread(vs, f + kRead);
+            pv_slot(2 * f, fb[f % (kRead + 1)]);
+            pv_slot(2 * f + 1, fb[f % (kRead + 1)]);
+            __builtin_amdgcn_sched_barrier(0);
+        });
+    };
+
+    // One tile: a fixed slot sequence, fragment reads kRead fragments ahead, softmax units
+    // and DMA transfers at planned slots; sched_barrier fences keep the order. Every tile runs
+    // the same sequence: where a wave has nothing to do the work is harmless (P of tile -1 is
+    // zero against a zeroed V stage, scores of a tile past the last are never used, keys a row
+    // cannot see are masked to -inf and give P = 0).
+    auto tile = [&](int n, f32x16 *s0, f32x16 *s1c, f32x16 *s1n) INL {
+        const uint8_t *vs = vstage(n - 1), *ks = kstage(n + 1);
+        u32x4 fb[kRead + 1];
+        smfma_drain(s0[0], s0[1], s1c[0], s1c[1]);
+        mask(0, s0, n);
+        mask(1, s1c, n);
+        // half 1: P.V of tile n-1 for both blocks | softmax(n) of block 0
+        static_for<0, kRead>([&](auto fc) INL { fb[fc.value] = vread(vs, fc.value); });
+        static_for<0, NM>([&](auto ic) INL {
+            constexpr int i = decltype(ic)::value, f = i >> 1;
+            if constexpr ((i & 1) == 0 && f + kRead < 4 * NDT)
+                fb[(f + kRead) % (kRead + 1)] = vread(vs, f + kRead);
+            pv_slot(i, fb[f % (kRead + 1)]);
+            static_for<PL::h1.first[i], PL::h1.first[i + 1]>([&](auto uc) INL {
+                unit(0, s0, decltype(uc)::value);
+            });
+            __builtin_amdgcn_sched_barrier(0);
+        });
+        apply_rescale(0);
+        // half 2: scores of tile n+1 for both blocks | rest of block 0, softmax(n) of block 1
+        auto unit2 = [&](auto uc) INL {
+            constexpr int u = decltype(uc)::value;
+            if constexpr (u < PL::carry)
+                unit(0, s0, PL::c0 + u);
+            else
+                unit(1, s1c, u - PL::carry);
+        };
+        static_for<0, kRead>([&](auto fc) INL { fb[fc.value] = kread(ks, fc.value); });
+        static_for<0, NM>([&](auto ic) INL {
+            constexpr int i = decltype(ic)::value, f = i >> 1;
+            if constexpr ((i & 1) == 0 && f + kRead < 2 * NST)
+                fb[(f + kRead) % (kRead + 1)] = kread(ks, f + kRead);
+            s_slot(i, fb[f % (kRead + 1)], s0, s1n);
+            static_for<PL::h2.first[i], PL::h2.first[i + 1]>(unit2);
+            if constexpr ((i & 3) == 1 && (i >> 2) < 2 * G::NDMA)
+                dma_part(n, i >> 2);
+            __builtin_amdgcn_sched_barrier(0);
+        });
+        static_for<PL::h2.first[NM], PL::carry + kUnits>(unit2);
+        apply_rescale(1);
+    };
+
+    // ---- pipeline --------------------------------------------------------------------------------
+    // Iteration n reads K(n+1) and V(n-1) and refills the stages of K(n) and V(n-2), which the
+    // barrier shows every wave is done with, with K(n+4) and V(n+2). Before barrier n the
+    // transfers issued in iterations n-1 and n-2 (2 tiles each) may still be in flight,
+    // nothing older.
+    auto wait_tiles = [&](int pend_tiles) INL {
+        if (pend_tiles >= 4)
+            __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(4 * G::NDMA));
+        else if (pend_tiles >= 2)
+            __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(2 * G::NDMA));
+        else
+            __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+        asm volatile("s_barrier" ::: "memory");
+    };
+    // prologue: K(0..3), V(0..1)
+    if (nb > 0) {
+#pragma unroll
+        for (int tl = 0; tl < 4; ++tl)
+#pragma unroll
+            for (int i = 0; i < G::NDMA; ++i)
+                dma_one(false, tl, tl, i);
+#pragma unroll
+        for (int tl = 0; tl < 2; ++tl)
+#pragma unroll
+            for (int i = 0; i < G::NDMA; ++i)
+                dma_one(true, kStages + tl, tl, i);
     }
-    // no DMA is outstanding here: the last wait was for zero pending tiles
+
+    // V stage kStages-1 stands in for tile -1: zeros, so that P.V of tile -1 adds nothing
+    // (P is zero too); the DMA of tile kStages-1 into it is issued after barrier 1
+    {
+        uint8_t *z = vstage(-1);
+        for (int o = t * 16; o < G::TILE; o += kNT * 16)
+            *(u32x4 *)(z + o) = (u32x4){0u, 0u, 0u, 0u};
+        for (int i = 0; i < 4; ++i)
+            pf[0][i] = pf[1][i] = (u32x4){0u, 0u, 0u, 0u};
+    }
+    f32x16 s0[2], s1a[2], s1b[2];
+    auto iteration = [&](int n, f32x16 *s1c, f32x16 *s1n) INL {
+        wait_tiles(2 * min(n, 2));
+        tile(n, s0, s1c, s1n);
+    };
+    if (nb > 0) {
+        wait_tiles(0);           // K(0) resident; also orders the zero fill before its reads
+        scores_all(kstage(0), s0, s1a);
+    }
+    for (int n = 0; n < nb; n += 2) {
+        iteration(n, s1a, s1b);
+        if (n + 1 < nb)
+            iteration(n + 1, s1b, s1a);
+    }
+    // the last tile's P.V: its V may have been in flight at the last barrier
+    wait_tiles(0);
+    if (nb >= 1)
+        pv_all(vstage(nb - 1));
 
     // ---- epilogue ----------------------------------------------------------------------------
-    const float ltot = pair_sum(lsum);
-    if (!wave_on || qi >= a.Sq)
-        return;
-    const float inv = ltot > 0.0f ? 1.0f / ltot : 0.0f;
-    uint16_t *op = (uint16_t *)a.o + (((int64_t)b * a.Sq + qi) * a.Hq + h) * D;
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
+    for (int j = 0; j < 2; ++j) {
+        const float ltot = pair_sum(lsum[j]);
+        if (!wave_on || qi[j] >= a.Sq)
+            continue;
+        const float inv = ltot > 0.0f ? 1.0f / ltot : 0.0f;
+        uint16_t *op = (uint16_t *)a.o + (((int64_t)b * a.Sq + qi[j]) * a.Hq + h) * D;
 #pragma unroll
-        for (int ii = 0; ii < 4; ++ii) {
-            u32x2 w;
-            w[0] = pack2<BF>(acc[dt][4 * ii + 0] * inv, acc[dt][4 * ii + 1] * inv);
-            w[1] = pack2<BF>(acc[dt][4 * ii + 2] * inv, acc[dt][4 * ii + 3] * inv);
-            *(u32x2 *)(op + 32 * dt + 8 * ii + 4 * half) = w;
-        }
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) {
+                u32x2 w;
+                w[0] = pack2<BF>(acc[j][dt][4 * ii + 0] * inv, acc[j][dt][4 * ii + 1] * inv);
+                w[1] = pack2<BF>(acc[j][dt][4 * ii + 2] * inv, acc[j][dt][4 * ii + 3] * inv);
+                *(u32x2 *)(op + 32 * dt + 8 * ii + 4 * half) = w;
+            }
+    }
 }
 
 template <int D, bool BF>
@@ -348,6 +581,18 @@ hipError_t launch16(const Prefill16Params &p, int64_t n_wg, hipStream_t stream)
 
 }  // namespace
 
+PrefillGrid prefill16_grid(const AttnArgs &a)
+{
+    PrefillGrid g;
+    g.waves = kNW;
+    g.hpw = a.G < kNW ? a.G : kNW;
+    g.qsub = kNW / g.hpw;
+    g.n_qblk = (a.Sq + kQW * g.qsub - 1) / (kQW * g.qsub);
+    g.n_hchunk = (a.G + g.hpw - 1) / g.hpw;
+    g.n_wg = (int64_t)g.n_qblk * g.n_hchunk * a.Hkv * a.B;
+    return g;
+}
+
 hipError_t launch_prefill16(const AttnArgs &a, const PrefillGrid &g, hipStream_t stream)
 {
     const Prefill16Params p{a, g.hpw, g.qsub, g.n_qblk, g.n_hchunk};
@@ -357,5 +602,7 @@ hipError_t launch_prefill16(const AttnArgs &a, const PrefillGrid &g, hipStream_t
     return a.kv == KV_BF16 ? launch16<64, true>(p, g.n_wg, stream)
                            : launch16<64, false>(p, g.n_wg, stream);
 }
+
+#undef INL
 
 }  // namespace fa
