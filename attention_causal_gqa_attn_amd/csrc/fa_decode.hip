@@ -79,6 +79,54 @@ __device__ __forceinline__ void decode_tile(const uint16_t *lk, const uint16_t *
         acc[dt] = mfma16k16<BF>(*(const u32x2 *)(vr + 16 * dt * Geo::vStride), pf, acc[dt]);
 }
 
+// Combine the 4 waves' softmax states of each row (through LDS at cmb, 4*16*(D+2) floats)
+// and write the split's partial [F, L, O] rows.
+template <int D>
+__device__ __forceinline__ void decode_combine(const DecodeParams &p, float *cmb, int b, int kvh,
+                                               int s, int t, int wave, int quad, int r,
+                                               const f32x4 *acc, float frame, float lsum)
+{
+    const AttnArgs &a = p.a;
+    lsum += __shfl_xor(lsum, 16, 64);
+    lsum = pair_sum(lsum);
+    float *cmb_o = cmb;                             // [4 waves][16 rows][D]
+    float *cmb_f = cmb_o + 4 * 16 * D;              // [4][16]
+    float *cmb_l = cmb_f + 64;                      // [4][16]
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            cmb_o[(wave * 16 + r) * D + 16 * dt + 4 * quad + i] = acc[dt][i];
+    if (quad == 0) {
+        cmb_f[wave * 16 + r] = frame;
+        cmb_l[wave * 16 + r] = lsum;
+    }
+    __syncthreads();
+
+    float *out = p.part + (((int64_t)b * a.Hkv + kvh) * p.n_split + s) * p.rows * (D + 2);
+    for (int e = t; e < p.rows * D; e += kThreads) {
+        const int rr = e / D, d = e % D;
+        float F = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+            F = fmaxf(F, cmb_f[w * 16 + rr]);
+        float o = 0.0f, l = 0.0f;
+        if (F != -INFINITY) {
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const float sw = exp2_fast(cmb_f[w * 16 + rr] - F);   // 0 for an empty wave
+                o += sw * cmb_o[(w * 16 + rr) * D + d];
+                l += sw * cmb_l[w * 16 + rr];
+            }
+        }
+        out[rr * (D + 2) + d] = o;
+        if (d == 0) {
+            out[rr * (D + 2) + D] = F;
+            out[rr * (D + 2) + D + 1] = l;
+        }
+    }
+}
+
 // Tiles whose global loads are in flight at once per workgroup: decode has little work per
 // byte, so keeping HBM busy needs several tiles outstanding. The q4_0 staging registers are
 // small (10 per thread per tile), the 16-bit ones are not.
@@ -194,45 +242,146 @@ __global__ __launch_bounds__(kThreads, kDecodeOccupancy<KV>) void decode_split_k
         }
     }
 
-    // ---- combine the 4 waves' states of each row, write the split's partial ---------------
-    lsum += __shfl_xor(lsum, 16, 64);
-    lsum = pair_sum(lsum);
-    float *cmb_o = (float *)lds;                    // [4 waves][16 rows][D]
-    float *cmb_f = cmb_o + 4 * 16 * D;              // [4][16]
-    float *cmb_l = cmb_f + 64;                      // [4][16]
+    decode_combine<D>(p, (float *)lds, b, kvh, s, t, wave, quad, r, acc, frame, lsum);
+}
+
+// ---- q4_0 caches: raw blocks through an LDS-DMA ring -----------------------------------------
+// A key's q4_0 row of one KV head (D/32 blocks of 18 bytes) is cut into 12-byte chunks, each
+// copied into a 16-byte LDS slot by global_load_lds_dwordx3, in the slot layout the tile
+// loader reads (padding slots get a repeat of the row's last chunk); a whole tile (64 keys of
+// K, then of V) is NI wave-wide transfers, NIW per wave. Tiles run two ahead through kRS = 3
+// raw stages; the tile loader dequantizes a raw stage into the f16 K / V^T tiles as before.
+constexpr int kRS = 3;
+
+// One 12-byte LDS-DMA transfer per lane: gbase + voff -> LDS lds_base + 16 * lane. Issued from
+// asm for the same reason as in the prefill kernel (the compiler would wait for every
+// outstanding transfer before each LDS read); the kernel orders the LDS data with explicit
+// vmcnt waits and barriers, and nothing else in it uses M0. An SALU write of M0 needs one wait
+// state before the LDS-DMA load that reads it.
+__device__ __forceinline__ void dma12(const uint8_t *gbase, uint32_t voff, uint32_t lds_base)
+{
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx3 %0, %1"
+                 :: "v"(voff), "s"(gbase), "s"(lds_base) : "memory");
+}
+
+// s_waitcnt immediate: at most `vm` vector-memory ops outstanding, all LDS ops done
+constexpr int waitcnt_vm_lgkm0(int vm) { return (vm & 15) | ((vm >> 4) << 14) | (7 << 4); }
+
+template <int D>
+__global__ __launch_bounds__(kThreads, 2) void decode_q4_kernel(DecodeParams p)
+{
+    using Geo = TileGeom<D>;
+    using LD = TileLoader<D, KV_Q4_0>;
+    constexpr int CPR = LD::RAW_CPR;                // 12-byte chunks per key row
+    constexpr int ST = LD::RAW_STRIDE;              // slots per row (CPR rounded up to odd)
+    constexpr int RAW_T = 16 * LD::RAW_SLOTS;       // bytes of one tensor's raw tile in LDS
+    constexpr int NI = 2 * ST;                      // wave-wide transfers per tile (K, then V)
+    constexpr int NIW = (NI + 3) / 4;               // per wave (surplus ones repeat the last)
+    constexpr int kLdsElems = Geo::stage > 4 * 16 * (D + 2) * 2 ? Geo::stage
+                                                                 : 4 * 16 * (D + 2) * 2;
+    __shared__ __attribute__((aligned(16))) uint16_t lds[kLdsElems];
+    __shared__ __attribute__((aligned(16))) uint8_t raw[kRS * 2 * RAW_T];
+
+    const AttnArgs &a = p.a;
+    const int t = threadIdx.x, lane = t & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int quad = lane >> 4, r = lane & 15;
+
+    int rest = xcd_remap(blockIdx.x, gridDim.x);
+    const int kvh = rest % a.Hkv;
+    rest /= a.Hkv;
+    const int s = rest % p.n_split;
+    const int b = rest / p.n_split;
+
+    const int64_t ks = (int64_t)s * p.split_len;
+    const int64_t ke = min(ks + p.split_len, p.kend);
+    const int nb = ke > ks ? (int)((ke - ks + kBN - 1) / kBN) : 0;
+
+    const bool row_on = r < p.rows;
+    const int qi = row_on ? r / a.G : 0;
+    const int hl = row_on ? r % a.G : 0;
+    const int h = kvh * a.G + hl;
+    int64_t rowlim = ke - 1;
+    if (a.causal)
+        rowlim = min(rowlim, (int64_t)qi + a.offset);
+    if (!row_on)
+        rowlim = -1;
+
+    u32x4 qf[D / 32];
+    {
+        const uint16_t *qp = (const uint16_t *)a.q + (((int64_t)b * a.Sq + qi) * a.Hq + h) * D;
+#pragma unroll
+        for (int kk = 0; kk < D / 32; ++kk)
+            qf[kk] = row_on ? *(const u32x4 *)(qp + 32 * kk + 8 * quad) : (u32x4){};
+#pragma unroll
+        for (int kk = 0; kk < D / 32; ++kk)
+            settle(qf[kk]);
+    }
+    f32x4 acc[D / 16];
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt)
+        acc[dt] = (f32x4){};
+    float frame = -INFINITY, lsum = 0.0f;
+
+    // ---- transfers: this wave's m-th transfer of a tile is i = min(wave + 4 m, NI - 1) -----
+    const uint32_t grow = (uint32_t)a.Hkv * LD::ROWB;            // bytes between keys
+    const int64_t head0 = ((int64_t)b * a.Sk * a.Hkv + kvh) * LD::ROWB;
+    const uint8_t *kg = (const uint8_t *)a.k + head0, *vg = (const uint8_t *)a.v + head0;
+    const uint32_t raw0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t *)raw;
+    uint32_t crow[NIW], ccol[NIW];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            cmb_o[(wave * 16 + r) * D + 16 * dt + 4 * quad + i] = acc[dt][i];
-    if (quad == 0) {
-        cmb_f[wave * 16 + r] = frame;
-        cmb_l[wave * 16 + r] = lsum;
+    for (int m = 0; m < NIW; ++m) {
+        const int i = min(wave + 4 * m, NI - 1);
+        const int sl = (i % ST) * 64 + lane;        // slot within the tensor's tile
+        const int rr = sl / (32 * ST), kp = (sl % (32 * ST)) / ST, j = sl % ST;
+        crow[m] = (uint32_t)(2 * kp + rr);
+        ccol[m] = (uint32_t)(12 * min(j, CPR - 1));
+    }
+    auto dma_tile = [&](int kb) {
+        const int k0 = (int)ks + kb * kBN;
+        const uint32_t last = (uint32_t)min(kBN - 1, a.Sk - 1 - k0);
+        const uint32_t stage = raw0 + (uint32_t)((kb % kRS) * 2 * RAW_T);
+#pragma unroll
+        for (int m = 0; m < NIW; ++m) {
+            const int i = min(wave + 4 * m, NI - 1);
+            const bool is_v = i >= ST;
+            const uint8_t *gt = (is_v ? vg : kg) + (int64_t)k0 * grow;
+            const uint32_t lbase = stage + (uint32_t)((is_v ? RAW_T : 0) + (i % ST) * 64 * 16);
+            dma12(gt, min(crow[m], last) * grow + ccol[m],
+                  __builtin_amdgcn_readfirstlane(lbase));
+        }
+    };
+    // before the barrier of tile kb its raw stage is complete; tile kb+1 may be in flight
+    auto wait_raw = [&](bool next_pending) {
+        if (next_pending)
+            __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(NIW));
+        else
+            __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+        asm volatile("s_barrier" ::: "memory");
+    };
+
+    LD ld;
+    ld.init(a.k, a.v, (int64_t)b * a.Sk * a.Hkv + kvh, a.Hkv, a.Sk, t);
+    uint16_t *lk = lds, *lv = lds + Geo::kElems;
+    if (nb > 0)
+        dma_tile(0);
+    if (nb > 1)
+        dma_tile(1);
+    for (int kb = 0; kb < nb; ++kb) {
+        // raw(kb) resident; every wave is done with the f16 tiles of kb-1 and (dequantized in
+        // iteration kb-1) the raw stage that tile kb+2 now goes into
+        wait_raw(kb + 1 < nb);
+        if (kb + 2 < nb)
+            dma_tile(kb + 2);
+        const uint8_t *rs = raw + (kb % kRS) * 2 * RAW_T;
+        ld.load_raw(rs, rs + RAW_T);
+        ld.store(lk, lv);
+        __syncthreads();
+        decode_tile<D, false>(lk, lv, (int)ks + kb * kBN, wave, quad, r, rowlim, a.c, qf, acc,
+                              frame, lsum);
     }
     __syncthreads();
-
-    float *out = p.part + (((int64_t)b * a.Hkv + kvh) * p.n_split + s) * p.rows * (D + 2);
-    for (int e = t; e < p.rows * D; e += kThreads) {
-        const int rr = e / D, d = e % D;
-        float F = -INFINITY;
-#pragma unroll
-        for (int w = 0; w < 4; ++w)
-            F = fmaxf(F, cmb_f[w * 16 + rr]);
-        float o = 0.0f, l = 0.0f;
-        if (F != -INFINITY) {
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                const float sw = exp2_fast(cmb_f[w * 16 + rr] - F);   // 0 for an empty wave
-                o += sw * cmb_o[(w * 16 + rr) * D + d];
-                l += sw * cmb_l[w * 16 + rr];
-            }
-        }
-        out[rr * (D + 2) + d] = o;
-        if (d == 0) {
-            out[rr * (D + 2) + D] = F;
-            out[rr * (D + 2) + D + 1] = l;
-        }
-    }
+    decode_combine<D>(p, (float *)lds, b, kvh, s, t, wave, quad, r, acc, frame, lsum);
 }
 
 // One wave per (b, KV head, row): log-sum-exp merge of the row's n_split partials.
@@ -284,8 +433,12 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeParams p)
 template <int D, int KV>
 hipError_t launch(const DecodeParams &p, int64_t n_wg, hipStream_t stream)
 {
-    hipLaunchKernelGGL((decode_split_kernel<D, KV>), dim3((unsigned)n_wg), dim3(kThreads), 0,
-                       stream, p);
+    if constexpr (KV == KV_Q4_0)
+        hipLaunchKernelGGL((decode_q4_kernel<D>), dim3((unsigned)n_wg), dim3(kThreads), 0,
+                           stream, p);
+    else
+        hipLaunchKernelGGL((decode_split_kernel<D, KV>), dim3((unsigned)n_wg), dim3(kThreads), 0,
+                           stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
@@ -297,9 +450,9 @@ hipError_t launch(const DecodeParams &p, int64_t n_wg, hipStream_t stream)
 
 }  // namespace
 
-// Split choice: about 1024 workgroups in all (several per CU), each split a whole number of
+// Split choice: about 512 workgroups in all (two per CU), each split a whole number of
 // 64-key tiles and at least one tile.
-constexpr int64_t kTargetWorkgroups = 1024;
+constexpr int64_t kTargetWorkgroups = 512;
 
 DecodeGrid decode_grid(int B, int Hq, int Hkv, int Sq, int Sk, int D, int64_t kend, bool bound)
 {

@@ -215,6 +215,37 @@ struct TileLoader<D, KV_Q4_0, NT> {
         }
     }
 
+    // Staging through LDS instead: the raw tile is copied into LDS by 12-byte LDS-DMA
+    // transfers, each landing in a 16-byte slot. Chunk j (bytes 12j .. 12j+11) of key row
+    // 2*kp + rr sits in slot (rr*32 + kp) * RAW_STRIDE + j: even and odd rows in separate
+    // halves and an odd slot stride, so the 16-byte reads of consecutive lanes (consecutive kp)
+    // hit distinct LDS banks. A block (18 bytes from 18*blk) spans chunks jA = 18*blk / 12 and
+    // jA + 1, starting at byte 0 or 6 of chunk jA.
+    static constexpr int RAW_CPR = ROWB / 12;
+    static constexpr int RAW_STRIDE = RAW_CPR | 1;
+    static constexpr int RAW_SLOTS = 64 * RAW_STRIDE;          // slots of one tensor's tile
+    static_assert(ROWB % 12 == 0, "key rows split into 12-byte chunks");
+    __device__ __forceinline__ void load_raw(const uint8_t *rk, const uint8_t *rv)
+    {
+        if (!busy())
+            return;
+        const uint8_t *r = tensor ? rv : rk;
+        const int ja = (18 * blk) / 12;
+#pragma unroll
+        for (int rr = 0; rr < 2; ++rr) {
+            const uint8_t *sa = r + 16 * ((rr * 32 + kp) * RAW_STRIDE + ja);
+            const u32x4 A = *(const u32x4 *)sa, Bq = *(const u32x4 *)(sa + 16);
+            // the 5-dword window of load(): starts at byte 0 of chunk jA (mis 0) or 4 (mis 2)
+            if (mis == 0) {
+                w[rr][0] = A[0]; w[rr][1] = A[1]; w[rr][2] = A[2];
+                w[rr][3] = Bq[0]; w[rr][4] = Bq[1];
+            } else {
+                w[rr][0] = A[1]; w[rr][1] = A[2]; w[rr][2] = Bq[0];
+                w[rr][3] = Bq[1]; w[rr][4] = Bq[2];
+            }
+        }
+    }
+
     // K (V) halves: threads [0, D) stage K, [D, 2D) stage V; at D = 128 this is wave-uniform.
     __device__ __forceinline__ void load_k(int k0)
     {
