@@ -137,35 +137,165 @@ __device__ __forceinline__ void static_for(F &&f)
         static_for_impl<B>(f, std::make_integer_sequence<int, E - B>{});
 }
 
-// ---- compile-time placement of the softmax work over the MFMA slots of a half --------------
-// The softmax of one block and tile is 25 units: 8 partial maxima (unit 0..7), the frame
-// update (8), and 16 exponential units (9..24; unit 9 + 4*t4 + e makes P chunk t4, pair e).
-// Units run in order; each goes into the first slot at or after its earliest slot with room
-// (room 2 per slot: a partial maximum weighs 1, any other unit 2). Units that do not fit run
-// after the last slot.
-constexpr int kUnits = 25;
-struct UnitList {
-    int n;
-    int earliest[2 * kUnits];
-    int weight[2 * kUnits];
+// ---- compile-time placement of the softmax work over the MFMA slots of a tile ---------------
+// A tile is 2*NM MFMA slots: slots [0, NM) are half 1 (P.V), [NM, 2*NM) half 2 (scores). The
+// softmax of each block j is cut into short units:
+//   M0..M7  partial maxima of the 32 scores (m8[i] = max of 4)
+//   T1, T2  the rest of the lane's max;  P  the lane-pair max (the row max)
+//   F1, F2  frame update: alpha, new frame, lsum *= alpha, whether any lane rescales
+//   E0..E15 two scores to P values (exp2(s*c - frame)); Cu packs E u's pair into P chunk
+//           t4 = u/4 (slot e = u%4) and adds it to lsum
+// A list scheduler places them: every unit after the units it depends on (in an earlier
+// slot: the slot's MFMA covers the latency), not before its earliest slot, within a cycle
+// budget per slot (issue cycles of its VALU instructions; an MFMA leaves about 16 of its 32).
+// Earliest slots: C units of block 0 write pf[0][t4], which the block-0 P.V MFMAs of chunk t4
+// read in half 1 (the last one in slot 2*(t4*NDT + NDT - 1)); block 1's C units write
+// pf[1][t4] (read up to slot 2*(t4*NDT + NDT - 1) + 1). Deadlines, checked below: block 0's
+// E units for chunks 2, 3 read its hf = 1 scores, which the block-0 score MFMAs of hf = 1
+// overwrite from slot NM + 2*NST on (those of chunks 0, 1, hf = 0, from slot NM).
+enum UnitKind { UM, UT1, UT2, UP, UF1, UF2, UE, UC };
+struct Unit {
+    int j, kind, idx;
 };
-struct UnitPlan {
-    int first[64 + 1];       // units [first[s], first[s+1]) run in slot s; first[NM]: leftovers
-};
-constexpr UnitPlan plan_units(int nslots, const UnitList &l)
+constexpr int kUnitsPerBlock = 8 + 5 + 16 + 16;
+constexpr int kNU = 2 * kUnitsPerBlock;
+constexpr int unit_cost(int kind)
 {
-    UnitPlan pl{};
-    int u = 0;
-    for (int s = 0; s < nslots; ++s) {
-        pl.first[s] = u;
-        int room = 2;
-        while (u < l.n && l.earliest[u] <= s && l.weight[u] <= room) {
-            room -= l.weight[u];
-            ++u;
+    switch (kind) {
+    case UM: return 8;
+    case UT1: return 16;
+    case UT2: return 12;
+    case UP: return 24;
+    case UF1: return 12;
+    case UF2: return 28;
+    case UE: return 26;
+    default: return 8;
+    }
+}
+struct Schedule {
+    Unit unit[kNU];           // in slot order
+    int slot[kNU];            // slot of unit[i]
+    int first[129];           // units [first[s], first[s+1]) run in slot s; first[2*NM]: after
+};
+template <int NDT, int NST, int NM, int BUDGET>
+constexpr Schedule make_schedule()
+{
+    // priority order
+    Unit u[kNU] = {};
+    int n = 0;
+    auto chain = [&](int j) {
+        for (int i = 0; i < 8; ++i)
+            u[n++] = Unit{j, UM, i};
+        u[n++] = Unit{j, UT1, 0};
+        u[n++] = Unit{j, UT2, 0};
+        u[n++] = Unit{j, UP, 0};
+        u[n++] = Unit{j, UF1, 0};
+        u[n++] = Unit{j, UF2, 0};
+    };
+    auto expc = [&](int j, int lo, int hi) {       // E lo..hi-1, each C one E behind
+        for (int e = lo; e < hi; ++e) {
+            u[n++] = Unit{j, UE, e};
+            if (e > lo)
+                u[n++] = Unit{j, UC, e - 1};
+        }
+        u[n++] = Unit{j, UC, hi - 1};
+    };
+    chain(0);
+    expc(0, 0, 8);
+    chain(1);
+    expc(0, 8, 16);
+    expc(1, 0, 16);
+    auto earliest = [&](const Unit &x) {
+        if (x.kind == UC) {
+            const int t4 = x.idx / 4;
+            return 2 * (t4 * NDT + NDT - 1) + 1 + x.j;
+        }
+        if (x.j == 1 && x.kind == UE)
+            return NM;
+        return 0;
+    };
+    // dependencies: index of each unit's predecessor(s) in u[]
+    auto find = [&](int j, int kind, int idx) {
+        for (int i = 0; i < kNU; ++i)
+            if (u[i].j == j && u[i].kind == kind && u[i].idx == idx)
+                return i;
+        return -1;
+    };
+    int placed[kNU] = {};
+    for (int i = 0; i < kNU; ++i)
+        placed[i] = -1;
+    Schedule sc{};
+    int out = 0;
+    const int budget = BUDGET;
+    for (int s = 0; s < 2 * NM; ++s) {
+        sc.first[s] = out;
+        int room = budget;
+        for (int i = 0; i < kNU; ++i) {
+            if (placed[i] >= 0 || earliest(u[i]) > s)
+                continue;
+            const Unit &x = u[i];
+            bool ready = true;
+            auto need = [&](int k) {
+                if (k < 0 || placed[k] < 0 || placed[k] >= s)
+                    ready = false;
+            };
+            if (x.kind == UT1)
+                for (int m = 0; m < 8; ++m)
+                    need(find(x.j, UM, m));
+            if (x.kind == UT2)
+                need(find(x.j, UT1, 0));
+            if (x.kind == UP)
+                need(find(x.j, UT2, 0));
+            if (x.kind == UF1)
+                need(find(x.j, UP, 0));
+            if (x.kind == UF2)
+                need(find(x.j, UF1, 0));
+            if (x.kind == UE)
+                need(find(x.j, UF2, 0));
+            if (x.kind == UC)
+                need(find(x.j, UE, x.idx));
+            if (!ready)
+                continue;
+            const int c = unit_cost(x.kind);
+            if (c > room && room < budget)
+                continue;
+            room -= c;
+            placed[i] = s;
+            sc.unit[out] = x;
+            sc.slot[out] = s;
+            ++out;
+            if (room <= 0)
+                break;
         }
     }
-    pl.first[nslots] = u;
-    return pl;
+    sc.first[2 * NM] = out;
+    // anything left runs after the last slot, in priority order
+    for (int i = 0; i < kNU; ++i)
+        if (placed[i] < 0) {
+            sc.unit[out] = u[i];
+            sc.slot[out] = 2 * NM;
+            ++out;
+        }
+    return sc;
+}
+// checks: block 0's E units meet their deadlines, block 0's frame update (which the rescale
+// between the halves needs) is in half 1, and only block 1 units run after the last slot
+template <int NDT, int NST, int NM>
+constexpr bool schedule_ok(const Schedule &sc)
+{
+    for (int i = 0; i < kNU; ++i) {
+        const Unit &x = sc.unit[i];
+        if (x.j == 0 && x.kind == UE) {
+            const int deadline = (x.idx / 8) == 0 ? NM : NM + 2 * NST;   // hf of chunk idx/4
+            if (sc.slot[i] >= deadline)
+                return false;
+        }
+        if (x.j == 0 && x.kind == UF2 && sc.slot[i] >= NM)
+            return false;
+        if (x.j == 0 && sc.slot[i] >= 2 * NM)
+            return false;
+    }
+    return true;
 }
 
 template <int D>
@@ -174,36 +304,10 @@ struct Plans {
     static constexpr int NST = D / 16;                 // k-steps of a score chain
     static constexpr int NM = 8 * NDT;                 // MFMA slots per half
     static_assert(NM == 4 * NST && NM <= 64, "both halves have NM MFMA slots");
-    // half 1: the exponential units of chunk t4 overwrite pf[0][t4], which the block-0 MFMAs
-    // of chunk t4 read; the last of those is in slot 2 * (t4 * NDT + NDT - 1)
-    static constexpr UnitList list1()
-    {
-        UnitList l{};
-        l.n = kUnits;
-        for (int u = 0; u < kUnits; ++u) {
-            l.earliest[u] = u < 9 ? 0 : 2 * (((u - 9) / 4) * NDT + NDT - 1) + 1;
-            l.weight[u] = u < 8 ? 1 : 2;
-        }
-        return l;
-    }
-    static constexpr UnitPlan h1 = plan_units(NM, list1());
-    static constexpr int c0 = h1.first[NM];            // first unit of block 0 left to half 2
-    static constexpr int carry = kUnits - c0;
-    // half 2: block 0's leftover units first (they read block 0's hf = 1 scores, which the
-    // block-0 score MFMAs of hf = 1 overwrite from slot 2 * NST on), then block 1's 25 units
-    static constexpr UnitList list2()
-    {
-        UnitList l{};
-        l.n = carry + kUnits;
-        for (int u = 0; u < l.n; ++u) {
-            l.earliest[u] = 0;
-            l.weight[u] = (u >= carry && u - carry < 8) ? 1 : 2;
-        }
-        return l;
-    }
-    static constexpr UnitPlan h2 = plan_units(NM, list2());
-    static_assert(c0 >= 9 + 8, "only exponential units of chunks 2, 3 (hf = 1) are carried");
-    static_assert(h2.first[2 * NST] >= carry, "carried units run before the hf = 1 scores");
+    // VALU cycles per slot: an MFMA slot leaves about 16; D = 64 has half the MFMAs for the
+    // same softmax work and packs the units tighter
+    static constexpr Schedule sc = make_schedule<NDT, NST, NM, D == 128 ? 24 : 56>();
+    static_assert(schedule_ok<NDT, NST, NM>(sc), "softmax units placed in time");
 };
 
 template <int D, bool BF>
@@ -356,7 +460,9 @@ __global__ __launch_bounds__(kNT, 1) void prefill16_kernel(Prefill16Params p)
 
     // ---- softmax of block j over the scores s (S^T registers of tile n) ------------------------
     u32x4 pf[2][4];
-    float m8[8];
+    float m8[2][8], mx[2], m2[2];
+    bool need[2];
+    float pv2[2][16][2];                           // P values between an E unit and its C unit
     auto mask = [&](int j, f32x16 *s, int n) INL {
         const int k0 = n * kBN;
         if ((int64_t)k0 + kBN - 1 > klim_min[j]) {
@@ -369,30 +475,48 @@ __global__ __launch_bounds__(kNT, 1) void prefill16_kernel(Prefill16Params p)
                         s[hf][i] = -INFINITY;
         }
     };
-    auto unit = [&](int j, f32x16 *s, int u) INL {
-        if (u < 8) {
-            m8[u] = fmaxf(fmaxf(s[0][2 * u], s[0][2 * u + 1]), fmaxf(s[1][2 * u], s[1][2 * u + 1]));
-            pin(m8[u]);
-        } else if (u == 8) {
+    // softmax unit number ic of the schedule (see make_schedule), of block x.j
+    auto run_unit = [&](auto ic, f32x16 *s0, f32x16 *s1) INL {
+        constexpr Unit x = PL::sc.unit[decltype(ic)::value];
+        constexpr int j = x.j;
+        f32x16 *s = j == 0 ? s0 : s1;
+        if constexpr (x.kind == UM) {
+            constexpr int u = x.idx;
+            m8[j][u] = fmaxf(fmaxf(s[0][2 * u], s[0][2 * u + 1]),
+                             fmaxf(s[1][2 * u], s[1][2 * u + 1]));
+            pin(m8[j][u]);
+        } else if constexpr (x.kind == UT1) {
 #pragma unroll
-            for (int w = 4; w >= 1; w >>= 1)
-#pragma unroll
-                for (int i = 0; i < w; ++i)
-                    m8[i] = fmaxf(m8[i], m8[i + w]);
-            const float m2 = pair_max(m8[0]) * a.c;
-            const bool need = m2 > frame[j] + kRescaleMarginLog2;
-            alpha[j] = need ? exp2_fast(frame[j] - m2) : 1.0f;
-            frame[j] = need ? m2 : frame[j];
+            for (int i = 0; i < 4; ++i) {
+                m8[j][i] = fmaxf(m8[j][i], m8[j][i + 4]);
+                pin(m8[j][i]);
+            }
+        } else if constexpr (x.kind == UT2) {
+            m8[j][0] = fmaxf(fmaxf(m8[j][0], m8[j][2]), fmaxf(m8[j][1], m8[j][3]));
+            pin(m8[j][0]);
+        } else if constexpr (x.kind == UP) {
+            mx[j] = pair_max(m8[j][0]);
+            pin(mx[j]);
+        } else if constexpr (x.kind == UF1) {
+            m2[j] = mx[j] * a.c;
+            need[j] = m2[j] > frame[j] + kRescaleMarginLog2;
+            pin(m2[j]);
+        } else if constexpr (x.kind == UF2) {
+            alpha[j] = need[j] ? exp2_fast(frame[j] - m2[j]) : 1.0f;
+            frame[j] = need[j] ? m2[j] : frame[j];
             fr[j] = (frame[j] == -INFINITY) ? 0.0f : frame[j];
             lsum[j] *= alpha[j];
-            rescale[j] = __any(need);
+            rescale[j] = __any(need[j]);
             pin(fr[j]);
+        } else if constexpr (x.kind == UE) {
+            constexpr int t4 = x.idx >> 2, e = x.idx & 3, i = 8 * (t4 & 1) + 2 * e;
+            pv2[j][x.idx][0] = exp2_fast(__builtin_fmaf(s[t4 >> 1][i], a.c, -fr[j]));
+            pv2[j][x.idx][1] = exp2_fast(__builtin_fmaf(s[t4 >> 1][i + 1], a.c, -fr[j]));
+            pin(pv2[j][x.idx][0]);
+            pin(pv2[j][x.idx][1]);
         } else {
-            const int t4 = (u - 9) >> 2, e = (u - 9) & 3;
-            const int i = 8 * (t4 & 1) + 2 * e;
-            const float p0 = exp2_fast(__builtin_fmaf(s[t4 >> 1][i], a.c, -fr[j]));
-            const float p1 = exp2_fast(__builtin_fmaf(s[t4 >> 1][i + 1], a.c, -fr[j]));
-            uint32_t pk = pack2<BF>(p0, p1);
+            constexpr int t4 = x.idx >> 2, e = x.idx & 3;
+            uint32_t pk = pack2<BF>(pv2[j][x.idx][0], pv2[j][x.idx][1]);
             pin(pk);
             pf[j][t4][e] = pk;
             lsum[j] = sum2<BF>(pk, lsum[j]);
@@ -460,39 +584,36 @@ __global__ __launch_bounds__(kNT, 1) void prefill16_kernel(Prefill16Params p)
         smfma_drain(s0[0], s0[1], s1c[0], s1c[1]);
         mask(0, s0, n);
         mask(1, s1c, n);
-        // half 1: P.V of tile n-1 for both blocks | softmax(n) of block 0
+        auto units = [&](auto sc_) INL {          // the softmax units of slot sc_
+            constexpr int sl = decltype(sc_)::value;
+            static_for<PL::sc.first[sl], PL::sc.first[sl + 1]>([&](auto ic) INL {
+                run_unit(ic, s0, s1c);
+            });
+        };
+        // half 1: P.V of tile n-1 for both blocks
         static_for<0, kRead>([&](auto fc) INL { fb[fc.value] = vread(vs, fc.value); });
         static_for<0, NM>([&](auto ic) INL {
             constexpr int i = decltype(ic)::value, f = i >> 1;
             if constexpr ((i & 1) == 0 && f + kRead < 4 * NDT)
                 fb[(f + kRead) % (kRead + 1)] = vread(vs, f + kRead);
             pv_slot(i, fb[f % (kRead + 1)]);
-            static_for<PL::h1.first[i], PL::h1.first[i + 1]>([&](auto uc) INL {
-                unit(0, s0, decltype(uc)::value);
-            });
+            units(ic);
             __builtin_amdgcn_sched_barrier(0);
         });
         apply_rescale(0);
-        // half 2: scores of tile n+1 for both blocks | rest of block 0, softmax(n) of block 1
-        auto unit2 = [&](auto uc) INL {
-            constexpr int u = decltype(uc)::value;
-            if constexpr (u < PL::carry)
-                unit(0, s0, PL::c0 + u);
-            else
-                unit(1, s1c, u - PL::carry);
-        };
+        // half 2: scores of tile n+1 for both blocks
         static_for<0, kRead>([&](auto fc) INL { fb[fc.value] = kread(ks, fc.value); });
         static_for<0, NM>([&](auto ic) INL {
             constexpr int i = decltype(ic)::value, f = i >> 1;
             if constexpr ((i & 1) == 0 && f + kRead < 2 * NST)
                 fb[(f + kRead) % (kRead + 1)] = kread(ks, f + kRead);
             s_slot(i, fb[f % (kRead + 1)], s0, s1n);
-            static_for<PL::h2.first[i], PL::h2.first[i + 1]>(unit2);
+            units(std::integral_constant<int, NM + i>{});
             if constexpr ((i & 3) == 1 && (i >> 2) < 2 * G::NDMA)
                 dma_part(n, i >> 2);
             __builtin_amdgcn_sched_barrier(0);
         });
-        static_for<PL::h2.first[NM], PL::carry + kUnits>(unit2);
+        static_for<PL::sc.first[2 * NM], kNU>([&](auto ic) INL { run_unit(ic, s0, s1c); });
         apply_rescale(1);
     };
 

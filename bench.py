@@ -8,6 +8,9 @@ One step = one pass of the whole path over resident inputs:
 Before each call a 1 GiB buffer is overwritten so that neither call finds its inputs in the
 256 MB last-level cache (the decode working set, 151 MB, would otherwise stay resident).
 
+Warm-up: untimed steps for 0.25 s of wall time (the GPU's clocks settle under load), then the
+W warm-up steps; then K timed steps.
+
 Prints one JSON line. `value` is prefill TFLOP/s (algorithmic FLOPs / mean kernel time from
 HIP events on the launch stream); the decode HBM GB/s figure sits in `decode`. `roofline` is
 for the prefill kernel, `roofline_decode` for the decode pair. `cpu_baseline` times the CPU
@@ -34,6 +37,7 @@ PEAK_HBM_GBS = 8000.0              # MI355X HBM3E, published
 PAGES_PREFILL_16K_TFLOPS = 1.20    # the pages' fixed kernel at 16K keys (Radeon 8060S, gfx1151)
 FLUSH_BYTES = 1 << 30
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_16k_f16_traffic.txt")
+CLOCK_WARMUP_S = 0.25
 
 
 def source_hash() -> str:
@@ -180,6 +184,14 @@ def main():
         if i is not None:
             ev[i][3].record(stream)
 
+    # Warm-up: the GPU's clocks take tens of milliseconds of load to settle, so before the W
+    # counted warm-up steps run untimed steps until CLOCK_WARMUP_S of wall time has passed.
+    t_warm = time.perf_counter()
+    k = 0
+    while time.perf_counter() - t_warm < CLOCK_WARMUP_S:
+        step(None, k)
+        torch.cuda.synchronize()
+        k += 1
     for k in range(args.warmup):
         step(None, k)
     torch.cuda.synchronize()
@@ -224,10 +236,10 @@ def main():
         "decode": {"value": round(gbs, 1), "unit": "GB/s", "ms_mean": round(float(d_ms.mean()), 5),
                    "ms_median": round(float(np.median(d_ms)), 5),
                    "ms_min": round(float(d_ms.min()), 5), "algorithmic_bytes": dbytes,
-                   "kernels": "decode_split_kernel + decode_merge_kernel"},
+                   "kernels": "decode_q4_kernel + decode_merge_kernel"},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 3), "peak": PEAK_MFMA_F16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK_MFMA_F16_TFLOPS, 4),
-                     "traffic": traffic, "kernel": "prefill_kernel<128, f16>",
+                     "traffic": traffic, "kernel": "prefill16_kernel<128, f16>",
                      "algorithmic_flops_per_launch": flops},
         "roofline_decode": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                             "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
