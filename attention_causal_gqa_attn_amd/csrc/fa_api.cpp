@@ -114,8 +114,15 @@ size_t fa_decode_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Sk, int D)
     if (B <= 0 || Hq <= 0 || Hkv <= 0 || Sq <= 0 || Sk < 0 || Hq % Hkv != 0 ||
         (D != 64 && D != 128))
         return 0;
-    // the largest split count any causal offset can produce for these sizes
-    return fa::decode_grid(B, Hq, Hkv, Sq, Sk, D, /*kend=*/Sk, /*bound=*/true).workspace_bytes;
+    // the largest split count any causal offset can produce for these sizes, over the
+    // kernels the cache types select
+    size_t bytes = 0;
+    for (int kv : {FA_KV_F16, FA_KV_Q4_0}) {
+        const size_t nb =
+            fa::decode_grid(B, Hq, Hkv, Sq, Sk, D, /*kend=*/Sk, /*bound=*/true, kv).workspace_bytes;
+        bytes = nb > bytes ? nb : bytes;
+    }
+    return bytes;
 }
 
 int fa_decode(const void *q, const void *k, const void *v, void *o, int B, int Hq, int Hkv,
@@ -132,7 +139,8 @@ int fa_decode(const void *q, const void *k, const void *v, void *o, int B, int H
     if ((int64_t)B * Sq == 0)
         return FA_OK;
     const fa::DecodeGrid g = fa::decode_grid(B, Hq, Hkv, Sq, Sk, D,
-                                             visible_end(Sq, Sk, a.causal, a.offset), false);
+                                             visible_end(Sq, Sk, a.causal, a.offset), false,
+                                             a.kv);
     if (g.n_wg > kMaxWorkgroups)
         return FA_ERR_UNSUPPORTED;
     if (g.workspace_bytes > 0) {

@@ -20,6 +20,10 @@
 
 namespace fa {
 
+// q4_0 decode with at most 4 query rows per KV head and a KV head count divisible by 4 takes
+// the head-group kernel (one workgroup per 4 heads and key range)
+bool q4_grouped(int kv, int rows, int Hkv) { return kv == KV_Q4_0 && rows <= 4 && Hkv % 4 == 0; }
+
 namespace {
 
 struct DecodeParams {
@@ -79,6 +83,39 @@ __device__ __forceinline__ void decode_tile(const uint16_t *lk, const uint16_t *
         acc[dt] = mfma16k16<BF>(*(const u32x2 *)(vr + 16 * dt * Geo::vStride), pf, acc[dt]);
 }
 
+// Combine per-wave softmax states held in LDS and write the split's partial [O, F, L] rows.
+// Wave w's row rr: unnormalised output at o0[w * ows + rr * D + d], frame f0[w * fws + rr],
+// sum l0[w * fws + rr]. A wave that saw no key has frame -inf and contributes nothing.
+template <int D>
+__device__ __forceinline__ void write_partial(const DecodeParams &p, const float *o0, int ows,
+                                              const float *f0, const float *l0, int fws,
+                                              int b, int kvh, int s, int t)
+{
+    const AttnArgs &a = p.a;
+    float *out = p.part + (((int64_t)b * a.Hkv + kvh) * p.n_split + s) * p.rows * (D + 2);
+    for (int e = t; e < p.rows * D; e += kThreads) {
+        const int rr = e / D, d = e % D;
+        float F = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+            F = fmaxf(F, f0[w * fws + rr]);
+        float o = 0.0f, l = 0.0f;
+        if (F != -INFINITY) {
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const float sw = exp2_fast(f0[w * fws + rr] - F);   // 0 for an empty wave
+                o += sw * o0[w * ows + rr * D + d];
+                l += sw * l0[w * fws + rr];
+            }
+        }
+        out[rr * (D + 2) + d] = o;
+        if (d == 0) {
+            out[rr * (D + 2) + D] = F;
+            out[rr * (D + 2) + D + 1] = l;
+        }
+    }
+}
+
 // Combine the 4 waves' softmax states of each row (through LDS at cmb, 4*16*(D+2) floats)
 // and write the split's partial [F, L, O] rows.
 template <int D>
@@ -86,7 +123,6 @@ __device__ __forceinline__ void decode_combine(const DecodeParams &p, float *cmb
                                                int s, int t, int wave, int quad, int r,
                                                const f32x4 *acc, float frame, float lsum)
 {
-    const AttnArgs &a = p.a;
     lsum += __shfl_xor(lsum, 16, 64);
     lsum = pair_sum(lsum);
     float *cmb_o = cmb;                             // [4 waves][16 rows][D]
@@ -102,29 +138,7 @@ __device__ __forceinline__ void decode_combine(const DecodeParams &p, float *cmb
         cmb_l[wave * 16 + r] = lsum;
     }
     __syncthreads();
-
-    float *out = p.part + (((int64_t)b * a.Hkv + kvh) * p.n_split + s) * p.rows * (D + 2);
-    for (int e = t; e < p.rows * D; e += kThreads) {
-        const int rr = e / D, d = e % D;
-        float F = -INFINITY;
-#pragma unroll
-        for (int w = 0; w < 4; ++w)
-            F = fmaxf(F, cmb_f[w * 16 + rr]);
-        float o = 0.0f, l = 0.0f;
-        if (F != -INFINITY) {
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                const float sw = exp2_fast(cmb_f[w * 16 + rr] - F);   // 0 for an empty wave
-                o += sw * cmb_o[(w * 16 + rr) * D + d];
-                l += sw * cmb_l[w * 16 + rr];
-            }
-        }
-        out[rr * (D + 2) + d] = o;
-        if (d == 0) {
-            out[rr * (D + 2) + D] = F;
-            out[rr * (D + 2) + D + 1] = l;
-        }
-    }
+    write_partial<D>(p, cmb_o, 16 * D, cmb_f, cmb_l, 16, b, kvh, s, t);
 }
 
 // Tiles whose global loads are in flight at once per workgroup: decode has little work per
@@ -384,6 +398,577 @@ __global__ __launch_bounds__(kThreads, 2) void decode_q4_kernel(DecodeParams p)
     decode_combine<D>(p, (float *)lds, b, kvh, s, t, wave, quad, r, acc, frame, lsum);
 }
 
+// ---- q4_0 caches, at most 4 query rows per KV head --------------------------------------------
+// v_mfma_f32_4x4x4_16b_f16 computes 16 independent 4x4 products with K = 4: lane i + 4*blk
+// holds row i of block blk's A (its 4 k values), column i of its B, and column i of its D
+// (register r = row r). The 4 columns are the query rows of a KV head, so no score, exp or
+// output element is padding. One wave carries one KV head's attention over whole tiles.
+//
+// The codes are never dequantized element by element. An f16 bit pattern with only low
+// mantissa bits set is the subnormal n * 2^-24, exact, and the MFMA multiplies subnormal f16
+// inputs exactly, so a code byte masked in place with 0x0F is its low nibble n * 2^-24 and
+// masked with 0xF0 its high nibble times 16 * 2^-24. The block scale d and the offset 8 are
+// applied outside the per-element path:
+//   scores:  s = sum_b D_b * (2^-24 sum_{e in b} n_e q_e - 2^-21 sum_{e in b} q_e), D_b = 2^24 d_b
+//            (one accumulator per block b, started at the q term; high nibbles meet q / 16);
+//   output:  o_e = sum_k P_k d_b(k) (n_ke - 8) = 2^24 sum_k P'_k n_ke 2^-24 - 8 sum_k P'_k with
+//            P'_k = P_k d_b(k) (f16) as the B operand and the sum of P' kept beside O.
+constexpr int kQ4Rows = 4;
+
+__device__ __forceinline__ f32x4 mfma4(uint32_t a0, uint32_t a1, u32x2 b, f32x4 c)
+{
+    return __builtin_amdgcn_mfma_f32_4x4x4f16(__builtin_bit_cast(f16x4, (u32x2){a0, a1}),
+                                              __builtin_bit_cast(f16x4, b), c, 0, 0, 0);
+}
+
+// x of lane (l & ~3) + I: DPP quad broadcast
+template <int I>
+__device__ __forceinline__ float quad_bcast(float x)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x),
+                                                              I * 0x55, 0xF, 0xF, false));
+}
+// max over lanes {l, l ^ 4, l ^ 8, l ^ 12} (one 16-lane row, same l % 4): DPP row rotates
+__device__ __forceinline__ float row4_max(float x)
+{
+    x = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x),
+                                                                    0x124, 0xF, 0xF, false)));
+    x = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x),
+                                                                    0x128, 0xF, 0xF, false)));
+    return x;
+}
+// max over the 16-lane row pair {row, row ^ 1}: v_permlane16_swap on two copies (as in
+// lane_halves for the 32-lane halves)
+__device__ __forceinline__ float rowpair_max(float x)
+{
+    float a = x, b = x;
+    asm("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+    return fmaxf(a, b);
+}
+
+// Wait until at most N vector-memory operations of this wave are outstanding; also a compiler
+// memory fence, so no LDS read of the landed data moves above it.
+template <int N>
+__device__ __forceinline__ void wait_vm()
+{
+    asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
+}
+
+// One wave's attention of the <= 4 query rows of one KV head over q4_0 tiles in LDS whose key
+// rows (the head's D/32 blocks of 18 bytes) are RS bytes apart.
+template <int D, int RS>
+struct Q4Head {
+    static constexpr int NB = D / 32;               // q4_0 blocks per key row
+    static constexpr int ROWB = 18 * NB;            // bytes of the head's key row
+    static constexpr int ROWDW = ROWB / 4;
+    static constexpr int KGC = 16 / NB;             // 4-key groups per P.V chunk
+    static constexpr int NCH = kBN / (4 * KGC);     // P.V chunks per tile
+
+    int lane, j, bq, kg;
+    int64_t rowlim, lim0;
+    uint32_t vlo, vhi, vsh, vsc;
+    int psrc;
+    u32x2 qlo[NB][4], qhi[NB][4];
+    f32x4 sinit[NB];
+    f32x4 oacc[8];                                  // P.V, MFMA q + 4 hh: byte q, nibble hh
+    float frame, lsum, csum;
+
+    // Query rows j = lane % 4 (qi * G + hl; rows >= p.rows are padding, computed and never
+    // written) of KV head kvh of batch b, over keys below ke.
+    __device__ __forceinline__ void init(const DecodeParams &p, int b, int kvh, int64_t ke,
+                                         int lane_)
+    {
+        const AttnArgs &a = p.a;
+        lane = lane_;
+        j = lane & 3;
+        const bool row_on = j < p.rows;
+        const int qi = row_on ? j / a.G : 0;
+        const int hl = row_on ? j % a.G : 0;
+        const int h = kvh * a.G + hl;
+        rowlim = ke - 1;
+        if (a.causal)
+            rowlim = min(rowlim, (int64_t)qi + a.offset);
+        if (!row_on)
+            rowlim = -1;
+        lim0 = ke - 1;                              // smallest limit of a real row (row 0)
+        if (a.causal)
+            lim0 = min(lim0, a.offset);
+
+        // B operands of the score MFMAs: row j of q in the k order of the A operands. Code
+        // dword pp of block bb holds bytes 4 pp .. 4 pp + 3; masked as in scores() its slots
+        // are elements 32 bb + 4 pp + {0, 2, 1, 3} (low nibbles) and 16 more (high nibbles).
+        const uint16_t *qp = (const uint16_t *)a.q + (((int64_t)b * a.Sq + qi) * a.Hq + h) * D;
+        u32x4 qv[NB][4];
+#pragma unroll
+        for (int bb = 0; bb < NB; ++bb)
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                qv[bb][u] = row_on ? *(const u32x4 *)(qp + 32 * bb + 8 * u) : (u32x4){};
+#pragma unroll
+        for (int bb = 0; bb < NB; ++bb)
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                settle(qv[bb][u]);
+        const f16x2 sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
+#pragma unroll
+        for (int bb = 0; bb < NB; ++bb) {
+            float qs = 0.0f;
+#pragma unroll
+            for (int pp = 0; pp < 4; ++pp) {
+                // element pairs (e, e + 1): the low half of the block in qv[bb][0..1], the
+                // high half in qv[bb][2..3]
+                const uint32_t l0 = qv[bb][pp / 2][2 * (pp % 2)];
+                const uint32_t l1 = qv[bb][pp / 2][2 * (pp % 2) + 1];
+                const uint32_t h0 = qv[bb][2 + pp / 2][2 * (pp % 2)];
+                const uint32_t h1 = qv[bb][2 + pp / 2][2 * (pp % 2) + 1];
+                qlo[bb][pp] = (u32x2){perm(l1, l0, 0x05040100u), perm(l1, l0, 0x07060302u)};
+                const uint32_t x0 = perm(h1, h0, 0x05040100u), x1 = perm(h1, h0, 0x07060302u);
+                qhi[bb][pp] = (u32x2){
+                    __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, x0) * sixteenth),
+                    __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, x1) * sixteenth)};
+                const f32x2 a0 = unpack2<false>(l0), a1 = unpack2<false>(l1);
+                const f32x2 c0 = unpack2<false>(h0), c1 = unpack2<false>(h1);
+                qs += (a0[0] + a0[1]) + (a1[0] + a1[1]) + (c0[0] + c0[1]) + (c1[0] + c1[1]);
+            }
+            const float q8 = -0x1p-21f * qs;
+            sinit[bb] = (f32x4){q8, q8, q8, q8};
+        }
+
+        // P.V roles: A row pp = lane % 4 (code dword pp of block bq of the 4 keys of group kg),
+        // B / D column j = lane % 4, block bq * KGC + kg = lane / 4. Even blocks start 2 bytes
+        // into a dword: their code dword is spliced from two.
+        bq = (lane >> 2) / KGC;
+        kg = (lane >> 2) % KGC;
+        const int pp = lane & 3;
+        vlo = (uint32_t)(RS * 4 * kg + 18 * bq + 4 * pp + ((bq & 1) ? 2 : 0));
+        vhi = vlo + ((bq & 1) ? 0u : 4u);
+        vsh = (bq & 1) ? 0u : 16u;
+        vsc = (uint32_t)(RS * 4 * kg + 18 * bq);                // scale of block bq
+        psrc = (lane & (4 * KGC - 1)) * 4;                       // + 16 KGC c for chunk c
+
+#pragma unroll
+        for (int m = 0; m < 8; ++m)
+            oacc[m] = (f32x4){};
+        frame = -INFINITY;
+        lsum = 0.0f;
+        csum = 0.0f;
+    }
+
+    // Scores of the tile's 64 keys (from key k0; kt = the head's key row 0 in LDS) and the
+    // softmax state update; returns P as two packed f16 pairs (keys 4 blk + 0..3 of row j).
+    // Lane l supplies key l's K row as A; D lane j + 4 blk, register r is key 4 blk + r.
+    __device__ __forceinline__ u32x2 scores(const uint8_t *kt, int64_t k0, float c)
+    {
+        uint32_t w[ROWDW];
+        const uint8_t *kr = kt + RS * lane;
+        if constexpr (ROWB % 8 == 0) {
+#pragma unroll
+            for (int u = 0; u < ROWDW / 2; ++u) {
+                const u32x2 x = *(const u32x2 *)(kr + 8 * u);
+                w[2 * u] = x[0];
+                w[2 * u + 1] = x[1];
+            }
+        } else {
+#pragma unroll
+            for (int u = 0; u < ROWDW; ++u)
+                w[u] = *(const uint32_t *)(kr + 4 * u);
+        }
+        f32x4 sacc[NB];
+        float dsc[NB];
+#pragma unroll
+        for (int bb = 0; bb < NB; ++bb) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                uint32_t cw;
+                if (bb % 2 == 0)
+                    cw = __builtin_amdgcn_alignbit(w[9 * bb / 2 + q + 1], w[9 * bb / 2 + q], 16);
+                else
+                    cw = w[(18 * bb + 2) / 4 + q];
+                const uint32_t y = cw >> 8;
+                sacc[bb] = mfma4(cw & 0x000F000Fu, y & 0x000F000Fu, qlo[bb][q],
+                                 q == 0 ? sinit[bb] : sacc[bb]);
+                sacc[bb] = mfma4(cw & 0x00F000F0u, y & 0x00F000F0u, qhi[bb][q], sacc[bb]);
+            }
+            const uint32_t dbits = (bb % 2 == 0) ? (w[9 * bb / 2] & 0xFFFFu)
+                                                 : (w[(18 * bb - 2) / 4] >> 16);
+            dsc[bb] = (float)__builtin_bit_cast(_Float16, (uint16_t)dbits) * 0x1p24f;
+        }
+        float sc[4];
+        {
+            float d0[NB], d1[NB], d2[NB], d3[NB];
+#pragma unroll
+            for (int bb = 0; bb < NB; ++bb) {
+                d0[bb] = quad_bcast<0>(dsc[bb]);
+                d1[bb] = quad_bcast<1>(dsc[bb]);
+                d2[bb] = quad_bcast<2>(dsc[bb]);
+                d3[bb] = quad_bcast<3>(dsc[bb]);
+            }
+            sc[0] = d0[0] * sacc[0][0];
+            sc[1] = d1[0] * sacc[0][1];
+            sc[2] = d2[0] * sacc[0][2];
+            sc[3] = d3[0] * sacc[0][3];
+#pragma unroll
+            for (int bb = 1; bb < NB; ++bb) {
+                sc[0] = __builtin_fmaf(d0[bb], sacc[bb][0], sc[0]);
+                sc[1] = __builtin_fmaf(d1[bb], sacc[bb][1], sc[1]);
+                sc[2] = __builtin_fmaf(d2[bb], sacc[bb][2], sc[2]);
+                sc[3] = __builtin_fmaf(d3[bb], sacc[bb][3], sc[3]);
+            }
+        }
+        if (k0 + kBN - 1 > lim0) {                  // wave-uniform: a row limit falls here
+            const int64_t key = k0 + 4 * (lane >> 2);
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                if (key + r > rowlim)
+                    sc[r] = -INFINITY;
+        }
+
+        // softmax state of row j (deferred rescale)
+        float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+        mx = row4_max(mx);
+        mx = rowpair_max(mx);
+        mx = pair_max(mx);
+        const float m2 = mx * c;
+        const bool need = m2 > frame + kRescaleMarginLog2;
+        if (__any(need)) {
+            const float alpha = need ? exp2_fast(frame - m2) : 1.0f;
+#pragma unroll
+            for (int m = 0; m < 8; ++m)
+                oacc[m] *= alpha;
+            lsum *= alpha;
+            csum *= alpha;
+            frame = need ? m2 : frame;
+        }
+        const float fr = (frame == -INFINITY) ? 0.0f : frame;
+        const uint32_t pk0 = pack2<false>(exp2_fast(__builtin_fmaf(sc[0], c, -fr)),
+                                          exp2_fast(__builtin_fmaf(sc[1], c, -fr)));
+        const uint32_t pk1 = pack2<false>(exp2_fast(__builtin_fmaf(sc[2], c, -fr)),
+                                          exp2_fast(__builtin_fmaf(sc[3], c, -fr)));
+        lsum = sum2<false>(pk1, sum2<false>(pk0, lsum));
+        return (u32x2){pk0, pk1};
+    }
+
+    // O += P V over the tile (vt = the head's V row 0 in LDS).
+    __device__ __forceinline__ void pv(const uint8_t *vt, u32x2 pk)
+    {
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+            // P of keys 4 (KGC c + kg) + 0..3, row j, from the score lane j + 4 kg + 16 KGC c
+            const int src = psrc + 16 * KGC * c;
+            const uint32_t b0 = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)pk[0]);
+            const uint32_t b1 = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)pk[1]);
+            const uint8_t *vr = vt + RS * 4 * KGC * c;
+            uint32_t cw[4];
+            uint16_t dq[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const uint32_t lo = *(const uint32_t *)(vr + RS * k + vlo);
+                const uint32_t hi = *(const uint32_t *)(vr + RS * k + vhi);
+                cw[k] = __builtin_amdgcn_alignbit(hi, lo, vsh);
+                dq[k] = *(const uint16_t *)(vr + RS * k + vsc);
+            }
+            const f16x2 s01 = __builtin_bit_cast(f16x2, (uint32_t)dq[0] | ((uint32_t)dq[1] << 16));
+            const f16x2 s23 = __builtin_bit_cast(f16x2, (uint32_t)dq[2] | ((uint32_t)dq[3] << 16));
+            const uint32_t p01 = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, b0) * s01);
+            const uint32_t p23 = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, b1) * s23);
+            csum = sum2<false>(p23, sum2<false>(p01, csum));
+            const u32x2 pb = {p01, p23};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const uint32_t sel = 0x0C000C00u | ((4u + q) << 16) | (uint32_t)q;
+                const uint32_t u01 = perm(cw[1], cw[0], sel), u23 = perm(cw[3], cw[2], sel);
+                oacc[q] = mfma4(u01 & 0x000F000Fu, u23 & 0x000F000Fu, pb, oacc[q]);
+                oacc[q + 4] = mfma4(u01 & 0x00F000F0u, u23 & 0x00F000F0u, pb, oacc[q + 4]);
+            }
+        }
+    }
+
+    // Reduce over the key-group lanes. Afterwards lanes with kg == 0 hold the unnormalised
+    // output of row j for block bq: o(r, q, hh) is element 32 bq + 4 r + q + 16 hh; every lane
+    // holds row j's frame and sum.
+    __device__ __forceinline__ void reduce()
+    {
+#pragma unroll
+        for (int sh = 4; sh < 4 * KGC; sh *= 2) {
+#pragma unroll
+            for (int m = 0; m < 8; ++m)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    oacc[m][r] += __shfl_xor(oacc[m][r], sh, 64);
+            csum += __shfl_xor(csum, sh, 64);
+        }
+#pragma unroll
+        for (int sh = 4; sh < 64; sh *= 2)
+            lsum += __shfl_xor(lsum, sh, 64);
+    }
+    __device__ __forceinline__ float out(int r, int q, int hh) const
+    {
+        return (hh ? 0x1p20f : 0x1p24f) * oacc[q + 4 * hh][r] - 8.0f * csum;
+    }
+};
+
+// One dword LDS-DMA transfer per lane: gbase + voff -> LDS lds_base + 4 * lane.
+__device__ __forceinline__ void dma4(const uint8_t *gbase, uint32_t voff, uint32_t lds_base)
+{
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
+                 :: "v"(voff), "s"(gbase), "s"(lds_base) : "memory");
+}
+// One 16-byte LDS-DMA transfer per lane: gbase + voff -> LDS lds_base + 16 * lane.
+__device__ __forceinline__ void dma16x(const uint8_t *gbase, uint32_t voff, uint32_t lds_base)
+{
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :: "v"(voff), "s"(gbase), "s"(lds_base) : "memory");
+}
+
+// (a) Head groups: a workgroup takes 4 adjacent KV heads (one per wave) over one key range. A
+// key's rows of the 4 heads are contiguous in memory (4 * 18 D/32 bytes, a multiple of 16), so
+// the waves together move whole 16-byte chunks with LDS-DMA: tile rows of S 16-byte slots (S
+// odd, the last a repeat when the data is an even number of chunks), so the 16-byte K row
+// reads of 16 consecutive keys fall into distinct LDS banks. NSTG stages; one barrier a tile.
+template <int D>
+struct Q4G {
+    static constexpr int NH = 4;                    // KV heads per workgroup, one per wave
+    static constexpr int ROWB = 18 * (D / 32);
+    static constexpr int GB = NH * ROWB;            // bytes of the group's key row
+    static constexpr int DS = GB / 16;              // its 16-byte chunks
+    static constexpr int S = DS | 1;                // LDS slots per key row
+    static constexpr int RS = 16 * S;
+    static constexpr int TB = kBN * RS;             // one tensor's tile in LDS
+    static constexpr int NI = 2 * S;                // wave-wide transfers per tile (K, then V)
+    static constexpr int NIW = (NI + 3) / 4;        // per wave (surplus ones repeat the last)
+    static constexpr int STAGE = 2 * TB;
+    static constexpr int NSTG = 2;
+    static_assert(GB % 16 == 0, "group rows are whole 16-byte chunks");
+};
+
+template <int D>
+__global__ __launch_bounds__(kThreads, 2) void decode_q4g_kernel(DecodeParams p)
+{
+    using G = Q4G<D>;
+    using H = Q4Head<D, G::RS>;
+    constexpr int NSTG = G::NSTG, NIW = G::NIW, S = G::S;
+    __shared__ __attribute__((aligned(16))) uint8_t lds[NSTG * G::STAGE];
+
+    const AttnArgs &a = p.a;
+    const int t = threadIdx.x, lane = t & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+
+    // head group fastest: the groups of one key range go to one XCD together and share its
+    // L2 lines (a key's rows of all KV heads are contiguous)
+    const int ngrp = a.Hkv / G::NH;
+    int rest = xcd_remap(blockIdx.x, gridDim.x);
+    const int grp = rest % ngrp;
+    rest /= ngrp;
+    const int s = rest % p.n_split;
+    const int b = rest / p.n_split;
+    const int kvh = grp * G::NH + wave;
+
+    const int64_t ks = (int64_t)s * p.split_len;
+    const int64_t ke = min(ks + p.split_len, p.kend);
+    const int nb = ke > ks ? (int)((ke - ks + kBN - 1) / kBN) : 0;
+
+    H hd;
+    hd.init(p, b, kvh, ke, lane);
+
+    // transfers: this wave's m-th of a tile is i = min(wave + 4 m, NI - 1); i < S moves K slot
+    // column i (slots 64 i .. 64 i + 63 of the tile), else V column i - S
+    const uint32_t grow = (uint32_t)a.Hkv * G::ROWB;                    // bytes between keys
+    const int64_t g0 = ((int64_t)b * a.Sk * a.Hkv + grp * G::NH) * G::ROWB;
+    const uint8_t *kgl = (const uint8_t *)a.k + g0, *vgl = (const uint8_t *)a.v + g0;
+    const uint32_t lds0 = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t *)lds);
+    uint32_t crow[NIW], ccol[NIW];
+#pragma unroll
+    for (int m = 0; m < NIW; ++m) {
+        const int i = min(wave + 4 * m, G::NI - 1);
+        const int sl = (i % S) * 64 + lane;
+        crow[m] = (uint32_t)(sl / S);
+        ccol[m] = 16u * (uint32_t)min(sl % S, G::DS - 1);
+    }
+    auto dma_tile = [&](int kb) {
+        const int64_t k0 = ks + (int64_t)kb * kBN;
+        const uint32_t last = (uint32_t)min((int64_t)kBN - 1, (int64_t)a.Sk - 1 - k0);
+        const uint32_t st = lds0 + (uint32_t)((kb % NSTG) * G::STAGE);
+#pragma unroll
+        for (int m = 0; m < NIW; ++m) {
+            const int i = min(wave + 4 * m, G::NI - 1);
+            const bool is_v = i >= S;
+            dma16x((is_v ? vgl : kgl) + k0 * grow, min(crow[m], last) * grow + ccol[m],
+                   __builtin_amdgcn_readfirstlane(st + (uint32_t)((is_v ? G::TB : 0) +
+                                                                  (i % S) * 1024)));
+        }
+    };
+
+#pragma unroll
+    for (int u = 0; u < NSTG - 1; ++u)
+        if (u < nb)
+            dma_tile(u);
+    for (int kb = 0; kb < nb; ++kb) {
+        // tile kb landed for every wave; every wave is done with tile kb - 1, whose stage the
+        // next transfer refills
+        if constexpr (NSTG == 3) {
+            if (kb + 1 < nb)
+                wait_vm<NIW>();
+            else
+                wait_vm<0>();
+        } else {
+            wait_vm<0>();
+        }
+        asm volatile("s_barrier" ::: "memory");
+        if (kb + NSTG - 1 < nb)
+            dma_tile(kb + NSTG - 1);
+        const uint8_t *kt = lds + (kb % NSTG) * G::STAGE + wave * G::ROWB;
+        const u32x2 pk = hd.scores(kt, ks + (int64_t)kb * kBN, a.c);
+        hd.pv(kt + G::TB, pk);
+    }
+
+    // this wave's head: write the split's partial rows directly
+    hd.reduce();
+    if (hd.kg == 0 && hd.j < p.rows) {
+        float *out = p.part + ((((int64_t)b * a.Hkv + kvh) * p.n_split + s) * p.rows + hd.j) *
+                                  (D + 2);
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    out[32 * hd.bq + 16 * hh + 4 * r + q] = hd.out(r, q, hh);
+        if (hd.bq == 0) {
+            out[D] = hd.frame;
+            out[D + 1] = hd.lsum;
+        }
+    }
+}
+
+// (b) Any KV head count: each wave owns every 4th tile of the workgroup's key range of one
+// head (kb = wave, wave + 4, ...) and two raw LDS stages of its own, filled by dword LDS-DMA
+// (the tile's 64 K rows, then its 64 V rows, densely packed); nothing in the loop waits for
+// another wave, and the 4 waves' states are combined through LDS at the end.
+template <int D>
+struct Q4W {
+    static constexpr int ROWB = 18 * (D / 32);      // bytes per key row
+    static constexpr int ROWDW = ROWB / 4;
+    static constexpr int TILEB = kBN * ROWB;        // one tensor's raw tile
+    static constexpr int NX = TILEB / 256;          // dword LDS-DMA transfers per tensor tile
+    static constexpr int NV = NX < 9 ? NX : 9;      // distinct lane offsets among them
+    static constexpr int RSTEP = 64 * NV / ROWDW;   // key rows spanned by NV transfers
+    static constexpr int STAGE = 2 * TILEB;         // K rows then V rows
+    static constexpr int WAVE_LDS = 2 * STAGE;      // two stages per wave
+    static_assert((64 * NV) % ROWDW == 0, "offset reuse");
+    static_assert(4 * D + 8 <= WAVE_LDS / 4, "combine scratch fits in a wave's stages");
+};
+
+template <int D>
+__global__ __launch_bounds__(kThreads, 2) void decode_q4w_kernel(DecodeParams p)
+{
+    using W = Q4W<D>;
+    using H = Q4Head<D, W::ROWB>;
+    constexpr int ROWDW = W::ROWDW, TILEB = W::TILEB, NX = W::NX, NV = W::NV;
+    __shared__ __attribute__((aligned(16))) uint8_t lds[4 * W::WAVE_LDS];
+
+    const AttnArgs &a = p.a;
+    const int t = threadIdx.x, lane = t & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+
+    int rest = xcd_remap(blockIdx.x, gridDim.x);
+    const int kvh = rest % a.Hkv;
+    rest /= a.Hkv;
+    const int s = rest % p.n_split;
+    const int b = rest / p.n_split;
+
+    const int64_t ks = (int64_t)s * p.split_len;
+    const int64_t ke = min(ks + p.split_len, p.kend);
+    const int nb = ke > ks ? (int)((ke - ks + kBN - 1) / kBN) : 0;
+    const int ni = nb > wave ? (nb - wave + 3) / 4 : 0;      // tiles wave + 4 i, i < ni
+
+    H hd;
+    hd.init(p, b, kvh, ke, lane);
+
+    // transfers: lane offsets of the first NV dword transfers of a tensor tile
+    const uint32_t grow = (uint32_t)a.Hkv * W::ROWB;                    // bytes between keys
+    const int64_t head0 = ((int64_t)b * a.Sk * a.Hkv + kvh) * W::ROWB;
+    const uint8_t *kgl = (const uint8_t *)a.k + head0, *vgl = (const uint8_t *)a.v + head0;
+    uint8_t *wl = lds + wave * W::WAVE_LDS;
+    const uint32_t wl0 = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t *)wl);
+    uint32_t vo[NV];
+#pragma unroll
+    for (int m = 0; m < NV; ++m) {
+        const int e = 64 * m + lane;
+        vo[m] = (uint32_t)(e / ROWDW) * grow + 4u * (uint32_t)(e % ROWDW);
+    }
+    auto dma_tile = [&](int i) {
+        const int64_t k0 = ks + (int64_t)(wave + 4 * i) * kBN;
+        const uint32_t st = wl0 + (uint32_t)((i & 1) * W::STAGE);
+        const int64_t last = min((int64_t)kBN - 1, (int64_t)a.Sk - 1 - k0);
+        if (last == kBN - 1) {
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                for (int x = 0; x < NX; ++x)
+                    dma4((tt ? vgl : kgl) + (k0 + (int64_t)(x / NV) * W::RSTEP) * grow,
+                         vo[x % NV], st + (uint32_t)(tt * TILEB + 256 * x));
+        } else {
+            // the sequence's last, partial tile: rows past its last key re-read that key (a
+            // rolled loop, so the compiler cannot merge it into the common path with selects)
+#pragma unroll 1
+            for (int tt = 0; tt < 2; ++tt)
+#pragma unroll 1
+                for (int x = 0; x < NX; ++x) {
+                    const int e = 64 * x + lane;
+                    const uint32_t row = (uint32_t)min(e / ROWDW, (int)last);
+                    dma4((tt ? vgl : kgl) + k0 * grow, row * grow + 4u * (uint32_t)(e % ROWDW),
+                         st + (uint32_t)(tt * TILEB + 256 * x));
+                }
+        }
+    };
+
+    if (ni > 0)
+        dma_tile(0);
+    if (ni > 1)
+        dma_tile(1);
+    for (int i = 0; i < ni; ++i) {
+        const bool more = i + 1 < ni;
+        const uint8_t *sk = wl + (i & 1) * W::STAGE;
+        // K rows of tile i have landed (its V rows and tile i + 1 may still be in flight)
+        if (more)
+            wait_vm<3 * NX>();
+        else
+            wait_vm<NX>();
+        const u32x2 pk = hd.scores(sk, ks + (int64_t)(wave + 4 * i) * kBN, a.c);
+        // V rows of tile i have landed
+        if (more)
+            wait_vm<2 * NX>();
+        else
+            wait_vm<0>();
+        hd.pv(sk + TILEB, pk);
+        if (i + 2 < ni)
+            dma_tile(i + 2);
+    }
+
+    // this wave's state -> LDS (its own stage area; all its transfers have landed)
+    hd.reduce();
+    float *fo = (float *)wl;                        // [4 rows][D], then f[4], l[4]
+    if (hd.kg == 0) {
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    fo[hd.j * D + 32 * hd.bq + 16 * hh + 4 * r + q] = hd.out(r, q, hh);
+        if (hd.bq == 0) {
+            fo[4 * D + hd.j] = hd.frame;
+            fo[4 * D + 4 + hd.j] = hd.lsum;
+        }
+    }
+    __syncthreads();
+    const float *f0 = (const float *)lds;
+    write_partial<D>(p, f0, W::WAVE_LDS / 4, f0 + 4 * D, f0 + 4 * D + 4, W::WAVE_LDS / 4, b,
+                     kvh, s, t);
+}
+
 // One wave per (b, KV head, row): log-sum-exp merge of the row's n_split partials.
 template <int D, bool BF>
 __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeParams p)
@@ -433,9 +1018,17 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeParams p)
 template <int D, int KV>
 hipError_t launch(const DecodeParams &p, int64_t n_wg, hipStream_t stream)
 {
-    if constexpr (KV == KV_Q4_0)
-        hipLaunchKernelGGL((decode_q4_kernel<D>), dim3((unsigned)n_wg), dim3(kThreads), 0,
-                           stream, p);
+    if constexpr (KV == KV_Q4_0) {
+        if (q4_grouped(p.a.kv, p.rows, p.a.Hkv))
+            hipLaunchKernelGGL((decode_q4g_kernel<D>), dim3((unsigned)n_wg), dim3(kThreads), 0,
+                               stream, p);
+        else if (p.rows <= kQ4Rows)
+            hipLaunchKernelGGL((decode_q4w_kernel<D>), dim3((unsigned)n_wg), dim3(kThreads), 0,
+                               stream, p);
+        else
+            hipLaunchKernelGGL((decode_q4_kernel<D>), dim3((unsigned)n_wg), dim3(kThreads), 0,
+                               stream, p);
+    }
     else
         hipLaunchKernelGGL((decode_split_kernel<D, KV>), dim3((unsigned)n_wg), dim3(kThreads), 0,
                            stream, p);
@@ -454,12 +1047,15 @@ hipError_t launch(const DecodeParams &p, int64_t n_wg, hipStream_t stream)
 // 64-key tiles and at least one tile.
 constexpr int64_t kTargetWorkgroups = 512;
 
-DecodeGrid decode_grid(int B, int Hq, int Hkv, int Sq, int Sk, int D, int64_t kend, bool bound)
+DecodeGrid decode_grid(int B, int Hq, int Hkv, int Sq, int Sk, int D, int64_t kend, bool bound,
+                       int kv)
 {
     DecodeGrid g;
     g.rows = (Hq / Hkv) * Sq;
     const int64_t heads = (int64_t)B * Hkv;
-    int64_t want = heads > 0 ? (kTargetWorkgroups + heads - 1) / heads : 1;
+    // workgroups per key range: one per KV head, or one per group of 4 heads
+    const int64_t per = q4_grouped(kv, g.rows, Hkv) ? heads / 4 : heads;
+    int64_t want = per > 0 ? (kTargetWorkgroups + per - 1) / per : 1;
     if (want > 1024)
         want = 1024;     // the merge kernel keeps one weight per split in LDS
     const int64_t tiles = (kend + kBN - 1) / kBN;
@@ -470,7 +1066,7 @@ DecodeGrid decode_grid(int B, int Hq, int Hkv, int Sq, int Sk, int D, int64_t ke
         const int64_t all_tiles = ((int64_t)Sk + kBN - 1) / kBN;
         g.n_split = (int)(all_tiles < want ? (all_tiles > 0 ? all_tiles : 1) : want);
     }
-    g.n_wg = heads * g.n_split;
+    g.n_wg = per * g.n_split;
     g.workspace_bytes = (size_t)heads * g.n_split * g.rows * (D + 2) * sizeof(float);
     return g;
 }

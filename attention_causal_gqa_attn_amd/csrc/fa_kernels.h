@@ -39,8 +39,11 @@ struct DecodeGrid {
     size_t workspace_bytes;
 };
 // kend: keys any row can see, [0, kend). With bound = true the result's workspace_bytes is
-// the largest any kend <= Sk can need (the split count is not monotone in kend).
-DecodeGrid decode_grid(int B, int Hq, int Hkv, int Sq, int Sk, int D, int64_t kend, bool bound);
+// the largest any kend <= Sk can need (the split count is not monotone in kend). kv picks the
+// kernel, which sets how many workgroups share a key range.
+DecodeGrid decode_grid(int B, int Hq, int Hkv, int Sq, int Sk, int D, int64_t kend, bool bound,
+                       int kv);
+bool q4_grouped(int kv, int rows, int Hkv);
 hipError_t launch_decode(const AttnArgs &a, const DecodeGrid &g, void *workspace,
                          hipStream_t stream);
 

@@ -175,9 +175,17 @@ struct TileLoader<D, KV_Q4_0, NT> {
         tensor = t / D;                         // 0: K, 1: V, >= 2: idle
         const int u = t % D;
         kp = u % 32;
-        blk = u / 32;
+        if constexpr (D == 128) {
+            // a wave takes the even blocks {0, 2} or the odd blocks {1, 3} of its tensor, so
+            // the block's alignment (blocks start at byte 0 or 2 of a dword) is wave-uniform
+            const int wi = __builtin_amdgcn_readfirstlane(t >> 6) & 1;
+            blk = 2 * ((u >> 5) & 1) + wi;
+            mis = 2 * wi;
+        } else {
+            blk = u / 32;
+            mis = (18 * blk) & 3;
+        }
         const int boff = 18 * blk;
-        mis = boff & 3;
         base = (const uint8_t *)(tensor ? v : k) + head_off_rows * ROWB;
         row = (uint32_t)(row_rows * ROWB);
         Sk = Sk_;

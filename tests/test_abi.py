@@ -115,9 +115,11 @@ def test_decode_rejects(kw, code):
 
 def test_decode_workspace_bound():
     n = fa.fa_decode_workspace_bytes(4, 32, 8, 1, 32768, 128)
-    # about 512 splits in all (16 per (b, KV head) here), each split a row of 4 heads x
-    # (128 outputs + frame + sum) f32
-    assert n == 4 * 8 * 16 * 4 * 130 * 4
+    # about 512 workgroups in all: for a q4_0 cache one per 4 KV heads and key range, so 64
+    # splits per (b, KV head) here (16 for the 16-bit caches); each split a row of 4 query
+    # heads x (128 outputs + frame + sum) f32, and the bound covers every cache type
+    assert n == 4 * 8 * 64 * 4 * 130 * 4
+    assert fa.fa_decode_workspace_bytes(4, 32, 4, 1, 32768, 128) == 4 * 4 * 32 * 8 * 130 * 4
     assert fa.fa_decode_workspace_bytes(4, 32, 8, 1, 0, 128) == 4 * 8 * 1 * 4 * 130 * 4
     assert fa.fa_decode_workspace_bytes(0, 32, 8, 1, 100, 128) == 0
     assert fa.fa_decode_workspace_bytes(1, 32, 8, 1, 100, 96) == 0

@@ -143,6 +143,14 @@ DECODE = [
     wl("decode_negative_offset", 1, 4, 1, 4, 100, 128, "f16", True, -2, seed=46),
     wl("decode_mha_d64", 2, 8, 8, 16, 300, 64, "f16", True, 284, seed=47),
     wl("decode_one_key", 1, 8, 2, 1, 1, 128, "q4_0", True, 0, seed=48),
+    # q4_0 with at most 4 query rows per KV head (the 4-column MFMA path): fewer rows than
+    # columns, two query tokens, D = 64, one KV head per query head, empty waves, no keys
+    wl("decode_q4_0_g2", 2, 16, 8, 1, 1000, 128, "q4_0", True, 999, seed=50),
+    wl("decode_q4_0_g2_sq2", 1, 8, 4, 2, 2500, 128, "q4_0", True, 2498, seed=51),
+    wl("decode_q4_0_d64_g4", 2, 16, 4, 1, 3333, 64, "q4_0", True, 3332, seed=52),
+    wl("decode_q4_0_mha_noncausal", 1, 4, 4, 1, 130, 128, "q4_0", False, 0, seed=53),
+    wl("decode_q4_0_sq4_g1", 1, 2, 2, 4, 700, 128, "q4_0", True, 690, seed=54),
+    wl("decode_q4_0_before_keys", 1, 8, 2, 1, 300, 128, "q4_0", True, -5, seed=55),
 ]
 
 
