@@ -573,22 +573,30 @@ struct Q4Head {
             for (int u = 0; u < ROWDW; ++u)
                 w[u] = *(const uint32_t *)(kr + 4 * u);
         }
+        // the NB accumulators' chains interleaved, so consecutive MFMAs are independent
         f32x4 sacc[NB];
         float dsc[NB];
 #pragma unroll
-        for (int bb = 0; bb < NB; ++bb) {
+        for (int q = 0; q < 4; ++q) {
+            uint32_t cw[NB], y[NB];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                uint32_t cw;
+            for (int bb = 0; bb < NB; ++bb) {
                 if (bb % 2 == 0)
-                    cw = __builtin_amdgcn_alignbit(w[9 * bb / 2 + q + 1], w[9 * bb / 2 + q], 16);
+                    cw[bb] = __builtin_amdgcn_alignbit(w[9 * bb / 2 + q + 1], w[9 * bb / 2 + q], 16);
                 else
-                    cw = w[(18 * bb + 2) / 4 + q];
-                const uint32_t y = cw >> 8;
-                sacc[bb] = mfma4(cw & 0x000F000Fu, y & 0x000F000Fu, qlo[bb][q],
-                                 q == 0 ? sinit[bb] : sacc[bb]);
-                sacc[bb] = mfma4(cw & 0x00F000F0u, y & 0x00F000F0u, qhi[bb][q], sacc[bb]);
+                    cw[bb] = w[(18 * bb + 2) / 4 + q];
+                y[bb] = cw[bb] >> 8;
             }
+#pragma unroll
+            for (int bb = 0; bb < NB; ++bb)
+                sacc[bb] = mfma4(cw[bb] & 0x000F000Fu, y[bb] & 0x000F000Fu, qlo[bb][q],
+                                 q == 0 ? sinit[bb] : sacc[bb]);
+#pragma unroll
+            for (int bb = 0; bb < NB; ++bb)
+                sacc[bb] = mfma4(cw[bb] & 0x00F000F0u, y[bb] & 0x00F000F0u, qhi[bb][q], sacc[bb]);
+        }
+#pragma unroll
+        for (int bb = 0; bb < NB; ++bb) {
             const uint32_t dbits = (bb % 2 == 0) ? (w[9 * bb / 2] & 0xFFFFu)
                                                  : (w[(18 * bb - 2) / 4] >> 16);
             dsc[bb] = (float)__builtin_bit_cast(_Float16, (uint16_t)dbits) * 0x1p24f;
@@ -648,24 +656,45 @@ struct Q4Head {
         return (u32x2){pk0, pk1};
     }
 
-    // O += P V over the tile (vt = the head's V row 0 in LDS).
-    __device__ __forceinline__ void pv(const uint8_t *vt, u32x2 pk)
+    // This lane's V operands of the tile (vt = the head's V row 0 in LDS), all read up front
+    // so their LDS latency overlaps the scores: per chunk c and key k, the two dwords the code
+    // dword is spliced from, and the block scale.
+    uint32_t vlo_w[NCH][4], vhi_w[NCH][4];
+    uint16_t vdq[NCH][4];
+    __device__ __forceinline__ void load_v(const uint8_t *vt)
     {
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+            const uint8_t *vr = vt + RS * 4 * KGC * c;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                vlo_w[c][k] = *(const uint32_t *)(vr + RS * k + vlo);
+                vhi_w[c][k] = *(const uint32_t *)(vr + RS * k + vhi);
+                vdq[c][k] = *(const uint16_t *)(vr + RS * k + vsc);
+            }
+        }
+    }
+
+    // O += P V over the tile whose operands load_v() read.
+    __device__ __forceinline__ void pv(u32x2 pk)
+    {
+        uint32_t pb0[NCH], pb1[NCH];
 #pragma unroll
         for (int c = 0; c < NCH; ++c) {
             // P of keys 4 (KGC c + kg) + 0..3, row j, from the score lane j + 4 kg + 16 KGC c
             const int src = psrc + 16 * KGC * c;
-            const uint32_t b0 = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)pk[0]);
-            const uint32_t b1 = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)pk[1]);
-            const uint8_t *vr = vt + RS * 4 * KGC * c;
+            pb0[c] = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)pk[0]);
+            pb1[c] = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)pk[1]);
+        }
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+            const uint32_t b0 = pb0[c], b1 = pb1[c];
             uint32_t cw[4];
             uint16_t dq[4];
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
-                const uint32_t lo = *(const uint32_t *)(vr + RS * k + vlo);
-                const uint32_t hi = *(const uint32_t *)(vr + RS * k + vhi);
-                cw[k] = __builtin_amdgcn_alignbit(hi, lo, vsh);
-                dq[k] = *(const uint16_t *)(vr + RS * k + vsc);
+                cw[k] = __builtin_amdgcn_alignbit(vhi_w[c][k], vlo_w[c][k], vsh);
+                dq[k] = vdq[c][k];
             }
             const f16x2 s01 = __builtin_bit_cast(f16x2, (uint32_t)dq[0] | ((uint32_t)dq[1] << 16));
             const f16x2 s23 = __builtin_bit_cast(f16x2, (uint32_t)dq[2] | ((uint32_t)dq[3] << 16));
@@ -737,12 +766,14 @@ struct Q4G {
     static constexpr int NI = 2 * S;                // wave-wide transfers per tile (K, then V)
     static constexpr int NIW = (NI + 3) / 4;        // per wave (surplus ones repeat the last)
     static constexpr int STAGE = 2 * TB;
-    static constexpr int NSTG = 2;
+    static constexpr int NSTG = 2;                  // stages (tiles in flight + 1)
+    static constexpr int OCC = 2;                   // workgroups per CU (LDS-bound)
     static_assert(GB % 16 == 0, "group rows are whole 16-byte chunks");
 };
+constexpr int kQ4gWorkgroups = 256 * Q4G<128>::OCC;
 
 template <int D>
-__global__ __launch_bounds__(kThreads, 2) void decode_q4g_kernel(DecodeParams p)
+__global__ __launch_bounds__(kThreads, Q4G<D>::OCC) void decode_q4g_kernel(DecodeParams p)
 {
     using G = Q4G<D>;
     using H = Q4Head<D, G::RS>;
@@ -806,7 +837,14 @@ __global__ __launch_bounds__(kThreads, 2) void decode_q4g_kernel(DecodeParams p)
     for (int kb = 0; kb < nb; ++kb) {
         // tile kb landed for every wave; every wave is done with tile kb - 1, whose stage the
         // next transfer refills
-        if constexpr (NSTG == 3) {
+        if constexpr (NSTG >= 4) {
+            if (kb + 2 < nb)
+                wait_vm<2 * NIW>();
+            else if (kb + 1 < nb)
+                wait_vm<NIW>();
+            else
+                wait_vm<0>();
+        } else if constexpr (NSTG == 3) {
             if (kb + 1 < nb)
                 wait_vm<NIW>();
             else
@@ -818,8 +856,9 @@ __global__ __launch_bounds__(kThreads, 2) void decode_q4g_kernel(DecodeParams p)
         if (kb + NSTG - 1 < nb)
             dma_tile(kb + NSTG - 1);
         const uint8_t *kt = lds + (kb % NSTG) * G::STAGE + wave * G::ROWB;
+        hd.load_v(kt + G::TB);
         const u32x2 pk = hd.scores(kt, ks + (int64_t)kb * kBN, a.c);
-        hd.pv(kt + G::TB, pk);
+        hd.pv(pk);
     }
 
     // this wave's head: write the split's partial rows directly
@@ -931,18 +970,14 @@ __global__ __launch_bounds__(kThreads, 2) void decode_q4w_kernel(DecodeParams p)
     for (int i = 0; i < ni; ++i) {
         const bool more = i + 1 < ni;
         const uint8_t *sk = wl + (i & 1) * W::STAGE;
-        // K rows of tile i have landed (its V rows and tile i + 1 may still be in flight)
-        if (more)
-            wait_vm<3 * NX>();
-        else
-            wait_vm<NX>();
-        const u32x2 pk = hd.scores(sk, ks + (int64_t)(wave + 4 * i) * kBN, a.c);
-        // V rows of tile i have landed
+        // tile i has landed (tile i + 1 may still be in flight)
         if (more)
             wait_vm<2 * NX>();
         else
             wait_vm<0>();
-        hd.pv(sk + TILEB, pk);
+        hd.load_v(sk + TILEB);
+        const u32x2 pk = hd.scores(sk, ks + (int64_t)(wave + 4 * i) * kBN, a.c);
+        hd.pv(pk);
         if (i + 2 < ni)
             dma_tile(i + 2);
     }
@@ -1004,12 +1039,25 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeParams p)
 
     const int qi = rr / a.G, hl = rr % a.G;
     uint16_t *op = (uint16_t *)a.o + (((int64_t)b * a.Sq + qi) * a.Hq + kvh * a.G + hl) * D;
+    // the splits' loads are issued 16 at a time, so their latencies overlap
     for (int d2 = lane; d2 < D / 2; d2 += 64) {
         float o0 = 0.0f, o1 = 0.0f;
-        for (int s = 0; s < p.n_split; ++s) {
-            const float w = wts[s];
-            o0 += w * base[(int64_t)s * stride + 2 * d2];
-            o1 += w * base[(int64_t)s * stride + 2 * d2 + 1];
+        int s = 0;
+        for (; s + 16 <= p.n_split; s += 16) {
+            f32x2 x[16];
+#pragma unroll
+            for (int u = 0; u < 16; ++u)
+                x[u] = *(const f32x2 *)(base + (int64_t)(s + u) * stride + 2 * d2);
+#pragma unroll
+            for (int u = 0; u < 16; ++u) {
+                o0 += wts[s + u] * x[u][0];
+                o1 += wts[s + u] * x[u][1];
+            }
+        }
+        for (; s < p.n_split; ++s) {
+            const f32x2 x = *(const f32x2 *)(base + (int64_t)s * stride + 2 * d2);
+            o0 += wts[s] * x[0];
+            o1 += wts[s] * x[1];
         }
         *(uint32_t *)(op + 2 * d2) = pack2<BF>(o0 * inv, o1 * inv);
     }
@@ -1054,8 +1102,10 @@ DecodeGrid decode_grid(int B, int Hq, int Hkv, int Sq, int Sk, int D, int64_t ke
     g.rows = (Hq / Hkv) * Sq;
     const int64_t heads = (int64_t)B * Hkv;
     // workgroups per key range: one per KV head, or one per group of 4 heads
-    const int64_t per = q4_grouped(kv, g.rows, Hkv) ? heads / 4 : heads;
-    int64_t want = per > 0 ? (kTargetWorkgroups + per - 1) / per : 1;
+    const bool grouped = q4_grouped(kv, g.rows, Hkv);
+    const int64_t per = grouped ? heads / 4 : heads;
+    const int64_t target = grouped ? kQ4gWorkgroups : kTargetWorkgroups;
+    int64_t want = per > 0 ? (target + per - 1) / per : 1;
     if (want > 1024)
         want = 1024;     // the merge kernel keeps one weight per split in LDS
     const int64_t tiles = (kend + kBN - 1) / kBN;

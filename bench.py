@@ -160,7 +160,9 @@ def main():
     do = torch.empty_like(dq)
     ws = torch.empty(max(16, fa.decode_workspace_bytes(wd.B, wd.Hq, wd.Hkv, wd.Sq, wd.Sk, wd.D)),
                      dtype=torch.uint8, device=dev)
-    flush = torch.ones(FLUSH_BYTES // 4, dtype=torch.int32, device=dev)
+    # float32, so sum() is one reduction kernel that only reads (an int32 sum would first
+    # write an int64 copy)
+    flush = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
 
