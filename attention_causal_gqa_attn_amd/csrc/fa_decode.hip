@@ -1018,6 +1018,57 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeParams p)
     const int b = rest / a.Hkv;
     const int stride = p.rows * (D + 2);
     const float *base = p.part + ((int64_t)b * a.Hkv + kvh) * p.n_split * stride + rr * (D + 2);
+    const int qi = rr / a.G, hl = rr % a.G;
+    uint16_t *op = (uint16_t *)a.o + (((int64_t)b * a.Sq + qi) * a.Hq + kvh * a.G + hl) * D;
+
+    if (p.n_split <= 64) {
+        // One memory round trip: every split's outputs (E per lane), frames and sums are
+        // loaded at once; split u's weight is lane u's, read back with v_readlane.
+        constexpr int E = D / 64;
+        const int ns = p.n_split;
+        float x[64][E];
+#pragma unroll
+        for (int u = 0; u < 64; ++u) {
+            const float *src = base + (int64_t)min(u, ns - 1) * stride + E * lane;
+            if constexpr (E == 2) {
+                const f32x2 v2 = *(const f32x2 *)src;
+                x[u][0] = v2[0];
+                x[u][1] = v2[1];
+            } else {
+                x[u][0] = *src;
+            }
+        }
+        const bool on = lane < ns;
+        const float f = on ? base[(int64_t)lane * stride + D] : -INFINITY;
+        const float l = on ? base[(int64_t)lane * stride + D + 1] : 0.0f;
+        float F = f;
+#pragma unroll
+        for (int m = 32; m >= 1; m >>= 1)
+            F = fmaxf(F, __shfl_xor(F, m, 64));
+        const float w = (F == -INFINITY || !on) ? 0.0f : exp2_fast(f - F);
+        float L = w * l;
+#pragma unroll
+        for (int m = 32; m >= 1; m >>= 1)
+            L += __shfl_xor(L, m, 64);
+        const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+        float o[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+            o[e] = 0.0f;
+#pragma unroll
+        for (int u = 0; u < 64; ++u) {
+            const float wu = __builtin_bit_cast(
+                float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), u));
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+                o[e] += wu * x[u][e];
+        }
+        if constexpr (E == 2)
+            *(uint32_t *)(op + 2 * lane) = pack2<BF>(o[0] * inv, o[1] * inv);
+        else
+            op[lane] = (uint16_t)(pack2<BF>(o[0] * inv, 0.0f) & 0xFFFFu);
+        return;
+    }
 
     float F = -INFINITY;
     for (int s = lane; s < p.n_split; s += 64)
@@ -1037,8 +1088,6 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeParams p)
     __syncthreads();
     const float inv = L > 0.0f ? 1.0f / L : 0.0f;
 
-    const int qi = rr / a.G, hl = rr % a.G;
-    uint16_t *op = (uint16_t *)a.o + (((int64_t)b * a.Sq + qi) * a.Hq + kvh * a.G + hl) * D;
     // the splits' loads are issued 16 at a time, so their latencies overlap
     for (int d2 = lane; d2 < D / 2; d2 += 64) {
         float o0 = 0.0f, o1 = 0.0f;

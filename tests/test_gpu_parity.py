@@ -151,6 +151,8 @@ DECODE = [
     wl("decode_q4_0_mha_noncausal", 1, 4, 4, 1, 130, 128, "q4_0", False, 0, seed=53),
     wl("decode_q4_0_sq4_g1", 1, 2, 2, 4, 700, 128, "q4_0", True, 690, seed=54),
     wl("decode_q4_0_before_keys", 1, 8, 2, 1, 300, 128, "q4_0", True, -5, seed=55),
+    # one KV head: more than 64 splits, the merge kernel's looped path
+    wl("decode_many_splits", 1, 4, 1, 1, 10000, 128, "f16", True, 9999, seed=56),
 ]
 
 
