@@ -18,17 +18,15 @@ struct AttnArgs {
     float c;            // scale * log2(e)
 };
 
-// Prefill workgroup decomposition: `waves` waves (4 or 8) of 32 query rows; hpw heads of one
-// KV group by qsub 32-row sub-blocks (hpw * qsub <= waves); heads beyond `waves` of a group go
-// to further chunks.
+// Prefill workgroup decomposition (fa_prefill16.hip): `waves` (4) waves of 64 query rows; hpw
+// heads of one KV group by qsub 64-row sub-blocks (hpw * qsub = waves); heads beyond `waves`
+// of a group go to further chunks.
 struct PrefillGrid {
     int waves, hpw, qsub, n_qblk, n_hchunk;
     int64_t n_wg;
 };
 PrefillGrid prefill_grid(const AttnArgs &a);
 hipError_t launch_prefill(const AttnArgs &a, hipStream_t stream);
-// f16 / bf16 caches: 4-wave workgroups of 64-row waves, tiles moved by LDS DMA
-// (fa_prefill16.hip)
 PrefillGrid prefill16_grid(const AttnArgs &a);
 hipError_t launch_prefill16(const AttnArgs &a, const PrefillGrid &g, hipStream_t stream);
 

@@ -16,7 +16,11 @@
 //  * tiles keep their row-major [key][d] layout in LDS with 16-byte chunks XOR-swizzled per
 //    row, so K fragment reads (16 bytes) and V^T transpose reads (ds_read_b64_tr_b16) are free
 //    of bank conflicts; K runs 4 tiles ahead of its use and V 2 tiles, through 4-stage rings,
-//    so every tile has three loop iterations to arrive.
+//    so every tile has three loop iterations to arrive;
+//  * a q4_0 cache arrives raw (12-byte LDS-DMA chunks, K 4 tiles and V 2 tiles ahead) and the
+//    waves dequantize it into 2-stage f16 K and V rings of the same layout, one tile of each per
+//    iteration (K two tiles ahead of its scores, V one ahead of its P.V), so everything after
+//    the dequantization is the f16 kernel.
 #include <cstdlib>
 #include <utility>
 
@@ -54,6 +58,14 @@ constexpr int waitcnt_vm_lgkm0(int vm) { return (vm & 15) | ((vm >> 4) << 14) | 
 __device__ __forceinline__ void dma16(const uint8_t *gbase, uint32_t voff, uint32_t lds_base)
 {
     asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :: "v"(voff), "s"(gbase), "s"(lds_base) : "memory");
+}
+
+// One 12-byte LDS-DMA transfer per lane: gbase + voff -> LDS lds_base + 16 * lane (a 16-byte
+// slot per lane), for the q4_0 rows, whose 18-byte blocks split into 12-byte chunks.
+__device__ __forceinline__ void dma12(const uint8_t *gbase, uint32_t voff, uint32_t lds_base)
+{
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx3 %0, %1"
                  :: "v"(voff), "s"(gbase), "s"(lds_base) : "memory");
 }
 
@@ -122,6 +134,20 @@ struct Geom16 {
     // chunk swizzles: slot = chunk ^ sw(row)
     __device__ static __forceinline__ int swk(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
     __device__ static __forceinline__ int swv(int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
+};
+
+// q4_0 caches: a key row of one KV head (D/32 blocks of 18 bytes) is CPR 12-byte chunks, each
+// landing in a 16-byte LDS slot (row r's chunk c in slot r * CPR + c); K raw tiles run 4 tiles
+// ahead through KR stages, V 2 tiles through VR; the f16 K and V rings have 2 stages each.
+template <int D>
+struct Q4Raw {
+    static constexpr int ROWB = 18 * (D / 32);         // bytes of a key row
+    static constexpr int CPR = ROWB / 12;
+    static constexpr int RAWT = kBN * CPR * 16;        // one tensor's raw tile in LDS
+    static constexpr int NX = CPR;                     // wave-wide transfers per tensor tile
+    static constexpr int NIW = (2 * NX + kNW - 1) / kNW;   // per wave per iteration, K + V
+    static constexpr int KR = 4, VR = 3;
+    static constexpr int LDS = 4 * Geom16<D>::TILE + (KR + VR) * RAWT;
 };
 
 // f(std::integral_constant<int, I>) for I = B .. E-1, expanded at compile time
@@ -310,13 +336,16 @@ struct Plans {
     static_assert(schedule_ok<NDT, NST, NM>(sc), "softmax units placed in time");
 };
 
-template <int D, bool BF>
+template <int D, int KVT>
 __global__ __launch_bounds__(kNT, 1) void prefill16_kernel(Prefill16Params p)
 {
+    constexpr bool BF = KVT == KV_BF16;
+    constexpr bool Q4 = KVT == KV_Q4_0;
     using G = Geom16<D>;
+    using QR = Q4Raw<D>;
     using PL = Plans<D>;
     constexpr int NDT = PL::NDT, NST = PL::NST, NM = PL::NM;
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[G::LDS];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[Q4 ? QR::LDS : G::LDS];
     typedef __attribute__((address_space(3))) s16x4_t lds_s16x4;
 
     const AttnArgs &a = p.a;
@@ -408,8 +437,10 @@ __global__ __launch_bounds__(kNT, 1) void prefill16_kernel(Prefill16Params p)
         lwave[i] = __builtin_amdgcn_readfirstlane(lds0 + (uint32_t)((i * kNW + wave) * 1024));
     }
     // K stages [0, kStages), V stages [kStages, 2*kStages); tile j lives in stage j % kStages
-    auto kstage = [&](int tl) INL { return lds + (tl & (kStages - 1)) * G::TILE; };
-    auto vstage = [&](int tl) INL { return lds + (kStages + (tl & (kStages - 1))) * G::TILE; };
+    // (q4_0: f16 K stages [0, 2), V stages [2, 4), then the raw stages)
+    constexpr int FS = Q4 ? 2 : kStages;
+    auto kstage = [&](int tl) INL { return lds + (tl & (FS - 1)) * G::TILE; };
+    auto vstage = [&](int tl) INL { return lds + (FS + (tl & (FS - 1))) * G::TILE; };
     // Transfer i of tile tl of K (is_v false) or V into a stage. Tiles past the last one
     // re-read the last tile (into a stage nobody reads any more), so every loop iteration
     // issues the same transfers and the wait counts stay fixed; rows past the end of the
@@ -428,6 +459,77 @@ __global__ __launch_bounds__(kNT, 1) void prefill16_kernel(Prefill16Params p)
             dma_one(false, (n + 4) & (kStages - 1), n + 4, i);
         else
             dma_one(true, kStages + ((n + 2) & (kStages - 1)), n + 2, i - G::NDMA);
+    };
+
+    // ---- q4_0: raw transfers and the dequantization into the f16 rings ----------------------
+    const uint32_t growq = (uint32_t)a.Hkv * QR::ROWB;
+    const uint8_t *kq = (const uint8_t *)a.k + ((int64_t)b * a.Sk * a.Hkv + kvh) * QR::ROWB;
+    const uint8_t *vq = (const uint8_t *)a.v + ((int64_t)b * a.Sk * a.Hkv + kvh) * QR::ROWB;
+    auto rawk = [&](int tl) INL { return lds + 4 * G::TILE + (tl & (QR::KR - 1)) * QR::RAWT; };
+    auto rawv = [&](int tl) INL {
+        return lds + 4 * G::TILE + QR::KR * QR::RAWT + (tl % QR::VR) * QR::RAWT;
+    };
+    // transfer x of raw tile tl (slots 64 x .. 64 x + 63); tiles past the last re-read the last
+    // one, rows past the sequence's end repeat its last key
+    auto dma_raw = [&](bool is_v, int tl, int x) INL {
+        const uint8_t *stg = is_v ? rawv(tl) : rawk(tl);
+        tl = min(tl, nb - 1);
+        const int64_t k0 = (int64_t)tl * kBN;
+        const int sl = 64 * x + lane;
+        const int last = (int)min((int64_t)kBN - 1, (int64_t)a.Sk - 1 - k0);
+        const uint32_t row = (uint32_t)min(sl / QR::CPR, last);
+        dma12((is_v ? vq : kq) + k0 * growq, row * growq + 12u * (uint32_t)(sl % QR::CPR),
+              __builtin_amdgcn_readfirstlane(lds_addr(stg) + (uint32_t)(1024 * x)));
+    };
+    // this wave's m-th transfer of iteration n: raw K(n+4), then raw V(n+2)
+    auto dma_q4 = [&](int n, int m) INL {
+        const int i = min(wave + kNW * m, 2 * QR::NX - 1);
+        if (i < QR::NX)
+            dma_raw(false, n + 4, i);
+        else
+            dma_raw(true, n + 2, i - QR::NX);
+    };
+    // This thread's (key row, block) item of a tile: at D = 128 one K and one V item, wave w
+    // taking the blocks of parity w & 1 (whether a block starts at byte 0 or 6 of its first
+    // chunk is then wave-uniform); at D = 64 waves 0, 1 take K and waves 2, 3 V (block w & 1).
+    const int dq_row = D == 128 ? 32 * (wave >> 1) + (lane & 31) : lane;
+    const int dq_blk = D == 128 ? 2 * (lane >> 5) + (wave & 1) : (wave & 1);
+    auto dequant_item = [&](const uint8_t *raw, uint8_t *dst, bool is_v) INL {
+        const uint8_t *sa = raw + 16 * (dq_row * QR::CPR + (3 * dq_blk) / 2);
+        const u32x4 A = *(const u32x4 *)sa, Bq = *(const u32x4 *)(sa + 16);
+        uint32_t dbits, codes[4];
+        if (wave & 1) {                            // odd block: 6 bytes into chunk A
+            dbits = A[1] >> 16;
+            codes[0] = A[2];
+            codes[1] = Bq[0];
+            codes[2] = Bq[1];
+            codes[3] = Bq[2];
+        } else {
+            dbits = A[0] & 0xFFFFu;
+            codes[0] = __builtin_amdgcn_alignbit(A[1], A[0], 16);
+            codes[1] = __builtin_amdgcn_alignbit(A[2], A[1], 16);
+            codes[2] = __builtin_amdgcn_alignbit(Bq[0], A[2], 16);
+            codes[3] = __builtin_amdgcn_alignbit(Bq[1], Bq[0], 16);
+        }
+        const uint32_t d2 = dbits * 0x10001u;
+        uint32_t lo[4][2], hi[4][2];
+#pragma unroll
+        for (int gg = 0; gg < 4; ++gg)
+            q4_unpack_row(codes[gg], d2, lo[gg], hi[gg]);
+        const int sw = is_v ? G::swv(dq_row) : G::swk(dq_row);
+        uint8_t *rp = dst + dq_row * G::ROW;
+        *(u32x4 *)(rp + 16 * ((4 * dq_blk + 0) ^ sw)) = (u32x4){lo[0][0], lo[0][1], lo[1][0], lo[1][1]};
+        *(u32x4 *)(rp + 16 * ((4 * dq_blk + 1) ^ sw)) = (u32x4){lo[2][0], lo[2][1], lo[3][0], lo[3][1]};
+        *(u32x4 *)(rp + 16 * ((4 * dq_blk + 2) ^ sw)) = (u32x4){hi[0][0], hi[0][1], hi[1][0], hi[1][1]};
+        *(u32x4 *)(rp + 16 * ((4 * dq_blk + 3) ^ sw)) = (u32x4){hi[2][0], hi[2][1], hi[3][0], hi[3][1]};
+    };
+    auto dequant_k = [&](int tl) INL {
+        if (D == 128 || wave < 2)
+            dequant_item(rawk(tl), kstage(tl), false);
+    };
+    auto dequant_v = [&](int tl) INL {
+        if (D == 128 || wave >= 2)
+            dequant_item(rawv(tl), vstage(tl), true);
     };
 
     // ---- fragment addressing -----------------------------------------------------------------
@@ -609,12 +711,24 @@ __global__ __launch_bounds__(kNT, 1) void prefill16_kernel(Prefill16Params p)
                 fb[(f + kRead) % (kRead + 1)] = kread(ks, f + kRead);
             s_slot(i, fb[f % (kRead + 1)], s0, s1n);
             units(std::integral_constant<int, NM + i>{});
-            if constexpr ((i & 3) == 1 && (i >> 2) < 2 * G::NDMA)
+            if constexpr (Q4) {
+                if constexpr ((i & 3) == 1 && (i >> 2) < QR::NIW)
+                    dma_q4(n, i >> 2);
+            } else if constexpr ((i & 3) == 1 && (i >> 2) < 2 * G::NDMA) {
                 dma_part(n, i >> 2);
+            }
             __builtin_amdgcn_sched_barrier(0);
         });
         static_for<PL::sc.first[2 * NM], kNU>([&](auto ic) INL { run_unit(ic, s0, s1c); });
         apply_rescale(1);
+        if constexpr (Q4) {
+            // K(n+2) and V(n) into the stages of K(n) and V(n-2), read in iteration n-1 (at the
+            // end of the tile, where the last score MFMAs are still executing)
+            __builtin_amdgcn_sched_barrier(0);
+            dequant_k(n + 2);
+            dequant_v(n);
+            __builtin_amdgcn_sched_barrier(0);
+        }
     };
 
     // ---- pipeline --------------------------------------------------------------------------------
@@ -631,22 +745,37 @@ __global__ __launch_bounds__(kNT, 1) void prefill16_kernel(Prefill16Params p)
             __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
         asm volatile("s_barrier" ::: "memory");
     };
-    // prologue: K(0..3), V(0..1)
+    // prologue: K(0..3), V(0..1) (q4_0: raw, the transfers dealt round-robin to the waves)
     if (nb > 0) {
+        if constexpr (Q4) {
 #pragma unroll
-        for (int tl = 0; tl < 4; ++tl)
+            for (int tl = 0; tl < 4; ++tl)
 #pragma unroll
-            for (int i = 0; i < G::NDMA; ++i)
-                dma_one(false, tl, tl, i);
+                for (int x = 0; x < QR::NX; ++x)
+                    if (x % kNW == wave)
+                        dma_raw(false, tl, x);
 #pragma unroll
-        for (int tl = 0; tl < 2; ++tl)
+            for (int tl = 0; tl < 2; ++tl)
 #pragma unroll
-            for (int i = 0; i < G::NDMA; ++i)
-                dma_one(true, kStages + tl, tl, i);
+                for (int x = 0; x < QR::NX; ++x)
+                    if (x % kNW == wave)
+                        dma_raw(true, tl, x);
+        } else {
+#pragma unroll
+            for (int tl = 0; tl < 4; ++tl)
+#pragma unroll
+                for (int i = 0; i < G::NDMA; ++i)
+                    dma_one(false, tl, tl, i);
+#pragma unroll
+            for (int tl = 0; tl < 2; ++tl)
+#pragma unroll
+                for (int i = 0; i < G::NDMA; ++i)
+                    dma_one(true, kStages + tl, tl, i);
+        }
     }
 
-    // V stage kStages-1 stands in for tile -1: zeros, so that P.V of tile -1 adds nothing
-    // (P is zero too); the DMA of tile kStages-1 into it is issued after barrier 1
+    // The V stage of tile -1 holds zeros, so that P.V of tile -1 adds nothing (P is zero too);
+    // tile kStages-1 (q4_0: tile 1) is written into it only after barrier 1
     {
         uint8_t *z = vstage(-1);
         for (int o = t * 16; o < G::TILE; o += kNT * 16)
@@ -656,11 +785,25 @@ __global__ __launch_bounds__(kNT, 1) void prefill16_kernel(Prefill16Params p)
     }
     f32x16 s0[2], s1a[2], s1b[2];
     auto iteration = [&](int n, f32x16 *s1c, f32x16 *s1n) INL {
-        wait_tiles(2 * min(n, 2));
+        if constexpr (Q4) {
+            // raw K(n+2) and V(n) landed: only iteration n-1's transfers may be in flight
+            if (n >= 1)
+                __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(QR::NIW));
+            else
+                __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+            asm volatile("s_barrier" ::: "memory");
+        } else {
+            wait_tiles(2 * min(n, 2));
+        }
         tile(n, s0, s1c, s1n);
     };
     if (nb > 0) {
         wait_tiles(0);           // K(0) resident; also orders the zero fill before its reads
+        if constexpr (Q4) {
+            dequant_k(0);
+            dequant_k(1);
+            wait_tiles(0);
+        }
         scores_all(kstage(0), s0, s1a);
     }
     for (int n = 0; n < nb; n += 2) {
@@ -693,10 +836,10 @@ __global__ __launch_bounds__(kNT, 1) void prefill16_kernel(Prefill16Params p)
     }
 }
 
-template <int D, bool BF>
+template <int D, int KVT>
 hipError_t launch16(const Prefill16Params &p, int64_t n_wg, hipStream_t stream)
 {
-    hipLaunchKernelGGL((prefill16_kernel<D, BF>), dim3((unsigned)n_wg), dim3(kNT), 0, stream, p);
+    hipLaunchKernelGGL((prefill16_kernel<D, KVT>), dim3((unsigned)n_wg), dim3(kNT), 0, stream, p);
     return hipGetLastError();
 }
 
@@ -714,14 +857,30 @@ PrefillGrid prefill16_grid(const AttnArgs &a)
     return g;
 }
 
+// every cache type takes this kernel (q4_0: raw LDS-DMA, dequantized into its f16 rings)
+PrefillGrid prefill_grid(const AttnArgs &a) { return prefill16_grid(a); }
+
+hipError_t launch_prefill(const AttnArgs &a, hipStream_t stream)
+{
+    const PrefillGrid g = prefill16_grid(a);
+    return g.n_wg == 0 ? hipSuccess : launch_prefill16(a, g, stream);
+}
+
 hipError_t launch_prefill16(const AttnArgs &a, const PrefillGrid &g, hipStream_t stream)
 {
     const Prefill16Params p{a, g.hpw, g.qsub, g.n_qblk, g.n_hchunk};
-    if (a.D == 128)
-        return a.kv == KV_BF16 ? launch16<128, true>(p, g.n_wg, stream)
-                               : launch16<128, false>(p, g.n_wg, stream);
-    return a.kv == KV_BF16 ? launch16<64, true>(p, g.n_wg, stream)
-                           : launch16<64, false>(p, g.n_wg, stream);
+    if (a.D == 128) {
+        if (a.kv == KV_BF16)
+            return launch16<128, KV_BF16>(p, g.n_wg, stream);
+        if (a.kv == KV_Q4_0)
+            return launch16<128, KV_Q4_0>(p, g.n_wg, stream);
+        return launch16<128, KV_F16>(p, g.n_wg, stream);
+    }
+    if (a.kv == KV_BF16)
+        return launch16<64, KV_BF16>(p, g.n_wg, stream);
+    if (a.kv == KV_Q4_0)
+        return launch16<64, KV_Q4_0>(p, g.n_wg, stream);
+    return launch16<64, KV_F16>(p, g.n_wg, stream);
 }
 
 #undef INL

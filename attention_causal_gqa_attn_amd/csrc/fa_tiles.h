@@ -1,5 +1,6 @@
-// K/V tile staging: global memory -> registers -> LDS, shared by the prefill and decode
-// kernels. A tile is kBN = 64 consecutive keys of one KV head:
+// K/V tile staging for the decode kernels that keep f16 tiles in LDS (the 16-bit caches, and
+// q4_0 with more than 4 query rows per KV head): global memory or a raw LDS stage -> registers
+// -> LDS. A tile is kBN = 64 consecutive keys of one KV head:
 //   K tile  [64 keys][D]      row stride D + 8 elements (16 B pad: conflict-free row reads)
 //   V^T tile [D][64 keys]     row stride 64 + 8 elements (transposed at store time, so the
 //                             P.V MFMA reads 8 consecutive keys of one d as one 16-byte load)
@@ -194,36 +195,7 @@ struct TileLoader<D, KV_Q4_0, NT> {
             off[r] = (uint32_t)(2 * kp + r) * row + (uint32_t)(boff & ~3);
     }
 
-    // Global loads of the tile starting at key k0 (k0 < Sk); in the last, partial tile keys
-    // past the end repeat the last key.
-    __device__ __forceinline__ void load(int k0)
-    {
-        if (!busy())
-            return;
-        const uint8_t *tile = base + (int64_t)k0 * row;
-        if (k0 + kBN <= Sk) {
-#pragma unroll
-            for (int r = 0; r < 2; ++r) {
-                const uint32_t *p = (const uint32_t *)(tile + off[r]);
-#pragma unroll
-                for (int i = 0; i < 5; ++i)
-                    w[r][i] = p[i];
-            }
-        } else {
-            const int last = Sk - 1 - k0;
-#pragma unroll
-            for (int r = 0; r < 2; ++r) {
-                const uint32_t key = (uint32_t)min(2 * kp + r, last);
-                const uint32_t *p =
-                    (const uint32_t *)(tile + key * row + (uint32_t)((18 * blk) & ~3));
-#pragma unroll
-                for (int i = 0; i < 5; ++i)
-                    w[r][i] = p[i];
-            }
-        }
-    }
-
-    // Staging through LDS instead: the raw tile is copied into LDS by 12-byte LDS-DMA
+    // The raw tile is copied into LDS by 12-byte LDS-DMA
     // transfers, each landing in a 16-byte slot. Chunk j (bytes 12j .. 12j+11) of key row
     // 2*kp + rr sits in slot (rr*32 + kp) * RAW_STRIDE + j: even and odd rows in separate
     // halves and an odd slot stride, so the 16-byte reads of consecutive lanes (consecutive kp)
@@ -252,28 +224,6 @@ struct TileLoader<D, KV_Q4_0, NT> {
                 w[rr][3] = Bq[1]; w[rr][4] = Bq[2];
             }
         }
-    }
-
-    // K (V) halves: threads [0, D) stage K, [D, 2D) stage V; at D = 128 this is wave-uniform.
-    __device__ __forceinline__ void load_k(int k0)
-    {
-        if (tensor == 0)
-            load(k0);
-    }
-    __device__ __forceinline__ void load_v(int k0)
-    {
-        if (tensor == 1)
-            load(k0);
-    }
-    __device__ __forceinline__ void store_k(uint16_t *lk) const
-    {
-        if (tensor == 0)
-            store(lk, nullptr);
-    }
-    __device__ __forceinline__ void store_v(uint16_t *lv) const
-    {
-        if (tensor == 1)
-            store(nullptr, lv);
     }
 
     __device__ void store(uint16_t *lk, uint16_t *lv) const
