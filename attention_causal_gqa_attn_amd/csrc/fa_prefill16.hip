@@ -494,9 +494,15 @@ __global__ __launch_bounds__(kNT, 1) void prefill16_kernel(Prefill16Params p)
     // chunk is then wave-uniform); at D = 64 waves 0, 1 take K and waves 2, 3 V (block w & 1).
     const int dq_row = D == 128 ? 32 * (wave >> 1) + (lane & 31) : lane;
     const int dq_blk = D == 128 ? 2 * (lane >> 5) + (wave & 1) : (wave & 1);
-    auto dequant_item = [&](const uint8_t *raw, uint8_t *dst, bool is_v) INL {
+    struct RawBlock {
+        u32x4 A, Bq;
+    };
+    auto dq_load = [&](const uint8_t *raw) INL -> RawBlock {
         const uint8_t *sa = raw + 16 * (dq_row * QR::CPR + (3 * dq_blk) / 2);
-        const u32x4 A = *(const u32x4 *)sa, Bq = *(const u32x4 *)(sa + 16);
+        return RawBlock{*(const u32x4 *)sa, *(const u32x4 *)(sa + 16)};
+    };
+    auto dq_store = [&](const RawBlock &rb, uint8_t *dst, bool is_v) INL {
+        const u32x4 &A = rb.A, &Bq = rb.Bq;
         uint32_t dbits, codes[4];
         if (wave & 1) {                            // odd block: 6 bytes into chunk A
             dbits = A[1] >> 16;
@@ -525,11 +531,20 @@ __global__ __launch_bounds__(kNT, 1) void prefill16_kernel(Prefill16Params p)
     };
     auto dequant_k = [&](int tl) INL {
         if (D == 128 || wave < 2)
-            dequant_item(rawk(tl), kstage(tl), false);
+            dq_store(dq_load(rawk(tl)), kstage(tl), false);
     };
-    auto dequant_v = [&](int tl) INL {
-        if (D == 128 || wave >= 2)
-            dequant_item(rawv(tl), vstage(tl), true);
+    // K tile tk and V tile tv together: both raw reads are issued before either item's stores
+    // (the compiler cannot move a read of the raw stages past a store into the f16 rings)
+    auto dequant_kv = [&](int tk, int tv) INL {
+        if constexpr (D == 128) {
+            const RawBlock rk = dq_load(rawk(tk)), rv = dq_load(rawv(tv));
+            dq_store(rk, kstage(tk), false);
+            dq_store(rv, vstage(tv), true);
+        } else if (wave < 2) {
+            dq_store(dq_load(rawk(tk)), kstage(tk), false);
+        } else {
+            dq_store(dq_load(rawv(tv)), vstage(tv), true);
+        }
     };
 
     // ---- fragment addressing -----------------------------------------------------------------
@@ -725,8 +740,7 @@ __global__ __launch_bounds__(kNT, 1) void prefill16_kernel(Prefill16Params p)
             // K(n+2) and V(n) into the stages of K(n) and V(n-2), read in iteration n-1 (at the
             // end of the tile, where the last score MFMAs are still executing)
             __builtin_amdgcn_sched_barrier(0);
-            dequant_k(n + 2);
-            dequant_v(n);
+            dequant_kv(n + 2, n);
             __builtin_amdgcn_sched_barrier(0);
         }
     };

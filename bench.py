@@ -4,7 +4,10 @@ One step = one pass of the whole path over resident inputs:
   * prefill: 2048 f16 queries as the last positions of 16384 keys, GQA 32/8, D=128, causal
     (fa_prefill, one MFMA kernel);
   * decode:  4 sequences x 1 query against 32768 q4_0-cached keys, GQA 32/8, D=128
-    (fa_decode, split kernel + merge kernel).
+    (fa_decode, split kernel + merge kernel);
+  * the same prefill against a q4_0 cache (fa_prefill, dequantization in the kernel), and
+    the unfused arm beside it: fa_dequant_q4_0 of K and V into f16 buffers, then the f16
+    fa_prefill (reported, not part of `value`).
 Before each call a 1 GiB buffer is read so that neither call finds its inputs in the 256 MB
 last-level cache (the decode working set, 151 MB, would otherwise stay resident). The flush
 reads rather than writes: a written flush leaves up to 256 MB of dirty lines in that cache,
@@ -152,12 +155,20 @@ def main():
 
     wp = W.WORKLOADS["prefill_16k_f16"]
     wd = W.WORKLOADS["decode_q4_0"]
+    wq = W.WORKLOADS["prefill_16k_q4_0"]
     xp = W.generate(wp)
     xd = W.generate(wd)
+    xq = W.generate(wq)
     pq, pk, pv = to_dev(xp.q, "f16"), to_dev(xp.k, "f16"), to_dev(xp.v, "f16")
     dq, dk, dv = to_dev(xd.q, "f16"), to_dev(xd.k, "q4_0"), to_dev(xd.v, "q4_0")
+    qq, qk, qv = to_dev(xq.q, "f16"), to_dev(xq.k, "q4_0"), to_dev(xq.v, "q4_0")
     po = torch.empty_like(pq)
     do = torch.empty_like(dq)
+    qo = torch.empty_like(qq)
+    qo2 = torch.empty_like(qq)
+    kf = torch.empty(wq.B, wq.Sk, wq.Hkv, wq.D, dtype=torch.float16, device=dev)
+    vf = torch.empty_like(kf)
+    q_blocks = qk.numel() // 18
     ws = torch.empty(max(16, fa.decode_workspace_bytes(wd.B, wd.Hq, wd.Hkv, wd.Sq, wd.Sk, wd.D)),
                      dtype=torch.uint8, device=dev)
     # float32, so sum() is one reduction kernel that only reads (an int32 sum would first
@@ -174,21 +185,31 @@ def main():
         fa.decode(dq, dk, dv, causal=True, offset=wd.causal_offset, scale=wd.scale, out=do,
                   workspace=ws, stream=stream)
 
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    def prefill_q4():
+        fa.prefill(qq, qk, qv, causal=True, offset=wq.causal_offset, scale=wq.scale, out=qo,
+                   stream=stream)
+
+    def prefill_q4_unfused():
+        for src, dst in ((qk, kf), (qv, vf)):
+            rc = fa.fa_dequant_q4_0(src.data_ptr(), q_blocks, None, dst.data_ptr(),
+                                    stream.cuda_stream)
+            if rc != fa.FA_OK:
+                raise fa.FAError(rc, "fa_dequant_q4_0")
+        fa.prefill(qq, kf, vf, causal=True, offset=wq.causal_offset, scale=wq.scale, out=qo2,
+                   stream=stream)
+
+    calls = [prefill, decode, prefill_q4, prefill_q4_unfused]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * len(calls))]
+          for _ in range(args.steps)]
 
     def step(i=None, k=0):
-        flush.sum()
-        if i is not None:
-            ev[i][0].record(stream)
-        prefill()
-        if i is not None:
-            ev[i][1].record(stream)
-        flush.sum()
-        if i is not None:
-            ev[i][2].record(stream)
-        decode()
-        if i is not None:
-            ev[i][3].record(stream)
+        for c, call in enumerate(calls):
+            flush.sum()
+            if i is not None:
+                ev[i][2 * c].record(stream)
+            call()
+            if i is not None:
+                ev[i][2 * c + 1].record(stream)
 
     # Warm-up: the GPU's clocks take tens of milliseconds of load to settle, so before the W
     # counted warm-up steps run untimed steps until CLOCK_WARMUP_S of wall time has passed.
@@ -209,6 +230,9 @@ def main():
 
     p_ms = np.array([e[0].elapsed_time(e[1]) for e in ev])
     d_ms = np.array([e[2].elapsed_time(e[3]) for e in ev])
+    q_ms = np.array([e[4].elapsed_time(e[5]) for e in ev])
+    u_ms = np.array([e[6].elapsed_time(e[7]) for e in ev])
+    qflops = W.attention_flops(wq)
     flops = W.attention_flops(wp)
     dbytes = W.algorithmic_bytes(wd)
     p_s = float(p_ms.mean()) * 1e-3
@@ -250,6 +274,20 @@ def main():
         "roofline_decode": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                             "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
                             "algorithmic_bytes_per_call": dbytes},
+        "prefill_q4_0": {"workload": "prefill_16k_q4_0 (the prefill workload against a q4_0 "
+                                     "K/V cache, dequantized in the kernel)",
+                         "tflops": round(qflops / (float(q_ms.mean()) * 1e-3) / 1e12, 3),
+                         "ms_mean": round(float(q_ms.mean()), 5),
+                         "ms_median": round(float(np.median(q_ms)), 5),
+                         "frac_of_mfma_peak": round(qflops / (float(q_ms.mean()) * 1e-3) / 1e12
+                                                    / PEAK_MFMA_F16_TFLOPS, 4),
+                         "kernel": "prefill16_kernel<128, q4_0>"},
+        "prefill_q4_0_unfused": {"tflops": round(qflops / (float(u_ms.mean()) * 1e-3) / 1e12, 3),
+                                 "ms_mean": round(float(u_ms.mean()), 5),
+                                 "ms_median": round(float(np.median(u_ms)), 5),
+                                 "what": "fa_dequant_q4_0 of K and V to f16 buffers (two "
+                                         "launches), then the f16 fa_prefill",
+                                 "extra_bytes": int(kf.numel() * 2 * 2)},
         "source_hash": source_hash(),
     }
     if not args.no_cpu_baseline:

@@ -129,6 +129,25 @@ def test_prefill_second_seeds():
         compare(w, got[rows], oracle_out(w, x, rows=rows), f"{name}/seed{seed}")
 
 
+def test_q4_0_prefill_fused_equals_unfused():
+    """The q4_0 prefill against its unfused arm (fa_dequant_q4_0 of K and V to f16, then the
+    f16 prefill): identical bits, since the kernel dequantizes to the same f16 values and then
+    runs the f16 schedule; D = 128 and D = 64."""
+    for w in (W.WORKLOADS["prefill_16k_q4_0"].with_(Sk=4096 + 37, Sq=1000, offset=None),
+              wl("q4_d64_unfused", 2, 8, 2, 300, 700, 64, "q4_0", True, 400, seed=61)):
+        say(f"q4_0 fused vs unfused {w}")
+        x = W.generate(w)
+        q, k, v = (to_dev(x.q, w.q_dtype), to_dev(x.k, w.kv), to_dev(x.v, w.kv))
+        fused = fa.prefill(q, k, v, causal=w.causal, offset=w.causal_offset, scale=w.scale)
+        _, kf = fa.dequant_q4_0(k.reshape(-1))
+        _, vf = fa.dequant_q4_0(v.reshape(-1))
+        shape = (w.B, w.Sk, w.Hkv, w.D)
+        unfused = fa.prefill(q, kf.view(shape), vf.view(shape), causal=w.causal,
+                             offset=w.causal_offset, scale=w.scale)
+        torch.cuda.synchronize()
+        assert torch.equal(fused, unfused), w.name
+
+
 # ---------------------------------------------------------------------------------------------
 # decode (split-K + log-sum-exp merge)
 # ---------------------------------------------------------------------------------------------
