@@ -6,6 +6,9 @@ O = softmax(scale * Q K^T + causal mask) V as an explicit f32 matmul + softmax +
 (mlxcel PR #2306, commit message 2; mi210-llm-stack build guide, Verification). It shares no
 code with the HIP path and never calls it.
 
+It also holds the q4_0 cache writer's reference (quantize_q4_0: d = f16(max|x| / 8), codes
+clamp(round_half_away(x / d) + 8, 0, 15)), a reading of the q4_0 format the pages name.
+
 Argument conventions: q is [B, Sq, Hq, D] as numpy float16 (f16) or uint16 bit patterns
 (bf16); k and v are [B, Sk, Hkv, D] in the same way, or uint8 [B, Sk, Hkv, D/32*18] q4_0
 blocks. Results are float32.
@@ -62,8 +65,9 @@ class Oracle:
         lib.orc_dequant_q4_0.argtypes = [vp, i64, vp, vp]
         lib.orc_half_to_float.argtypes = [vp, i64, vp]
         lib.orc_float_to_half.argtypes = [vp, i64, vp]
+        lib.orc_quantize_q4_0.argtypes = [vp, i32, i64, vp]
         for fn in (lib.orc_attention, lib.orc_probs, lib.orc_dequant_q4_0,
-                   lib.orc_half_to_float, lib.orc_float_to_half):
+                   lib.orc_half_to_float, lib.orc_float_to_half, lib.orc_quantize_q4_0):
             fn.restype = i32
         self.path = path
         self.lib = lib
@@ -126,6 +130,19 @@ class Oracle:
             raise ValueError("oracle rejected the arguments")
         return f32, f16
 
+    def quantize_q4_0(self, x: np.ndarray, src: str = "f32") -> np.ndarray:
+        """q4_0 cache writer: source elements (float32 values for src "f32", uint16 bit
+        patterns for "f16" / "bf16"), a multiple of 32 of them, -> uint8 blocks [n, 18]."""
+        code = {"f32": 0, "f16": 1, "bf16": 2}[src]
+        x = _c(np.asarray(x, dtype=np.float32 if src == "f32" else np.uint16))
+        if x.size % 32:
+            raise ValueError("the source must hold whole 32-element blocks")
+        n = x.size // 32
+        out = np.empty((n, 18), np.uint8)
+        if self.lib.orc_quantize_q4_0(_ptr(x), code, n, _ptr(out)):
+            raise ValueError("oracle rejected the arguments")
+        return out
+
     def half_to_float(self, bits: np.ndarray) -> np.ndarray:
         bits = _c(np.asarray(bits, dtype=np.uint16))
         out = np.empty(bits.shape, np.float32)
@@ -164,6 +181,10 @@ def probs(*a, **kw):
 
 def dequant_q4_0(*a, **kw):
     return default().dequant_q4_0(*a, **kw)
+
+
+def quantize_q4_0(*a, **kw):
+    return default().quantize_q4_0(*a, **kw)
 
 
 def half_to_float(*a, **kw):

@@ -149,6 +149,63 @@ int orc_float_to_half(const float *x, int64_t n, uint16_t *out)
     return ORC_OK;
 }
 
+/* ---------------------------------------------------------------------------------------- */
+/* q4_0 cache writer                                                                          */
+/* ---------------------------------------------------------------------------------------- */
+/* The pages name the q4_0 cache type (mi210-llm-stack page 1, "-ctk q4_0 -ctv q4_0") without
+ * defining it; the benchmark configurations give the scale d = max|x| / 8 and the element value
+ * (c - 8) * d. The rest is a reading: d is that quotient rounded to the nearest binary16, ties
+ * to even; an element's code is c = clamp(round_half_away(x / d) + 8, 0, 15) with x / d the
+ * correctly rounded f32 quotient (so the element +max|x| gives 16, clamped to 15); every code is
+ * 8 when d == 0. Source elements (f32, f16 or bf16) are widened exactly to f32 first; non-finite
+ * inputs and max|x| / 8 above the largest binary16 are outside the reading. */
+enum { ORC_SRC_F32 = 0, ORC_SRC_F16 = 1, ORC_SRC_BF16 = 2 };
+
+static void q4_0_quantize_block(const float *x, uint8_t *blk)
+{
+    float amax = 0.0f;
+    for (int t = 0; t < 32; ++t)
+        if (fabsf(x[t]) > amax)
+            amax = fabsf(x[t]);
+    const uint16_t dbits = float_to_half_bits_rne(amax / 8.0f);
+    const float d = half_bits_to_float(dbits);
+    int c[32];
+    for (int t = 0; t < 32; ++t) {
+        int v = 8;
+        if (d != 0.0f) {
+            v = (int)roundf(x[t] / d) + 8;
+            v = v < 0 ? 0 : (v > 15 ? 15 : v);
+        }
+        c[t] = v;
+    }
+    blk[0] = (uint8_t)(dbits & 0xFFu);
+    blk[1] = (uint8_t)(dbits >> 8);
+    for (int t = 0; t < 16; ++t)
+        blk[2 + t] = (uint8_t)(c[t] | (c[t + 16] << 4));
+}
+
+/* n_blocks blocks of 32 consecutive source elements -> n_blocks q4_0 blocks of 18 bytes. */
+int orc_quantize_q4_0(const void *x, int x_dtype, int64_t n_blocks, uint8_t *blocks)
+{
+    if (n_blocks < 0 || (n_blocks > 0 && (!x || !blocks)) ||
+        (x_dtype != ORC_SRC_F32 && x_dtype != ORC_SRC_F16 && x_dtype != ORC_SRC_BF16))
+        return ORC_ERR_ARG;
+    for (int64_t b = 0; b < n_blocks; ++b) {
+        float v[32];
+        for (int t = 0; t < 32; ++t) {
+            const int64_t e = 32 * b + t;
+            if (x_dtype == ORC_SRC_F32)
+                v[t] = ((const float *)x)[e];
+            else if (x_dtype == ORC_SRC_F16)
+                v[t] = half_bits_to_float(((const uint16_t *)x)[e]);
+            else
+                v[t] = bf16_bits_to_float(((const uint16_t *)x)[e]);
+        }
+        q4_0_quantize_block(v, blocks + 18 * b);
+    }
+    return ORC_OK;
+}
+
 /* Widen `rows` rows of D elements stored as `dtype` into a new f32 buffer. */
 static float *upcast_rows(const void *src, int dtype, int64_t rows, int D)
 {

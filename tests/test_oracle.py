@@ -306,6 +306,60 @@ def check_round_trip(orc):
     assert np.array_equal(again, blocks)
 
 
+# ---- q4_0 cache writer (quantize) ------------------------------------------------------------
+
+def check_quant_round_trip(orc):
+    """Blocks whose values are exactly (c - 8) d with a normal d and one code 0 (so max|x| = 8d)
+    quantize back to themselves: pins the scale rule, the code mapping and the packing."""
+    rng = np.random.default_rng(21)
+    n = 4000
+    d_bits = rng.integers(0x0400, 0x7800, size=n).astype(np.uint16)
+    codes = rng.integers(0, 16, size=(n, 32)).astype(np.uint8)
+    codes[np.arange(n), rng.integers(0, 32, size=n)] = 0
+    blocks = W.pack_q4_0_blocks(d_bits, codes)
+    f32, _ = orc.dequant_q4_0(blocks)
+    assert np.array_equal(orc.quantize_q4_0(f32, "f32"), blocks)
+
+
+def check_quant_hand_block(orc):
+    """A hand-built block with max|x| = 4 (so d = 0.5): ties (k + 1/2) d round away from zero,
+    +8d clamps to code 15, -8d is code 0, values inside round to the nearest code."""
+    x = np.zeros(32, np.float32)
+    x[0], x[1], x[2], x[3] = 1.25, -1.25, 0.25, -0.25       # +-2.5 d, +-0.5 d (ties)
+    x[4], x[5], x[6], x[7] = 4.0, -4.0, 0.74, -0.76         # +8d, -8d, 1.48 d, -1.52 d
+    x[16], x[17], x[18] = 3.75, -3.75, 2.0                   # +-7.5 d (ties), 4 d
+    codes = [11, 5, 9, 7, 15, 0, 9, 6] + [8] * 8 + [15, 0, 12] + [8] * 13
+    expect = np.zeros(18, np.uint8)
+    expect[0], expect[1] = 0x00, 0x38                        # f16 0.5 = 0x3800
+    for t in range(16):
+        expect[2 + t] = codes[t] | (codes[t + 16] << 4)
+    assert np.array_equal(orc.quantize_q4_0(x, "f32")[0], expect)
+
+
+def check_quant_zero_and_sources(orc):
+    """An all-zero block gives d = 0 and codes 8; the same values given as f32, f16 and bf16
+    (all exactly representable) give the same bytes."""
+    z = orc.quantize_q4_0(np.zeros(32, np.float32), "f32")[0]
+    assert np.array_equal(z, np.array([0, 0] + [0x88] * 16, np.uint8))
+    rng = np.random.default_rng(22)
+    v = (rng.integers(-64, 65, size=(64, 32)) * 2.0 ** rng.integers(-8, 3, size=(64, 1)))
+    v = v.astype(np.float32)
+    a = orc.quantize_q4_0(v, "f32")
+    b = orc.quantize_q4_0(v.astype(np.float16).view(np.uint16), "f16")
+    c = orc.quantize_q4_0((v.view(np.uint32) >> 16).astype(np.uint16), "bf16")
+    assert np.array_equal(a, b) and np.array_equal(a, c)
+
+
+def check_quant_matches_recipe(orc):
+    """The input recipe's numpy quantizer (an independent implementation of the same reading)
+    and the oracle agree byte for byte on N(0,1) data at several magnitudes, including blocks
+    whose scale is a binary16 subnormal."""
+    rng = np.random.default_rng(23)
+    x = rng.standard_normal((3000, 32), dtype=np.float32)
+    x *= (10.0 ** rng.uniform(-7, 3, size=(3000, 1))).astype(np.float32)
+    assert np.array_equal(orc.quantize_q4_0(x, "f32"), W.quantize_q4_0(x))
+
+
 ALL_CHECKS = (
     [(f"brute_force[{i}]", (lambda c: lambda o: check_brute_force(o, c))(c))
      for i, c in enumerate(BRUTE_CASES)]
@@ -321,7 +375,10 @@ ALL_CHECKS = (
        ("scale", check_scale_exponent), ("dominant_key", check_dominant_key),
        ("half_decode", check_half_decode), ("half_encode", check_half_encode),
        ("dequant_exhaustive", check_dequant_exhaustive), ("dequant_fixture", check_dequant_fixture),
-       ("round_trip", check_round_trip)])
+       ("round_trip", check_round_trip),
+       ("quant_round_trip", check_quant_round_trip), ("quant_hand_block", check_quant_hand_block),
+       ("quant_zero_sources", check_quant_zero_and_sources),
+       ("quant_recipe", check_quant_matches_recipe)])
 
 
 # ----------------------------------------------------------------------------------------
@@ -392,6 +449,12 @@ MUTANTS = [
     ("round to half away", "nearbyintf(ldexpf(a, 10 - k))", "roundf(ldexpf(a, 10 - k))"),
     ("query index", "const int64_t i = (r / p->Hq) % p->Sq;", "const int64_t i = (r / p->Hq) % p->Sk;"),
     ("max not taken", "if (prob[j] > m)\n            m = prob[j];", "if (prob[j] < m)\n            m = prob[j];"),
+    ("writer rounds half to even", "v = (int)roundf(x[t] / d) + 8;", "v = (int)nearbyintf(x[t] / d) + 8;"),
+    ("writer scale max/7", "float_to_half_bits_rne(amax / 8.0f)", "float_to_half_bits_rne(amax / 7.0f)"),
+    ("writer scale not rounded", "const float d = half_bits_to_float(dbits);", "const float d = amax / 8.0f;"),
+    ("writer nibbles swapped", "blk[2 + t] = (uint8_t)(c[t] | (c[t + 16] << 4));",
+     "blk[2 + t] = (uint8_t)(c[t + 16] | (c[t] << 4));"),
+    ("writer clamp at 16", "v = v < 0 ? 0 : (v > 15 ? 15 : v);", "v = v < 0 ? 0 : (v > 16 ? 16 : v);"),
 ]
 
 
