@@ -7,8 +7,8 @@ runs in the HIP kernels of libfa.so; there is no Python or CPU fallback, and if 
 missing every call raises.
 
 Raw entry points with the C names (pointers and ints): fa_prefill, fa_decode,
-fa_decode_workspace_bytes, fa_dequant_q4_0, fa_strerror, fa_version.
-Tensor helpers: prefill, decode, decode_workspace_bytes, dequant_q4_0.
+fa_decode_workspace_bytes, fa_dequant_q4_0, fa_quantize_q4_0, fa_strerror, fa_version.
+Tensor helpers: prefill, decode, decode_workspace_bytes, dequant_q4_0, quantize_q4_0.
 """
 from __future__ import annotations
 
@@ -19,6 +19,7 @@ from typing import Optional
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 
 FA_KV_F16, FA_KV_BF16, FA_KV_Q4_0 = 0, 1, 2
+FA_SRC_F32, FA_SRC_F16, FA_SRC_BF16 = 0, 1, 2
 Q4_0_BYTES = 18
 
 FA_OK = 0
@@ -32,7 +33,7 @@ FA_ERR_HIP = -7
 FA_ERR_VALUE = -8
 
 EXPORTS = ("fa_prefill", "fa_decode", "fa_decode_workspace_bytes", "fa_dequant_q4_0",
-           "fa_strerror", "fa_version")
+           "fa_quantize_q4_0", "fa_strerror", "fa_version")
 
 
 class FAError(RuntimeError):
@@ -63,6 +64,8 @@ def load() -> ctypes.CDLL:
         lib.fa_decode_workspace_bytes.restype = sz
         lib.fa_dequant_q4_0.argtypes = [vp, i64, vp, vp, vp]
         lib.fa_dequant_q4_0.restype = i32
+        lib.fa_quantize_q4_0.argtypes = [vp, i32, vp, i64, i64, i32, i64, i64, vp]
+        lib.fa_quantize_q4_0.restype = i32
         lib.fa_strerror.argtypes = [i32]
         lib.fa_strerror.restype = ctypes.c_char_p
         lib.fa_version.argtypes = []
@@ -91,6 +94,12 @@ def fa_decode_workspace_bytes(B, Hq, Hkv, Sq, Sk, D) -> int:
 
 def fa_dequant_q4_0(blocks, n_blocks, out_f32, out_f16, stream) -> int:
     return load().fa_dequant_q4_0(blocks, n_blocks, out_f32, out_f16, stream)
+
+
+def fa_quantize_q4_0(x, x_dtype, blocks, n_seq, rows_per_seq, D, x_seq_stride,
+                     blocks_seq_stride, stream) -> int:
+    return load().fa_quantize_q4_0(x, x_dtype, blocks, n_seq, rows_per_seq, D, x_seq_stride,
+                                   blocks_seq_stride, stream)
 
 
 def fa_strerror(code: int) -> str:
@@ -198,3 +207,32 @@ def dequant_q4_0(blocks, stream=None):
     if rc != FA_OK:
         raise FAError(rc, "fa_dequant_q4_0")
     return f32, f16
+
+
+def quantize_q4_0(x, out=None, stream=None):
+    """q4_0 cache writer via fa_quantize_q4_0: a contiguous float32 / float16 / bfloat16 tensor
+    [..., D] (D a multiple of 32) -> uint8 q4_0 blocks [..., D/32*18]. With `out` (a uint8 view
+    whose rows of D/32*18 bytes are contiguous within out's first dimension, e.g. the positions
+    [pos, pos + S_new) of a [B, Smax, Hkv, D/32*18] cache with x of [B, S_new, Hkv, D]) the
+    blocks are written there."""
+    torch = _torch()
+    codes = {torch.float32: FA_SRC_F32, torch.float16: FA_SRC_F16, torch.bfloat16: FA_SRC_BF16}
+    if x.dtype not in codes or not x.is_contiguous() or x.dim() < 1:
+        raise ValueError("x must be a contiguous float32, float16 or bfloat16 tensor")
+    D = x.shape[-1]
+    rowb = D // 32 * Q4_0_BYTES
+    if out is None:
+        out = torch.empty(*x.shape[:-1], rowb, dtype=torch.uint8, device=x.device)
+    if out.dtype != torch.uint8 or tuple(out.shape) != (*x.shape[:-1], rowb):
+        raise ValueError("out must be uint8 of x's shape with D/32*18 bytes last")
+    if not (out[0] if out.dim() > 1 else out).is_contiguous():
+        raise ValueError("out's rows must be contiguous within its first dimension")
+    n_seq = x.shape[0] if x.dim() > 1 else 1
+    rows = x.numel() // D // max(n_seq, 1) if x.numel() else 0
+    x_stride = x.stride(0) if x.dim() > 1 else x.numel()
+    o_stride = out.stride(0) if out.dim() > 1 else out.numel()
+    rc = fa_quantize_q4_0(x.data_ptr(), codes[x.dtype], out.data_ptr(), n_seq, rows, D,
+                          x_stride, o_stride, _stream(x, stream))
+    if rc != FA_OK:
+        raise FAError(rc, "fa_quantize_q4_0")
+    return out

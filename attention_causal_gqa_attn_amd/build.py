@@ -18,7 +18,7 @@ import tempfile
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libfa.so")
-SOURCES = ["fa_api.cpp", "fa_prefill16.hip", "fa_decode.hip", "fa_dequant.hip"]
+SOURCES = ["fa_api.cpp", "fa_prefill16.hip", "fa_decode.hip", "fa_dequant.hip", "fa_quant.hip"]
 ARCH = "gfx950"
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

@@ -169,6 +169,38 @@ int fa_dequant_q4_0(const void *blocks, int64_t n_blocks, float *out_f32, void *
                                               (hipStream_t)stream));
 }
 
+int fa_quantize_q4_0(const void *x, int x_dtype, void *blocks, int64_t n_seq,
+                     int64_t rows_per_seq, int D, int64_t x_seq_stride,
+                     int64_t blocks_seq_stride, fa_stream_t stream)
+{
+    if (x_dtype != FA_SRC_F32 && x_dtype != FA_SRC_F16 && x_dtype != FA_SRC_BF16)
+        return FA_ERR_DTYPE;
+    if (n_seq < 0 || rows_per_seq < 0 || D <= 0 || D % 32)
+        return FA_ERR_SHAPE;
+    if (rows_per_seq > INT64_MAX / D)
+        return FA_ERR_SHAPE;
+    const int64_t elems = rows_per_seq * D;             // per sequence
+    const int64_t per = elems / 32;                     // blocks per sequence
+    if (n_seq == 0 || per == 0)
+        return FA_OK;
+    if (per > INT64_MAX / n_seq || elems > INT64_MAX / 18)
+        return FA_ERR_SHAPE;
+    if (n_seq > 1 && (x_seq_stride < elems || blocks_seq_stride < per * 18 ||
+                      x_seq_stride > INT64_MAX / 4 / n_seq ||
+                      blocks_seq_stride > INT64_MAX / n_seq))
+        return FA_ERR_SHAPE;
+    if (!x || !blocks)
+        return FA_ERR_NULL;
+    const int64_t esz = x_dtype == FA_SRC_F32 ? 4 : 2;
+    if (!aligned(x, 16) || (n_seq > 1 && (x_seq_stride * esz) % 16) || !aligned(blocks, 2) ||
+        (n_seq > 1 && blocks_seq_stride % 2))
+        return FA_ERR_ALIGN;
+    if ((n_seq * per + 255) / 256 > kMaxWorkgroups)
+        return FA_ERR_UNSUPPORTED;
+    return hip_status(fa::launch_quantize_q4_0(x, x_dtype, blocks, n_seq, per, x_seq_stride,
+                                               blocks_seq_stride, (hipStream_t)stream));
+}
+
 const char *fa_strerror(int code)
 {
     switch (code) {

@@ -47,5 +47,9 @@ hipError_t launch_decode(const AttnArgs &a, const DecodeGrid &g, void *workspace
 
 hipError_t launch_dequant_q4_0(const void *blocks, int64_t n_blocks, float *out_f32,
                                void *out_f16, hipStream_t stream);
+// src: 0 f32, 1 f16, 2 bf16 (fa_src_dtype)
+hipError_t launch_quantize_q4_0(const void *x, int src, void *blocks, int64_t n_seq,
+                                int64_t blocks_per_seq, int64_t x_seq_stride,
+                                int64_t blk_seq_stride, hipStream_t stream);
 
 }  // namespace fa

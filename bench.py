@@ -7,7 +7,9 @@ One step = one pass of the whole path over resident inputs:
     (fa_decode, split kernel + merge kernel);
   * the same prefill against a q4_0 cache (fa_prefill, dequantization in the kernel), and
     the unfused arm beside it: fa_dequant_q4_0 of K and V into f16 buffers, then the f16
-    fa_prefill (reported, not part of `value`).
+    fa_prefill (reported, not part of `value`);
+  * the q4_0 cache writer: fa_quantize_q4_0 of the prefill workload's f16 K and V (16384
+    keys x 8 heads x 128) into q4_0 blocks (reported, HBM-bound).
 Before each call a 1 GiB buffer is read so that neither call finds its inputs in the 256 MB
 last-level cache (the decode working set, 151 MB, would otherwise stay resident). The flush
 reads rather than writes: a written flush leaves up to 256 MB of dirty lines in that cache,
@@ -169,6 +171,9 @@ def main():
     kf = torch.empty(wq.B, wq.Sk, wq.Hkv, wq.D, dtype=torch.float16, device=dev)
     vf = torch.empty_like(kf)
     q_blocks = qk.numel() // 18
+    wk = torch.empty(pk.numel() // 32 * 18, dtype=torch.uint8, device=dev)
+    wv = torch.empty_like(wk)
+    wbytes = (pk.numel() + pv.numel()) * 2 + wk.numel() + wv.numel()
     ws = torch.empty(max(16, fa.decode_workspace_bytes(wd.B, wd.Hq, wd.Hkv, wd.Sq, wd.Sk, wd.D)),
                      dtype=torch.uint8, device=dev)
     # float32, so sum() is one reduction kernel that only reads (an int32 sum would first
@@ -198,7 +203,11 @@ def main():
         fa.prefill(qq, kf, vf, causal=True, offset=wq.causal_offset, scale=wq.scale, out=qo2,
                    stream=stream)
 
-    calls = [prefill, decode, prefill_q4, prefill_q4_unfused]
+    def quantize():
+        fa.quantize_q4_0(pk.view(-1, wp.D), out=wk.view(-1, wp.D // 32 * 18), stream=stream)
+        fa.quantize_q4_0(pv.view(-1, wp.D), out=wv.view(-1, wp.D // 32 * 18), stream=stream)
+
+    calls = [prefill, decode, prefill_q4, prefill_q4_unfused, quantize]
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * len(calls))]
           for _ in range(args.steps)]
 
@@ -232,6 +241,7 @@ def main():
     d_ms = np.array([e[2].elapsed_time(e[3]) for e in ev])
     q_ms = np.array([e[4].elapsed_time(e[5]) for e in ev])
     u_ms = np.array([e[6].elapsed_time(e[7]) for e in ev])
+    w_ms = np.array([e[8].elapsed_time(e[9]) for e in ev])
     qflops = W.attention_flops(wq)
     flops = W.attention_flops(wp)
     dbytes = W.algorithmic_bytes(wd)
@@ -288,6 +298,13 @@ def main():
                                  "what": "fa_dequant_q4_0 of K and V to f16 buffers (two "
                                          "launches), then the f16 fa_prefill",
                                  "extra_bytes": int(kf.numel() * 2 * 2)},
+        "quantize_q4_0": {"what": "fa_quantize_q4_0 of f16 K and V [1, 16384, 8, 128] (two "
+                                  "launches)",
+                          "gbs": round(wbytes / (float(w_ms.mean()) * 1e-3) / 1e9, 1),
+                          "ms_mean": round(float(w_ms.mean()), 5),
+                          "bytes": int(wbytes),
+                          "frac_of_hbm_peak": round(wbytes / (float(w_ms.mean()) * 1e-3) / 1e9
+                                                    / PEAK_HBM_GBS, 4)},
         "source_hash": source_hash(),
     }
     if not args.no_cpu_baseline:

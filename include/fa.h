@@ -57,7 +57,7 @@ enum fa_status {
     FA_OK = 0,
     FA_ERR_NULL = -1,         /* a required pointer is NULL */
     FA_ERR_SHAPE = -2,        /* negative size, Hq % Hkv != 0, or an index that overflows */
-    FA_ERR_DTYPE = -3,        /* kv_dtype is not one of enum fa_kv_dtype */
+    FA_ERR_DTYPE = -3,        /* kv_dtype (x_dtype) not one of enum fa_kv_dtype (fa_src_dtype) */
     FA_ERR_UNSUPPORTED = -4,  /* valid but not built: D not in {64, 128}; decode rows > 16 */
     FA_ERR_WORKSPACE = -5,    /* decode workspace missing or smaller than required */
     FA_ERR_ALIGN = -6,        /* Q/O/K/V not 16-byte aligned (q4_0 K/V: 4-byte aligned) */
@@ -110,6 +110,40 @@ int fa_decode(const void *q, const void *k, const void *v, void *o,
  */
 int fa_dequant_q4_0(const void *blocks, int64_t n_blocks, float *out_f32, void *out_f16,
                     fa_stream_t stream);
+
+/* Source element types of fa_quantize_q4_0. */
+enum fa_src_dtype {
+    FA_SRC_F32 = 0,
+    FA_SRC_F16 = 1,
+    FA_SRC_BF16 = 2,
+};
+
+/*
+ * q4_0 cache writer, the step before the attention path: a new chunk's K and V rows are
+ * quantized into the q4_0 cache the kernels read (the q4_0 KV cache of mi210-llm-stack,
+ * "FlashAttention on gfx90a", "-ctk q4_0 -ctv q4_0"). Per 32 consecutive elements:
+ * d = max|x| / 8 rounded to the nearest f16 (ties to even); element code
+ * c = clamp(round_half_away(x / d) + 8, 0, 15) with x / d the correctly rounded f32 quotient
+ * (so +max|x| gives 16, clamped to 15); every code is 8 when d = 0. The block is d (2 bytes,
+ * little endian) then 16 bytes, byte t = c[t] | c[t + 16] << 4.
+ *   x         device pointer to x_dtype elements: n_seq sequences of rows_per_seq rows of D
+ *             elements (D > 0, a multiple of 32); sequence s starts at element
+ *             s * x_seq_stride and its rows are contiguous. 16-byte aligned, and
+ *             x_seq_stride * element size a multiple of 16.
+ *   blocks    device pointer: sequence s's rows start at byte s * blocks_seq_stride and are
+ *             contiguous, D / 32 * 18 bytes each. 2-byte aligned, blocks_seq_stride even.
+ *             An append of S_new positions at pos to a [B, Smax, Hkv, D/32] q4_0 cache is
+ *             blocks = cache + pos * Hkv * row bytes, n_seq = B, rows_per_seq = S_new * Hkv,
+ *             blocks_seq_stride = Smax * Hkv * row bytes.
+ * With n_seq > 1 each stride must cover a sequence (x_seq_stride >= rows_per_seq * D,
+ * blocks_seq_stride >= rows_per_seq * D / 32 * 18). Elements must be finite, with max|x| / 8
+ * inside the f16 range. Asynchronous on stream; the caller owns both buffers.
+ * Returns FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_DTYPE, FA_ERR_ALIGN, FA_ERR_UNSUPPORTED
+ * (more blocks than one launch takes) or FA_ERR_HIP.
+ */
+int fa_quantize_q4_0(const void *x, int x_dtype, void *blocks, int64_t n_seq,
+                     int64_t rows_per_seq, int D, int64_t x_seq_stride,
+                     int64_t blocks_seq_stride, fa_stream_t stream);
 
 /* Static text for a status code. */
 const char *fa_strerror(int code);

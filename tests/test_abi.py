@@ -138,6 +138,29 @@ def test_dequant_rejects():
     assert fa.fa_dequant_q4_0(P, 4, P + 2, P, None) == fa.FA_ERR_ALIGN
 
 
+def test_quantize_rejects():
+    q = fa.fa_quantize_q4_0
+    # (x, x_dtype, blocks, n_seq, rows_per_seq, D, x_seq_stride, blocks_seq_stride, stream)
+    assert q(P, 3, P, 1, 1, 32, 0, 0, None) == fa.FA_ERR_DTYPE
+    assert q(P, -1, P, 1, 1, 32, 0, 0, None) == fa.FA_ERR_DTYPE
+    assert q(P, 1, P, 1, 1, 48, 0, 0, None) == fa.FA_ERR_SHAPE          # D % 32
+    assert q(P, 1, P, 1, 1, 0, 0, 0, None) == fa.FA_ERR_SHAPE
+    assert q(P, 1, P, -1, 1, 32, 0, 0, None) == fa.FA_ERR_SHAPE
+    assert q(P, 1, P, 1, -1, 32, 0, 0, None) == fa.FA_ERR_SHAPE
+    assert q(P, 1, P, 2, 4, 32, 64, 72, None) == fa.FA_ERR_SHAPE        # x stride < 4 rows
+    assert q(P, 1, P, 2, 4, 32, 128, 70, None) == fa.FA_ERR_SHAPE       # block stride < 72
+    assert q(P, 1, P, 2, 1 << 40, 1 << 20, 1 << 62, 1 << 60, None) == fa.FA_ERR_SHAPE
+    assert q(None, 1, P, 1, 1, 32, 0, 0, None) == fa.FA_ERR_NULL
+    assert q(P, 1, None, 1, 1, 32, 0, 0, None) == fa.FA_ERR_NULL
+    assert q(ODD, 1, P, 1, 1, 32, 0, 0, None) == fa.FA_ERR_ALIGN        # x not 16-byte aligned
+    assert q(P, 1, P + 1, 1, 1, 32, 0, 0, None) == fa.FA_ERR_ALIGN     # blocks odd
+    assert q(P, 1, P, 2, 1, 32, 36, 18, None) == fa.FA_ERR_ALIGN       # 72-byte x stride
+    assert q(P, 1, P, 2, 1, 32, 44, 18, None) == fa.FA_ERR_ALIGN       # 88-byte x stride
+    assert q(P, 1, P, 2, 1, 32, 32, 19, None) == fa.FA_ERR_ALIGN       # odd block stride
+    assert q(None, 1, None, 0, 5, 32, 0, 0, None) == fa.FA_OK          # nothing to do
+    assert q(None, 1, None, 3, 0, 32, 0, 0, None) == fa.FA_OK
+
+
 def test_binding_refuses_without_library(monkeypatch, tmp_path):
     """The product path fails loudly when the HIP library is missing: no fallback."""
     monkeypatch.setattr(fa, "_lib", None)

@@ -149,6 +149,69 @@ def test_q4_0_prefill_fused_equals_unfused():
 
 
 # ---------------------------------------------------------------------------------------------
+# q4_0 cache writer: bit-exact against the oracle's quantizer
+# ---------------------------------------------------------------------------------------------
+
+def _writer_blocks(n_blocks, seed):
+    """N(0,1) blocks at magnitudes 1e-6 .. 1e3, plus a zero block, a block of ties and clamps
+    ((k + 1/2) d, +-8 d with d = 0.5), one with a binary16-subnormal scale, one of equal
+    magnitudes."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((n_blocks, 32), dtype=np.float32)
+    x *= (10.0 ** rng.uniform(-6, 3, size=(n_blocks, 1))).astype(np.float32)
+    x[0] = 0.0
+    x[1] = 0.0
+    x[1, :8] = [1.25, -1.25, 0.25, -0.25, 4.0, -4.0, 0.74, -0.76]
+    x[2] = (1e-6 * rng.standard_normal(32)).astype(np.float32)
+    x[3] = 3.0
+    x[3, 5] = -3.0
+    return x
+
+
+def _src_bits(x, src):
+    """Source elements as the oracle takes them (float32, or uint16 bit patterns)."""
+    if src == "f32":
+        return x
+    if src == "f16":
+        return x.astype(np.float16).view(np.uint16)
+    return (x.view(np.uint32) >> 16).astype(np.uint16)      # bf16 by truncation: any bf16
+
+
+def _src_dev(bits, src):
+    if src == "f16":
+        return to_dev(bits.view(np.float16), "f16")
+    return to_dev(bits, src)
+
+
+def test_quantize_q4_0_matches_oracle():
+    for src in ("f32", "f16", "bf16"):
+        say(f"q4_0 writer, {src} source")
+        bits = _src_bits(_writer_blocks(20003, seed=71), src)
+        expect = oracle.quantize_q4_0(bits, src)
+        got = fa.quantize_q4_0(_src_dev(bits, src).view(-1, 32))
+        torch.cuda.synchronize()
+        assert np.array_equal(got.cpu().numpy(), expect), src
+
+
+def test_quantize_q4_0_appends_into_cache():
+    """An append of S_new = 7 positions at pos = 11 of a [3, 50, 2, 72-byte] q4_0 cache writes
+    exactly those rows, and every other byte of the cache is untouched."""
+    B, Smax, Hkv, D, pos, S_new = 3, 50, 2, 128, 11, 7
+    say("q4_0 writer append into a cache slice")
+    x = _writer_blocks(B * S_new * Hkv * D // 32, seed=72).reshape(B, S_new, Hkv, D)
+    bits = _src_bits(x, "f16")
+    cache = torch.full((B, Smax, Hkv, D // 32 * 18), 0xAB, dtype=torch.uint8, device="cuda")
+    fa.quantize_q4_0(_src_dev(bits, "f16"), out=cache[:, pos:pos + S_new])
+    torch.cuda.synchronize()
+    host = cache.cpu().numpy()
+    expect = oracle.quantize_q4_0(bits, "f16").reshape(B, S_new, Hkv, D // 32 * 18)
+    assert np.array_equal(host[:, pos:pos + S_new], expect)
+    rest = np.ones(Smax, bool)
+    rest[pos:pos + S_new] = False
+    assert np.all(host[:, rest] == 0xAB)
+
+
+# ---------------------------------------------------------------------------------------------
 # decode (split-K + log-sum-exp merge)
 # ---------------------------------------------------------------------------------------------
 
