@@ -7,8 +7,10 @@ runs in the HIP kernels of libfa.so; there is no Python or CPU fallback, and if 
 missing every call raises.
 
 Raw entry points with the C names (pointers and ints): fa_prefill, fa_decode,
-fa_decode_workspace_bytes, fa_dequant_q4_0, fa_quantize_q4_0, fa_strerror, fa_version.
-Tensor helpers: prefill, decode, decode_workspace_bytes, dequant_q4_0, quantize_q4_0.
+fa_decode_paged, fa_decode_workspace_bytes, fa_dequant_q4_0, fa_quantize_q4_0, fa_strerror,
+fa_version.
+Tensor helpers: prefill, decode, decode_paged, decode_workspace_bytes, dequant_q4_0,
+quantize_q4_0.
 """
 from __future__ import annotations
 
@@ -32,8 +34,9 @@ FA_ERR_ALIGN = -6
 FA_ERR_HIP = -7
 FA_ERR_VALUE = -8
 
-EXPORTS = ("fa_prefill", "fa_decode", "fa_decode_workspace_bytes", "fa_dequant_q4_0",
-           "fa_quantize_q4_0", "fa_strerror", "fa_version")
+EXPORTS = ("fa_prefill", "fa_decode", "fa_decode_paged", "fa_decode_workspace_bytes",
+           "fa_dequant_q4_0", "fa_quantize_q4_0", "fa_strerror", "fa_version")
+PAGE_KEYS = 64
 
 
 class FAError(RuntimeError):
@@ -60,6 +63,9 @@ def load() -> ctypes.CDLL:
         lib.fa_prefill.restype = i32
         lib.fa_decode.argtypes = attn + [vp, sz, vp]
         lib.fa_decode.restype = i32
+        lib.fa_decode_paged.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
+                                        i32, i32, f32, i32, vp, sz, vp]
+        lib.fa_decode_paged.restype = i32
         lib.fa_decode_workspace_bytes.argtypes = [i32] * 6
         lib.fa_decode_workspace_bytes.restype = sz
         lib.fa_dequant_q4_0.argtypes = [vp, i64, vp, vp, vp]
@@ -94,6 +100,14 @@ def fa_decode_workspace_bytes(B, Hq, Hkv, Sq, Sk, D) -> int:
 
 def fa_dequant_q4_0(blocks, n_blocks, out_f32, out_f16, stream) -> int:
     return load().fa_dequant_q4_0(blocks, n_blocks, out_f32, out_f16, stream)
+
+
+def fa_decode_paged(q, k_pages, v_pages, o, block_table, seq_lens, B, Hq, Hkv, Sq, D,
+                    max_pages, n_pages, causal, scale, kv_dtype, workspace, workspace_bytes,
+                    stream) -> int:
+    return load().fa_decode_paged(q, k_pages, v_pages, o, block_table, seq_lens, B, Hq, Hkv, Sq,
+                                  D, max_pages, n_pages, causal, scale, kv_dtype, workspace,
+                                  workspace_bytes, stream)
 
 
 def fa_quantize_q4_0(x, x_dtype, blocks, n_seq, rows_per_seq, D, x_seq_stride,
@@ -191,6 +205,39 @@ def decode(q, k, v, *, causal: bool = True, offset: Optional[int] = None,
                    workspace.numel() * workspace.element_size(), _stream(q, stream))
     if rc != FA_OK:
         raise FAError(rc, "fa_decode")
+    return out
+
+
+def decode_paged(q, k_pages, v_pages, block_table, seq_lens, *, causal: bool = True,
+                 scale: Optional[float] = None, out=None, workspace=None, stream=None):
+    """Split-K decode over paged caches via fa_decode_paged. k_pages, v_pages: [n_pages, 64,
+    Hkv, D] (q4_0: uint8 [n_pages, 64, Hkv, D/32*18]); block_table: int32 [B, max_pages];
+    seq_lens: int32 [B]. Sequence b's Sq queries are its last Sq positions."""
+    torch = _torch()
+    kv = _kv_code(k_pages)
+    if block_table.dtype != torch.int32 or seq_lens.dtype != torch.int32:
+        raise ValueError("block_table and seq_lens must be int32")
+    if not (block_table.is_contiguous() and seq_lens.is_contiguous()) or block_table.dim() != 2:
+        raise ValueError("block_table must be a contiguous [B, max_pages] tensor")
+    if k_pages.dim() != 4 or k_pages.shape[1] != PAGE_KEYS or q.dim() != 4:
+        raise ValueError("pages must be [n_pages, 64, Hkv, row]; q [B, Sq, Hq, D]")
+    B, Sq, Hq, D = q.shape
+    n_pages, _, Hkv, _ = k_pages.shape
+    max_pages = block_table.shape[1]
+    if block_table.shape[0] != B or seq_lens.numel() != B or v_pages.shape != k_pages.shape:
+        raise ValueError("block_table, seq_lens and pages disagree with q")
+    scale = D ** -0.5 if scale is None else float(scale)
+    if out is None:
+        out = torch.empty_like(q)
+    if workspace is None:
+        nbytes = decode_workspace_bytes(B, Hq, Hkv, Sq, max_pages * PAGE_KEYS, D)
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    rc = fa_decode_paged(q.data_ptr(), k_pages.data_ptr(), v_pages.data_ptr(), out.data_ptr(),
+                         block_table.data_ptr(), seq_lens.data_ptr(), B, Hq, Hkv, Sq, D,
+                         max_pages, n_pages, int(bool(causal)), scale, kv, workspace.data_ptr(),
+                         workspace.numel() * workspace.element_size(), _stream(q, stream))
+    if rc != FA_OK:
+        raise FAError(rc, "fa_decode_paged")
     return out
 
 

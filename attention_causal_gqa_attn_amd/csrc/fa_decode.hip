@@ -29,9 +29,47 @@ namespace {
 struct DecodeParams {
     AttnArgs a;
     int rows, n_split, split_len;
-    int64_t kend;          // keys any row can see: [0, kend)
+    int64_t kend;          // keys any row can see: [0, kend) (contiguous caches)
     float *part;           // [B][Hkv][n_split][rows][D + 2]
+    // paged caches (block_table != nullptr): K and V are n_pages pages of kBN keys, each
+    // [kBN][Hkv][row]; key j of sequence b is key j % kBN of page block_table[b * max_pages +
+    // j / kBN]; sequence b has seq_lens[b] keys and its Sq queries are its last Sq positions
+    const int32_t *block_table, *seq_lens;
+    int max_pages, n_pages;
 };
+
+// One sequence's keys: how many it has, how many its rows can see ([0, kend)), and the
+// absolute position of its query 0.
+struct SeqView {
+    int64_t Sk, kend, offset;
+};
+__device__ __forceinline__ SeqView seq_view(const DecodeParams &p, int b)
+{
+    const AttnArgs &a = p.a;
+    if (!p.block_table)
+        return SeqView{a.Sk, p.kend, a.offset};
+    const int64_t sk = min(max((int64_t)p.seq_lens[b], (int64_t)0), (int64_t)p.max_pages * kBN);
+    return SeqView{sk, sk, sk - a.Sq};
+}
+// Byte offset of (b, key 0, KV head kvh) in K or V: contiguous caches are [B, Sk, Hkv, row];
+// pages are shared by every sequence.
+__device__ __forceinline__ int64_t head_off(const DecodeParams &p, int b, int kvh, int rowb)
+{
+    const AttnArgs &a = p.a;
+    return p.block_table ? (int64_t)kvh * rowb : ((int64_t)b * a.Sk * a.Hkv + kvh) * rowb;
+}
+// Byte offset from the head's key-0 row to the 64-key tile at key k0 (a multiple of kBN); rows
+// inside a tile are grow bytes apart in both layouts. A page index outside the page array is
+// clamped into it: the result is then wrong, but every load stays inside the buffers.
+__device__ __forceinline__ int64_t tile_off(const DecodeParams &p, int b, int64_t k0,
+                                            uint32_t grow)
+{
+    if (!p.block_table)
+        return k0 * grow;
+    int pg = p.block_table[(int64_t)b * p.max_pages + k0 / kBN];
+    pg = min(max(pg, 0), p.n_pages - 1);
+    return (int64_t)pg * kBN * grow;
+}
 
 // One 64-key tile of the split: each wave takes 16 keys.
 template <int D, bool BF>
@@ -174,9 +212,10 @@ __global__ __launch_bounds__(kThreads, kDecodeOccupancy<KV>) void decode_split_k
     rest /= a.Hkv;
     const int s = rest % p.n_split;
     const int b = rest / p.n_split;
+    const SeqView sv = seq_view(p, b);
 
     const int64_t ks = (int64_t)s * p.split_len;
-    const int64_t ke = min(ks + p.split_len, p.kend);
+    const int64_t ke = min(ks + p.split_len, sv.kend);
     const int nb = ke > ks ? (int)((ke - ks + kBN - 1) / kBN) : 0;
 
     // row r = qi * G + hl; rows >= p.rows are padding
@@ -186,7 +225,7 @@ __global__ __launch_bounds__(kThreads, kDecodeOccupancy<KV>) void decode_split_k
     const int h = kvh * a.G + hl;
     int64_t rowlim = ke - 1;                        // last key this row may see in the split
     if (a.causal)
-        rowlim = min(rowlim, (int64_t)qi + a.offset);
+        rowlim = min(rowlim, (int64_t)qi + sv.offset);
     if (!row_on)
         rowlim = -1;
 
@@ -212,7 +251,9 @@ __global__ __launch_bounds__(kThreads, kDecodeOccupancy<KV>) void decode_split_k
     TileLoader<D, KV> ld[NSETS];
 #pragma unroll
     for (int u = 0; u < NSETS; ++u)
-        ld[u].init(a.k, a.v, (int64_t)b * a.Sk * a.Hkv + kvh, a.Hkv, a.Sk, t);
+        ld[u].init(a.k, a.v, head_off(p, b, kvh, D * 2) / (D * 2), a.Hkv, (int)sv.Sk, t);
+    const uint32_t grow = (uint32_t)a.Hkv * D * 2;
+    auto load_set = [&](int u, int k0) { ld[u].load(k0, tile_off(p, b, k0, grow)); };
     uint16_t *lk = lds, *lv = lds + Geo::kElems;
     int kb0 = 0;
     if (nb >= 2 * NSETS) {
@@ -221,13 +262,13 @@ __global__ __launch_bounds__(kThreads, kDecodeOccupancy<KV>) void decode_split_k
         // waits only for set u, not for the sets issued after it.
 #pragma unroll
         for (int u = 0; u < NSETS; ++u)
-            ld[u].load((int)ks + u * kBN);
+            load_set(u, (int)ks + u * kBN);
         for (; kb0 + 2 * NSETS <= nb; kb0 += NSETS) {
 #pragma unroll
             for (int u = 0; u < NSETS; ++u) {
                 ld[u].store(lk, lv);
                 __syncthreads();
-                ld[u].load((int)ks + (kb0 + u + NSETS) * kBN);
+                load_set(u, (int)ks + (kb0 + u + NSETS) * kBN);
                 decode_tile<D, BF>(lk, lv, (int)ks + (kb0 + u) * kBN, wave, quad, r, rowlim,
                                    a.c, qf, acc, frame, lsum);
                 __syncthreads();
@@ -237,7 +278,7 @@ __global__ __launch_bounds__(kThreads, kDecodeOccupancy<KV>) void decode_split_k
 #pragma unroll
         for (int u = 0; u < NSETS; ++u)
             if (u < nb)
-                ld[u].load((int)ks + u * kBN);
+                load_set(u, (int)ks + u * kBN);
     }
     // tail: the last tiles (their loads are already in flight), loading only what exists
     for (; kb0 < nb; kb0 += NSETS) {
@@ -248,7 +289,7 @@ __global__ __launch_bounds__(kThreads, kDecodeOccupancy<KV>) void decode_split_k
                 ld[u].store(lk, lv);
                 __syncthreads();
                 if (kb + NSETS < nb)
-                    ld[u].load((int)ks + (kb + NSETS) * kBN);
+                    load_set(u, (int)ks + (kb + NSETS) * kBN);
                 decode_tile<D, BF>(lk, lv, (int)ks + kb * kBN, wave, quad, r, rowlim, a.c, qf,
                                    acc, frame, lsum);
                 __syncthreads();
@@ -306,9 +347,10 @@ __global__ __launch_bounds__(kThreads, 2) void decode_q4_kernel(DecodeParams p)
     rest /= a.Hkv;
     const int s = rest % p.n_split;
     const int b = rest / p.n_split;
+    const SeqView sv = seq_view(p, b);
 
     const int64_t ks = (int64_t)s * p.split_len;
-    const int64_t ke = min(ks + p.split_len, p.kend);
+    const int64_t ke = min(ks + p.split_len, sv.kend);
     const int nb = ke > ks ? (int)((ke - ks + kBN - 1) / kBN) : 0;
 
     const bool row_on = r < p.rows;
@@ -317,7 +359,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_q4_kernel(DecodeParams p)
     const int h = kvh * a.G + hl;
     int64_t rowlim = ke - 1;
     if (a.causal)
-        rowlim = min(rowlim, (int64_t)qi + a.offset);
+        rowlim = min(rowlim, (int64_t)qi + sv.offset);
     if (!row_on)
         rowlim = -1;
 
@@ -339,7 +381,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_q4_kernel(DecodeParams p)
 
     // ---- transfers: this wave's m-th transfer of a tile is i = min(wave + 4 m, NI - 1) -----
     const uint32_t grow = (uint32_t)a.Hkv * LD::ROWB;            // bytes between keys
-    const int64_t head0 = ((int64_t)b * a.Sk * a.Hkv + kvh) * LD::ROWB;
+    const int64_t head0 = head_off(p, b, kvh, LD::ROWB);
     const uint8_t *kg = (const uint8_t *)a.k + head0, *vg = (const uint8_t *)a.v + head0;
     const uint32_t raw0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t *)raw;
     uint32_t crow[NIW], ccol[NIW];
@@ -353,13 +395,14 @@ __global__ __launch_bounds__(kThreads, 2) void decode_q4_kernel(DecodeParams p)
     }
     auto dma_tile = [&](int kb) {
         const int k0 = (int)ks + kb * kBN;
-        const uint32_t last = (uint32_t)min(kBN - 1, a.Sk - 1 - k0);
+        const uint32_t last = (uint32_t)min((int64_t)kBN - 1, sv.Sk - 1 - k0);
         const uint32_t stage = raw0 + (uint32_t)((kb % kRS) * 2 * RAW_T);
+        const int64_t toff = tile_off(p, b, k0, grow);
 #pragma unroll
         for (int m = 0; m < NIW; ++m) {
             const int i = min(wave + 4 * m, NI - 1);
             const bool is_v = i >= ST;
-            const uint8_t *gt = (is_v ? vg : kg) + (int64_t)k0 * grow;
+            const uint8_t *gt = (is_v ? vg : kg) + toff;
             const uint32_t lbase = stage + (uint32_t)((is_v ? RAW_T : 0) + (i % ST) * 64 * 16);
             dma12(gt, min(crow[m], last) * grow + ccol[m],
                   __builtin_amdgcn_readfirstlane(lbase));
@@ -374,8 +417,8 @@ __global__ __launch_bounds__(kThreads, 2) void decode_q4_kernel(DecodeParams p)
         asm volatile("s_barrier" ::: "memory");
     };
 
-    LD ld;
-    ld.init(a.k, a.v, (int64_t)b * a.Sk * a.Hkv + kvh, a.Hkv, a.Sk, t);
+    LD ld;                                          // its raw-stage reads and f16 stores only
+    ld.init(a.k, a.v, 0, a.Hkv, (int)sv.Sk, t);
     uint16_t *lk = lds, *lv = lds + Geo::kElems;
     if (nb > 0)
         dma_tile(0);
@@ -476,7 +519,7 @@ struct Q4Head {
     // Query rows j = lane % 4 (qi * G + hl; rows >= p.rows are padding, computed and never
     // written) of KV head kvh of batch b, over keys below ke.
     __device__ __forceinline__ void init(const DecodeParams &p, int b, int kvh, int64_t ke,
-                                         int lane_)
+                                         int64_t offset, int lane_)
     {
         const AttnArgs &a = p.a;
         lane = lane_;
@@ -487,12 +530,12 @@ struct Q4Head {
         const int h = kvh * a.G + hl;
         rowlim = ke - 1;
         if (a.causal)
-            rowlim = min(rowlim, (int64_t)qi + a.offset);
+            rowlim = min(rowlim, (int64_t)qi + offset);
         if (!row_on)
             rowlim = -1;
         lim0 = ke - 1;                              // smallest limit of a real row (row 0)
         if (a.causal)
-            lim0 = min(lim0, a.offset);
+            lim0 = min(lim0, offset);
 
         // B operands of the score MFMAs: row j of q in the k order of the A operands. Code
         // dword pp of block bb holds bytes 4 pp .. 4 pp + 3; masked as in scores() its slots
@@ -793,18 +836,19 @@ __global__ __launch_bounds__(kThreads, Q4G<D>::OCC) void decode_q4g_kernel(Decod
     const int s = rest % p.n_split;
     const int b = rest / p.n_split;
     const int kvh = grp * G::NH + wave;
+    const SeqView sv = seq_view(p, b);
 
     const int64_t ks = (int64_t)s * p.split_len;
-    const int64_t ke = min(ks + p.split_len, p.kend);
+    const int64_t ke = min(ks + p.split_len, sv.kend);
     const int nb = ke > ks ? (int)((ke - ks + kBN - 1) / kBN) : 0;
 
     H hd;
-    hd.init(p, b, kvh, ke, lane);
+    hd.init(p, b, kvh, ke, sv.offset, lane);
 
     // transfers: this wave's m-th of a tile is i = min(wave + 4 m, NI - 1); i < S moves K slot
     // column i (slots 64 i .. 64 i + 63 of the tile), else V column i - S
     const uint32_t grow = (uint32_t)a.Hkv * G::ROWB;                    // bytes between keys
-    const int64_t g0 = ((int64_t)b * a.Sk * a.Hkv + grp * G::NH) * G::ROWB;
+    const int64_t g0 = head_off(p, b, grp * G::NH, G::ROWB);
     const uint8_t *kgl = (const uint8_t *)a.k + g0, *vgl = (const uint8_t *)a.v + g0;
     const uint32_t lds0 = __builtin_amdgcn_readfirstlane(
         (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t *)lds);
@@ -818,13 +862,14 @@ __global__ __launch_bounds__(kThreads, Q4G<D>::OCC) void decode_q4g_kernel(Decod
     }
     auto dma_tile = [&](int kb) {
         const int64_t k0 = ks + (int64_t)kb * kBN;
-        const uint32_t last = (uint32_t)min((int64_t)kBN - 1, (int64_t)a.Sk - 1 - k0);
+        const uint32_t last = (uint32_t)min((int64_t)kBN - 1, sv.Sk - 1 - k0);
         const uint32_t st = lds0 + (uint32_t)((kb % NSTG) * G::STAGE);
+        const int64_t toff = tile_off(p, b, k0, grow);
 #pragma unroll
         for (int m = 0; m < NIW; ++m) {
             const int i = min(wave + 4 * m, G::NI - 1);
             const bool is_v = i >= S;
-            dma16x((is_v ? vgl : kgl) + k0 * grow, min(crow[m], last) * grow + ccol[m],
+            dma16x((is_v ? vgl : kgl) + toff, min(crow[m], last) * grow + ccol[m],
                    __builtin_amdgcn_readfirstlane(st + (uint32_t)((is_v ? G::TB : 0) +
                                                                   (i % S) * 1024)));
         }
@@ -915,18 +960,19 @@ __global__ __launch_bounds__(kThreads, 2) void decode_q4w_kernel(DecodeParams p)
     rest /= a.Hkv;
     const int s = rest % p.n_split;
     const int b = rest / p.n_split;
+    const SeqView sv = seq_view(p, b);
 
     const int64_t ks = (int64_t)s * p.split_len;
-    const int64_t ke = min(ks + p.split_len, p.kend);
+    const int64_t ke = min(ks + p.split_len, sv.kend);
     const int nb = ke > ks ? (int)((ke - ks + kBN - 1) / kBN) : 0;
     const int ni = nb > wave ? (nb - wave + 3) / 4 : 0;      // tiles wave + 4 i, i < ni
 
     H hd;
-    hd.init(p, b, kvh, ke, lane);
+    hd.init(p, b, kvh, ke, sv.offset, lane);
 
     // transfers: lane offsets of the first NV dword transfers of a tensor tile
     const uint32_t grow = (uint32_t)a.Hkv * W::ROWB;                    // bytes between keys
-    const int64_t head0 = ((int64_t)b * a.Sk * a.Hkv + kvh) * W::ROWB;
+    const int64_t head0 = head_off(p, b, kvh, W::ROWB);
     const uint8_t *kgl = (const uint8_t *)a.k + head0, *vgl = (const uint8_t *)a.v + head0;
     uint8_t *wl = lds + wave * W::WAVE_LDS;
     const uint32_t wl0 = __builtin_amdgcn_readfirstlane(
@@ -940,13 +986,14 @@ __global__ __launch_bounds__(kThreads, 2) void decode_q4w_kernel(DecodeParams p)
     auto dma_tile = [&](int i) {
         const int64_t k0 = ks + (int64_t)(wave + 4 * i) * kBN;
         const uint32_t st = wl0 + (uint32_t)((i & 1) * W::STAGE);
-        const int64_t last = min((int64_t)kBN - 1, (int64_t)a.Sk - 1 - k0);
+        const int64_t last = min((int64_t)kBN - 1, sv.Sk - 1 - k0);
+        const int64_t toff = tile_off(p, b, k0, grow);
         if (last == kBN - 1) {
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
                 for (int x = 0; x < NX; ++x)
-                    dma4((tt ? vgl : kgl) + (k0 + (int64_t)(x / NV) * W::RSTEP) * grow,
+                    dma4((tt ? vgl : kgl) + toff + (int64_t)(x / NV) * W::RSTEP * grow,
                          vo[x % NV], st + (uint32_t)(tt * TILEB + 256 * x));
         } else {
             // the sequence's last, partial tile: rows past its last key re-read that key (a
@@ -957,7 +1004,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_q4w_kernel(DecodeParams p)
                 for (int x = 0; x < NX; ++x) {
                     const int e = 64 * x + lane;
                     const uint32_t row = (uint32_t)min(e / ROWDW, (int)last);
-                    dma4((tt ? vgl : kgl) + k0 * grow, row * grow + 4u * (uint32_t)(e % ROWDW),
+                    dma4((tt ? vgl : kgl) + toff, row * grow + 4u * (uint32_t)(e % ROWDW),
                          st + (uint32_t)(tt * TILEB + 256 * x));
                 }
         }
@@ -1171,7 +1218,7 @@ DecodeGrid decode_grid(int B, int Hq, int Hkv, int Sq, int Sk, int D, int64_t ke
 }
 
 hipError_t launch_decode(const AttnArgs &a, const DecodeGrid &g, void *workspace,
-                         hipStream_t stream)
+                         hipStream_t stream, const PagedKV *paged)
 {
     if (g.n_wg == 0)
         return hipSuccess;
@@ -1183,6 +1230,10 @@ hipError_t launch_decode(const AttnArgs &a, const DecodeGrid &g, void *workspace
     p.kend = a.causal ? min((int64_t)a.Sk, (int64_t)a.Sq - 1 + a.offset + 1) : (int64_t)a.Sk;
     if (p.kend < 0)
         p.kend = 0;
+    p.block_table = paged ? paged->block_table : nullptr;
+    p.seq_lens = paged ? paged->seq_lens : nullptr;
+    p.max_pages = paged ? paged->max_pages : 0;
+    p.n_pages = paged ? paged->n_pages : 0;
     p.part = (float *)workspace;
     if (a.D == 128) {
         if (a.kv == KV_F16)

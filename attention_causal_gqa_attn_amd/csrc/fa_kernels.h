@@ -42,8 +42,14 @@ struct DecodeGrid {
 DecodeGrid decode_grid(int B, int Hq, int Hkv, int Sq, int Sk, int D, int64_t kend, bool bound,
                        int kv);
 bool q4_grouped(int kv, int rows, int Hkv);
+// Paged K/V (fa_decode_paged): pages of 64 keys ([n_pages][64][Hkv][row]); sequence b's key j
+// is in page block_table[b * max_pages + j / 64]; seq_lens[b] keys (device arrays).
+struct PagedKV {
+    const int32_t *block_table, *seq_lens;
+    int max_pages, n_pages;
+};
 hipError_t launch_decode(const AttnArgs &a, const DecodeGrid &g, void *workspace,
-                         hipStream_t stream);
+                         hipStream_t stream, const PagedKV *paged = nullptr);
 
 hipError_t launch_dequant_q4_0(const void *blocks, int64_t n_blocks, float *out_f32,
                                void *out_f16, hipStream_t stream);

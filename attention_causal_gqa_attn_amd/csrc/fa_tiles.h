@@ -72,13 +72,15 @@ struct TileLoader {
         voff = (uint32_t)v_key0() * row + (uint32_t)v_dc() * 16u;
     }
 
-    // Global loads of the K (V) tile starting at key k0 (k0 < Sk): a uniform tile base plus a
-    // 32-bit offset (the per-pass / per-key part of it is uniform, the per-thread part fixed),
-    // both branches in 32 bits so the loads keep the scalar-base form after the compiler merges
-    // them. In the last, partial tile keys past the end repeat the last key.
-    __device__ __forceinline__ void load_k(int k0)
+    // Global loads of the K (V) tile starting at key k0 (k0 < Sk), whose key-0 row is toff
+    // bytes past the head's (k0 rows on in a contiguous cache, its page in a paged one): a
+    // uniform tile base plus a 32-bit offset (the per-pass / per-key part of it is uniform, the
+    // per-thread part fixed), both branches in 32 bits so the loads keep the scalar-base form
+    // after the compiler merges them. In the last, partial tile keys past the end repeat the
+    // last key.
+    __device__ __forceinline__ void load_k(int k0, int64_t toff)
     {
-        const uint8_t *kt = kbase + (int64_t)k0 * row;
+        const uint8_t *kt = kbase + toff;
         if (k0 + kBN <= Sk) {
 #pragma unroll
             for (int p = 0; p < KC; ++p)
@@ -93,9 +95,9 @@ struct TileLoader {
         }
     }
 
-    __device__ __forceinline__ void load_v(int k0)
+    __device__ __forceinline__ void load_v(int k0, int64_t toff)
     {
-        const uint8_t *vt = vbase + (int64_t)k0 * row;
+        const uint8_t *vt = vbase + toff;
         if (k0 + kBN <= Sk) {
 #pragma unroll
             for (int r = 0; r < KPT; ++r)
@@ -111,10 +113,10 @@ struct TileLoader {
         }
     }
 
-    __device__ __forceinline__ void load(int k0)
+    __device__ __forceinline__ void load(int k0, int64_t toff)
     {
-        load_k(k0);
-        load_v(k0);
+        load_k(k0, toff);
+        load_v(k0, toff);
     }
 
     __device__ __forceinline__ void store_k(uint16_t *lk) const

@@ -103,6 +103,26 @@ int fa_decode(const void *q, const void *k, const void *v, void *o,
               void *workspace, size_t workspace_bytes, fa_stream_t stream);
 
 /*
+ * Split-K decode over paged K/V caches (a batch of sequences of different lengths, as a
+ * serving loop keeps them). K and V are n_pages pages of 64 keys each, [n_pages, 64, Hkv, D]
+ * (q4_0: [n_pages, 64, Hkv, D/32] blocks of 18 bytes), shared by all sequences; sequence b has
+ * seq_lens[b] keys (clamped to [0, max_pages * 64]) and its key j is key j % 64 of page
+ * block_table[b * max_pages + j / 64]. Its Sq queries are its last Sq positions: with causal,
+ * query i (at position seq_lens[b] - Sq + i) sees keys j <= seq_lens[b] - Sq + i; otherwise
+ * all seq_lens[b] keys.
+ *   q, o          device pointers, [B, Sq, Hq, D], as fa_decode
+ *   block_table   device int32 [B, max_pages]; seq_lens device int32 [B]; 4-byte aligned.
+ *                 Entries outside [0, n_pages) are clamped into it (wrong output, never an
+ *                 access outside the pages).
+ *   workspace     >= fa_decode_workspace_bytes(B, Hq, Hkv, Sq, max_pages * 64, D) bytes.
+ * Other arguments, limits, errors and asynchrony as fa_decode.
+ */
+int fa_decode_paged(const void *q, const void *k_pages, const void *v_pages, void *o,
+                    const int32_t *block_table, const int32_t *seq_lens, int B, int Hq,
+                    int Hkv, int Sq, int D, int max_pages, int n_pages, int causal, float scale,
+                    int kv_dtype, void *workspace, size_t workspace_bytes, fa_stream_t stream);
+
+/*
  * Dequantize n_blocks q4_0 blocks (18 bytes each, 2-byte aligned) with the same device
  * routine the attention kernels use. out_f32 receives the exact values (c - 8) * d as
  * float (n_blocks * 32 floats); out_f16 receives their f16 forms, rounded to nearest even

@@ -138,6 +138,36 @@ def test_dequant_rejects():
     assert fa.fa_dequant_q4_0(P, 4, P + 2, P, None) == fa.FA_ERR_ALIGN
 
 
+def test_decode_paged_rejects():
+    d = fa.fa_decode_paged
+    # (q, k, v, o, table, lens, B, Hq, Hkv, Sq, D, max_pages, n_pages, causal, scale, kv,
+    #  workspace, workspace_bytes, stream)
+    base = [P, P, P, P, P, P, 4, 32, 8, 1, 128, 512, 4096, 1, 0.088, 2, P, 1 << 30, None]
+
+    def call(**kw):
+        names = ["q", "k", "v", "o", "table", "lens", "B", "Hq", "Hkv", "Sq", "D", "max_pages",
+                 "n_pages", "causal", "scale", "kv", "ws", "ws_bytes", "stream"]
+        args = list(base)
+        for key, val in kw.items():
+            args[names.index(key)] = val
+        return d(*args)
+
+    assert call(table=None) == fa.FA_ERR_NULL
+    assert call(lens=None) == fa.FA_ERR_NULL
+    assert call(table=P + 2) == fa.FA_ERR_ALIGN
+    assert call(max_pages=-1) == fa.FA_ERR_SHAPE
+    assert call(n_pages=-1) == fa.FA_ERR_SHAPE
+    assert call(n_pages=0) == fa.FA_ERR_SHAPE              # table entries must name a page
+    assert call(max_pages=1 << 26) == fa.FA_ERR_SHAPE
+    assert call(kv=7) == fa.FA_ERR_DTYPE
+    assert call(Hkv=2, Sq=2) == fa.FA_ERR_UNSUPPORTED       # 32 query rows per KV head
+    assert call(ws=None) == fa.FA_ERR_WORKSPACE
+    assert call(ws_bytes=100) == fa.FA_ERR_WORKSPACE
+    assert call(ws=P + 4) == fa.FA_ERR_ALIGN
+    assert call(B=0) == fa.FA_OK
+    assert call(Sq=0) == fa.FA_OK
+
+
 def test_quantize_rejects():
     q = fa.fa_quantize_q4_0
     # (x, x_dtype, blocks, n_seq, rows_per_seq, D, x_seq_stride, blocks_seq_stride, stream)

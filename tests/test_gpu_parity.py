@@ -261,3 +261,72 @@ def test_decode_equals_prefill_on_decode_shape():
     a = gpu_decode(w, x)
     b = gpu_prefill(w, x)
     assert float(np.max(np.abs(a - b))) <= TOL[w.kv]
+
+
+# ---------------------------------------------------------------------------------------------
+# paged decode: shuffled 64-key pages, per-sequence lengths
+# ---------------------------------------------------------------------------------------------
+
+PAGED = [
+    # (name, B, Hq, Hkv, Sq, lens, D, kv, causal, max_pages, seed); the kernels: head groups,
+    # wave-owned tiles (Hkv = 2), 8 rows per KV head, 16-bit caches
+    ("paged_q4_0_gqa4", 4, 32, 8, 1, [5000, 1, 0, 4133], 128, "q4_0", True, 80, 81),
+    ("paged_q4_0_hkv2", 3, 8, 2, 1, [700, 64, 130], 128, "q4_0", True, 12, 82),
+    ("paged_q4_0_rows8_d64", 2, 16, 2, 1, [300, 555], 64, "q4_0", True, 9, 83),
+    ("paged_f16_sq2", 2, 16, 4, 2, [1000, 77], 128, "f16", True, 16, 84),
+    ("paged_bf16_noncausal", 2, 8, 8, 3, [200, 64], 128, "bf16", False, 4, 85),
+]
+
+
+@pytest.mark.parametrize("case", PAGED, ids=[c[0] for c in PAGED])
+def test_decode_paged_matches_oracle(case):
+    name, B, Hq, Hkv, Sq, lens, D, kv, causal, max_pages, seed = case
+    say(f"paged decode {case}")
+    w = wl(name, B, Hq, Hkv, Sq, max_pages * 64, D, kv, causal, None, seed)
+    x = W.generate(w)
+    q = to_dev(x.q, w.q_dtype)
+    # cut every sequence into 64-key pages and scatter them (and a few unused ones) at random
+    rng = np.random.default_rng(seed)
+    n_pages = B * max_pages + 3
+    order = rng.permutation(n_pages)
+    table = np.empty((B, max_pages), np.int32)
+    kp = np.zeros((n_pages, 64) + x.k.shape[2:], x.k.dtype)
+    vp = np.zeros_like(kp)
+    for b in range(B):
+        for j in range(max_pages):
+            pg = order[b * max_pages + j]
+            table[b, j] = pg
+            kp[pg] = x.k[b, 64 * j:64 * j + 64]
+            vp[pg] = x.v[b, 64 * j:64 * j + 64]
+    got = fa.decode_paged(q, to_dev(kp, w.kv), to_dev(vp, w.kv),
+                          torch.from_numpy(table).cuda(),
+                          torch.tensor(lens, dtype=torch.int32, device="cuda"),
+                          causal=causal, scale=w.scale)
+    torch.cuda.synchronize()
+    got = got.float().cpu().numpy()
+    for b in range(B):
+        n = lens[b]
+        ref = oracle.attention(x.q[b:b + 1], x.k[b:b + 1, :n], x.v[b:b + 1, :n],
+                               q_dtype=w.q_dtype, kv_dtype=w.kv, causal=causal,
+                               offset=n - Sq, scale=w.scale)
+        err = float(np.max(np.abs(got[b] - ref[0])))
+        assert err <= TOL[w.kv], (name, b, n, err)
+
+
+def test_decode_paged_in_order_equals_contiguous():
+    """The full-size decode with its cache read as in-order pages gives the same bits as the
+    contiguous call: only where a tile's bytes come from differs."""
+    w = W.WORKLOADS["decode_q4_0"]
+    say(f"paged (in order) vs contiguous {w}")
+    x = W.generate(w)
+    q, k, v = to_dev(x.q, "f16"), to_dev(x.k, "q4_0"), to_dev(x.v, "q4_0")
+    a = fa.decode(q, k, v, causal=True, offset=w.causal_offset, scale=w.scale)
+    per = w.Sk // 64
+    kp = k.view(w.B * per, 64, w.Hkv, -1)
+    vp = v.view(w.B * per, 64, w.Hkv, -1)
+    table = torch.arange(w.B * per, dtype=torch.int32, device="cuda").view(w.B, per)
+    lens = torch.full((w.B,), w.Sk, dtype=torch.int32, device="cuda")
+    b = fa.decode_paged(q, kp, vp, table, lens, causal=True, scale=w.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
