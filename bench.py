@@ -9,7 +9,9 @@ One step = one pass of the whole path over resident inputs:
     the unfused arm beside it: fa_dequant_q4_0 of K and V into f16 buffers, then the f16
     fa_prefill (reported, not part of `value`);
   * the q4_0 cache writer: fa_quantize_q4_0 of the prefill workload's f16 K and V (16384
-    keys x 8 heads x 128) into q4_0 blocks (reported, HBM-bound).
+    keys x 8 heads x 128) into q4_0 blocks (reported, HBM-bound);
+  * the decode over a paged cache: the same 4 x 32768 q4_0 keys as 2048 pages of 64 keys in
+    a shuffled order (fa_decode_paged; reported, HBM-bound).
 Before each call a 1 GiB buffer is read so that neither call finds its inputs in the 256 MB
 last-level cache (the decode working set, 151 MB, would otherwise stay resident). The flush
 reads rather than writes: a written flush leaves up to 256 MB of dirty lines in that cache,
@@ -171,6 +173,16 @@ def main():
     kf = torch.empty(wq.B, wq.Sk, wq.Hkv, wq.D, dtype=torch.float16, device=dev)
     vf = torch.empty_like(kf)
     q_blocks = qk.numel() // 18
+    # the decode cache as 64-key pages in a seeded random order, and the block table
+    per = wd.Sk // 64
+    order = torch.from_numpy(np.random.default_rng(7).permutation(wd.B * per)).to(dev)
+    dkp = dk.view(wd.B * per, 64, wd.Hkv, -1)[order].contiguous()
+    dvp = dv.view(wd.B * per, 64, wd.Hkv, -1)[order].contiguous()
+    table = torch.empty(wd.B * per, dtype=torch.int32, device=dev)
+    table[order] = torch.arange(wd.B * per, dtype=torch.int32, device=dev)
+    table = table.view(wd.B, per)
+    lens = torch.full((wd.B,), wd.Sk, dtype=torch.int32, device=dev)
+    do2 = torch.empty_like(dq)
     wk = torch.empty(pk.numel() // 32 * 18, dtype=torch.uint8, device=dev)
     wv = torch.empty_like(wk)
     wbytes = (pk.numel() + pv.numel()) * 2 + wk.numel() + wv.numel()
@@ -207,7 +219,11 @@ def main():
         fa.quantize_q4_0(pk.view(-1, wp.D), out=wk.view(-1, wp.D // 32 * 18), stream=stream)
         fa.quantize_q4_0(pv.view(-1, wp.D), out=wv.view(-1, wp.D // 32 * 18), stream=stream)
 
-    calls = [prefill, decode, prefill_q4, prefill_q4_unfused, quantize]
+    def decode_paged():
+        fa.decode_paged(dq, dkp, dvp, table, lens, causal=True, scale=wd.scale, out=do2,
+                        workspace=ws, stream=stream)
+
+    calls = [prefill, decode, prefill_q4, prefill_q4_unfused, quantize, decode_paged]
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * len(calls))]
           for _ in range(args.steps)]
 
@@ -242,6 +258,7 @@ def main():
     q_ms = np.array([e[4].elapsed_time(e[5]) for e in ev])
     u_ms = np.array([e[6].elapsed_time(e[7]) for e in ev])
     w_ms = np.array([e[8].elapsed_time(e[9]) for e in ev])
+    g_ms = np.array([e[10].elapsed_time(e[11]) for e in ev])
     qflops = W.attention_flops(wq)
     flops = W.attention_flops(wp)
     dbytes = W.algorithmic_bytes(wd)
@@ -298,6 +315,12 @@ def main():
                                  "what": "fa_dequant_q4_0 of K and V to f16 buffers (two "
                                          "launches), then the f16 fa_prefill",
                                  "extra_bytes": int(kf.numel() * 2 * 2)},
+        "decode_paged": {"what": "the decode workload over its cache as 2048 shuffled pages of "
+                                 "64 keys (fa_decode_paged, split + merge)",
+                         "value": round(dbytes / (float(g_ms.mean()) * 1e-3) / 1e9, 1),
+                         "unit": "GB/s", "ms_mean": round(float(g_ms.mean()), 5),
+                         "frac_of_hbm_peak": round(dbytes / (float(g_ms.mean()) * 1e-3) / 1e9
+                                                   / PEAK_HBM_GBS, 4)},
         "quantize_q4_0": {"what": "fa_quantize_q4_0 of f16 K and V [1, 16384, 8, 128] (two "
                                   "launches)",
                           "gbs": round(wbytes / (float(w_ms.mean()) * 1e-3) / 1e9, 1),
