@@ -7,10 +7,10 @@ runs in the HIP kernels of libfa.so; there is no Python or CPU fallback, and if 
 missing every call raises.
 
 Raw entry points with the C names (pointers and ints): fa_prefill, fa_decode,
-fa_decode_paged, fa_decode_workspace_bytes, fa_dequant_q4_0, fa_quantize_q4_0, fa_strerror,
-fa_version.
-Tensor helpers: prefill, decode, decode_paged, decode_workspace_bytes, dequant_q4_0,
-quantize_q4_0.
+fa_decode_paged, fa_prefill_paged, fa_decode_workspace_bytes, fa_dequant_q4_0,
+fa_quantize_q4_0, fa_strerror, fa_version.
+Tensor helpers: prefill, prefill_paged, decode, decode_paged, decode_workspace_bytes,
+dequant_q4_0, quantize_q4_0.
 """
 from __future__ import annotations
 
@@ -34,8 +34,9 @@ FA_ERR_ALIGN = -6
 FA_ERR_HIP = -7
 FA_ERR_VALUE = -8
 
-EXPORTS = ("fa_prefill", "fa_decode", "fa_decode_paged", "fa_decode_workspace_bytes",
-           "fa_dequant_q4_0", "fa_quantize_q4_0", "fa_strerror", "fa_version")
+EXPORTS = ("fa_prefill", "fa_decode", "fa_decode_paged", "fa_prefill_paged",
+           "fa_decode_workspace_bytes", "fa_dequant_q4_0", "fa_quantize_q4_0", "fa_strerror",
+           "fa_version")
 PAGE_KEYS = 64
 
 
@@ -66,6 +67,9 @@ def load() -> ctypes.CDLL:
         lib.fa_decode_paged.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
                                         i32, i32, f32, i32, vp, sz, vp]
         lib.fa_decode_paged.restype = i32
+        lib.fa_prefill_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
+                                         i32, i32, i32, f32, i32, vp]
+        lib.fa_prefill_paged.restype = i32
         lib.fa_decode_workspace_bytes.argtypes = [i32] * 6
         lib.fa_decode_workspace_bytes.restype = sz
         lib.fa_dequant_q4_0.argtypes = [vp, i64, vp, vp, vp]
@@ -100,6 +104,13 @@ def fa_decode_workspace_bytes(B, Hq, Hkv, Sq, Sk, D) -> int:
 
 def fa_dequant_q4_0(blocks, n_blocks, out_f32, out_f16, stream) -> int:
     return load().fa_dequant_q4_0(blocks, n_blocks, out_f32, out_f16, stream)
+
+
+def fa_prefill_paged(q, k_pages, v_pages, o, block_table, seq_lens, q_lens, B, Hq, Hkv, Sq, D,
+                     max_pages, n_pages, causal, scale, kv_dtype, stream) -> int:
+    return load().fa_prefill_paged(q, k_pages, v_pages, o, block_table, seq_lens, q_lens, B, Hq,
+                                   Hkv, Sq, D, max_pages, n_pages, causal, scale, kv_dtype,
+                                   stream)
 
 
 def fa_decode_paged(q, k_pages, v_pages, o, block_table, seq_lens, B, Hq, Hkv, Sq, D,
@@ -208,6 +219,47 @@ def decode(q, k, v, *, causal: bool = True, offset: Optional[int] = None,
     return out
 
 
+def _paged_sizes(q, k_pages, v_pages, block_table, seq_lens, q_lens=None):
+    torch = _torch()
+    for name, t in (("block_table", block_table), ("seq_lens", seq_lens), ("q_lens", q_lens)):
+        if t is not None and (t.dtype != torch.int32 or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous int32 tensor")
+    if block_table.dim() != 2:
+        raise ValueError("block_table must be [B, max_pages]")
+    if k_pages.dim() != 4 or k_pages.shape[1] != PAGE_KEYS or q.dim() != 4:
+        raise ValueError("pages must be [n_pages, 64, Hkv, row]; q [B, Sq, Hq, D]")
+    if not (q.is_contiguous() and k_pages.is_contiguous() and v_pages.is_contiguous()):
+        raise ValueError("q and the pages must be contiguous")
+    B, Sq, Hq, D = q.shape
+    n_pages, _, Hkv, _ = k_pages.shape
+    if (block_table.shape[0] != B or seq_lens.numel() != B or v_pages.shape != k_pages.shape
+            or (q_lens is not None and q_lens.numel() != B)):
+        raise ValueError("block_table, seq_lens, q_lens and pages disagree with q")
+    return B, Hq, Hkv, Sq, D, block_table.shape[1], n_pages
+
+
+def prefill_paged(q, k_pages, v_pages, block_table, seq_lens, q_lens=None, *,
+                  causal: bool = True, scale: Optional[float] = None, out=None, stream=None):
+    """Prefill over paged caches via fa_prefill_paged. Pages, block_table and seq_lens as
+    decode_paged; q_lens: int32 [B] or None (Sq each). Sequence b's q_lens[b] queries are rows
+    [0, q_lens[b]) of q[b], its last q_lens[b] positions; rows past them of out are not
+    written (out defaults to zeros)."""
+    torch = _torch()
+    kv = _kv_code(k_pages)
+    B, Hq, Hkv, Sq, D, max_pages, n_pages = _paged_sizes(q, k_pages, v_pages, block_table,
+                                                         seq_lens, q_lens)
+    scale = D ** -0.5 if scale is None else float(scale)
+    if out is None:
+        out = torch.zeros_like(q)
+    rc = fa_prefill_paged(q.data_ptr(), k_pages.data_ptr(), v_pages.data_ptr(), out.data_ptr(),
+                          block_table.data_ptr(), seq_lens.data_ptr(),
+                          0 if q_lens is None else q_lens.data_ptr(), B, Hq, Hkv, Sq, D,
+                          max_pages, n_pages, int(bool(causal)), scale, kv, _stream(q, stream))
+    if rc != FA_OK:
+        raise FAError(rc, "fa_prefill_paged")
+    return out
+
+
 def decode_paged(q, k_pages, v_pages, block_table, seq_lens, *, causal: bool = True,
                  scale: Optional[float] = None, out=None, workspace=None, stream=None):
     """Split-K decode over paged caches via fa_decode_paged. k_pages, v_pages: [n_pages, 64,
@@ -215,17 +267,8 @@ def decode_paged(q, k_pages, v_pages, block_table, seq_lens, *, causal: bool = T
     seq_lens: int32 [B]. Sequence b's Sq queries are its last Sq positions."""
     torch = _torch()
     kv = _kv_code(k_pages)
-    if block_table.dtype != torch.int32 or seq_lens.dtype != torch.int32:
-        raise ValueError("block_table and seq_lens must be int32")
-    if not (block_table.is_contiguous() and seq_lens.is_contiguous()) or block_table.dim() != 2:
-        raise ValueError("block_table must be a contiguous [B, max_pages] tensor")
-    if k_pages.dim() != 4 or k_pages.shape[1] != PAGE_KEYS or q.dim() != 4:
-        raise ValueError("pages must be [n_pages, 64, Hkv, row]; q [B, Sq, Hq, D]")
-    B, Sq, Hq, D = q.shape
-    n_pages, _, Hkv, _ = k_pages.shape
-    max_pages = block_table.shape[1]
-    if block_table.shape[0] != B or seq_lens.numel() != B or v_pages.shape != k_pages.shape:
-        raise ValueError("block_table, seq_lens and pages disagree with q")
+    B, Hq, Hkv, Sq, D, max_pages, n_pages = _paged_sizes(q, k_pages, v_pages, block_table,
+                                                         seq_lens)
     scale = D ** -0.5 if scale is None else float(scale)
     if out is None:
         out = torch.empty_like(q)

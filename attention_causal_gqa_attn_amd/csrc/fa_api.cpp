@@ -208,6 +208,38 @@ int fa_decode_paged(const void *q, const void *k_pages, const void *v_pages, voi
     return hip_status(fa::launch_decode(a, g, workspace, (hipStream_t)stream, &pk));
 }
 
+int fa_prefill_paged(const void *q, const void *k_pages, const void *v_pages, void *o,
+                     const int32_t *block_table, const int32_t *seq_lens, const int32_t *q_lens,
+                     int B, int Hq, int Hkv, int Sq, int D, int max_pages, int n_pages,
+                     int causal, float scale, int kv_dtype, fa_stream_t stream)
+{
+    if (max_pages < 0 || n_pages < 0 || max_pages > (INT32_MAX - 2 * 64) / 64)
+        return FA_ERR_SHAPE;
+    const int Sk = max_pages * 64;                  // keys a block-table row can address
+    fa::AttnArgs a;
+    // the causal offset is per sequence (its queries are its last q_lens[b] positions)
+    const int rc = check_attention(q, k_pages, v_pages, o, B, Hq, Hkv, Sq, Sk, D, causal, 0,
+                                   scale, kv_dtype, a);
+    if (rc != FA_OK)
+        return rc;
+    if (mul4(n_pages, 64, Hkv, D) < 0)
+        return FA_ERR_SHAPE;
+    if (max_pages > fa::kPrefillMaxPages)
+        return FA_ERR_UNSUPPORTED;
+    if ((int64_t)B * Sq == 0)
+        return FA_OK;
+    if (max_pages > 0 && n_pages == 0)
+        return FA_ERR_SHAPE;
+    if (!block_table || !seq_lens)
+        return FA_ERR_NULL;
+    if (!aligned(block_table, 4) || !aligned(seq_lens, 4) || !aligned(q_lens, 4))
+        return FA_ERR_ALIGN;
+    if (fa::prefill_grid(a).n_wg > kMaxWorkgroups)
+        return FA_ERR_UNSUPPORTED;
+    const fa::PagedKV pk{block_table, seq_lens, max_pages, n_pages};
+    return hip_status(fa::launch_prefill(a, (hipStream_t)stream, &pk, q_lens));
+}
+
 int fa_quantize_q4_0(const void *x, int x_dtype, void *blocks, int64_t n_seq,
                      int64_t rows_per_seq, int D, int64_t x_seq_stride,
                      int64_t blocks_seq_stride, fa_stream_t stream)

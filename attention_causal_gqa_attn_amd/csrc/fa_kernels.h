@@ -26,9 +26,16 @@ struct PrefillGrid {
     int64_t n_wg;
 };
 PrefillGrid prefill_grid(const AttnArgs &a);
-hipError_t launch_prefill(const AttnArgs &a, hipStream_t stream);
+struct PagedKV;
+// paged: a paged cache (a.Sk = max_pages * 64, a.offset unused); q_lens (paged only, may be
+// null): sequence b's query count, rows [0, q_lens[b]) of its Sq
+hipError_t launch_prefill(const AttnArgs &a, hipStream_t stream, const PagedKV *paged = nullptr,
+                          const int32_t *q_lens = nullptr);
 PrefillGrid prefill16_grid(const AttnArgs &a);
-hipError_t launch_prefill16(const AttnArgs &a, const PrefillGrid &g, hipStream_t stream);
+hipError_t launch_prefill16(const AttnArgs &a, const PrefillGrid &g, hipStream_t stream,
+                            const PagedKV *paged = nullptr, const int32_t *q_lens = nullptr);
+// the paged prefill keeps a sequence's page numbers in LDS: at most this many per sequence
+constexpr int kPrefillMaxPages = 4096;
 
 // Decode: n_split key ranges per (b, KV head); rows = G * Sq query rows per KV head (<= 16).
 struct DecodeGrid {

@@ -20,7 +20,11 @@
 //  * a q4_0 cache arrives raw (12-byte LDS-DMA chunks, K 4 tiles and V 2 tiles ahead) and the
 //    waves dequantize it into 2-stage f16 K and V rings of the same layout, one tile of each per
 //    iteration (K two tiles ahead of its scores, V one ahead of its P.V), so everything after
-//    the dequantization is the f16 kernel.
+//    the dequantization is the f16 kernel;
+//  * a paged cache (64-key pages, a block table and per-sequence lengths) differs only in where
+//    a tile's bytes start and where a sequence ends: the workgroup copies its sequence's page
+//    numbers into LDS once, and each iteration reads the two it needs (K n+4, V n+2) at its
+//    start, before the slots that issue the transfers.
 #include <cstdlib>
 #include <utility>
 
@@ -43,6 +47,9 @@ constexpr int kStages = 4;             // tile stages per ring (K ring, V ring)
 struct Prefill16Params {
     AttnArgs a;
     int hpw, qsub, n_qblk, n_hchunk;
+    // paged caches only (see PagedKV); q_lens may be null (Sq queries in every sequence)
+    const int32_t *block_table, *seq_lens, *q_lens;
+    int max_pages, n_pages;
 };
 
 // s_waitcnt immediate: wait until at most `vm` vector-memory ops are outstanding and all LDS
@@ -336,7 +343,7 @@ struct Plans {
     static_assert(schedule_ok<NDT, NST, NM>(sc), "softmax units placed in time");
 };
 
-template <int D, int KVT>
+template <int D, int KVT, bool PAGED>
 __global__ __launch_bounds__(kNT, 1) void prefill16_kernel(Prefill16Params p)
 {
     constexpr bool BF = KVT == KV_BF16;
@@ -346,6 +353,7 @@ __global__ __launch_bounds__(kNT, 1) void prefill16_kernel(Prefill16Params p)
     using PL = Plans<D>;
     constexpr int NDT = PL::NDT, NST = PL::NST, NM = PL::NM;
     __shared__ __attribute__((aligned(1024))) uint8_t lds[Q4 ? QR::LDS : G::LDS];
+    __shared__ int32_t ptab[PAGED ? kPrefillMaxPages : 1];     // the sequence's page numbers
     typedef __attribute__((address_space(3))) s16x4_t lds_s16x4;
 
     const AttnArgs &a = p.a;
@@ -363,18 +371,29 @@ __global__ __launch_bounds__(kNT, 1) void prefill16_kernel(Prefill16Params p)
     const int b = rest / a.Hkv;
     const int qblk = a.causal ? p.n_qblk - 1 - qbl : qbl;    // heaviest blocks first
 
+    // this sequence's keys and queries, and the position of its first query
+    int sk = a.Sk, sq = a.Sq;
+    int64_t off = a.offset;
+    if constexpr (PAGED) {
+        sk = min(max(p.seq_lens[b], 0), p.max_pages * kBN);
+        sq = p.q_lens ? min(max(p.q_lens[b], 0), a.Sq) : a.Sq;
+        off = (int64_t)sk - sq;
+    }
+
     const int bmq = kQW * p.qsub;
     const int qwg0 = qblk * bmq;
+    if (PAGED && qwg0 >= sq)
+        return;                                  // whole workgroup: no row of it exists
     const int hs = wave % p.hpw, qs = wave / p.hpw;
     const int hl = hc * p.hpw + hs;
     const int q0 = qwg0 + qs * kQW;
-    const bool wave_on = (wave < p.hpw * p.qsub) && (hl < a.G) && (q0 < a.Sq);
+    const bool wave_on = (wave < p.hpw * p.qsub) && (hl < a.G) && (q0 < sq);
     const int h = kvh * a.G + min(hl, a.G - 1);
 
-    const int qlast_wg = min(qwg0 + bmq, a.Sq) - 1;
-    int64_t kend = a.Sk;
+    const int qlast_wg = min(qwg0 + bmq, sq) - 1;
+    int64_t kend = sk;
     if (a.causal)
-        kend = min((int64_t)a.Sk, (int64_t)qlast_wg + a.offset + 1);
+        kend = min((int64_t)sk, (int64_t)qlast_wg + off + 1);
     kend = max(kend, (int64_t)0);
     const int nb = (int)((kend + kBN - 1) / kBN);
 
@@ -384,9 +403,9 @@ __global__ __launch_bounds__(kNT, 1) void prefill16_kernel(Prefill16Params p)
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
         qi[j] = q0 + 32 * j + col;
-        klim[j] = a.causal ? min((int64_t)a.Sk - 1, (int64_t)qi[j] + a.offset) : (int64_t)a.Sk - 1;
-        klim_min[j] = a.causal ? min((int64_t)a.Sk - 1, (int64_t)(q0 + 32 * j) + a.offset)
-                               : (int64_t)a.Sk - 1;
+        klim[j] = a.causal ? min((int64_t)sk - 1, (int64_t)qi[j] + off) : (int64_t)sk - 1;
+        klim_min[j] = a.causal ? min((int64_t)sk - 1, (int64_t)(q0 + 32 * j) + off)
+                               : (int64_t)sk - 1;
     }
 
     // ---- Q once, as B operands: qf[j][st] = row qi[j], d = 16 st + 8 half .. + 7 -----------
@@ -419,8 +438,10 @@ __global__ __launch_bounds__(kNT, 1) void prefill16_kernel(Prefill16Params p)
     bool rescale[2] = {false, false};
 
     // ---- tile DMA: transfer i of thread t moves 16-byte chunk n = (i*kNW + wave)*64 + lane ---
-    const uint8_t *kg = (const uint8_t *)a.k + ((int64_t)b * a.Sk * a.Hkv + kvh) * G::ROW;
-    const uint8_t *vg = (const uint8_t *)a.v + ((int64_t)b * a.Sk * a.Hkv + kvh) * G::ROW;
+    // (b, kv head)'s key 0; a paged cache: kv head's row in a page, pages added per tile
+    const int64_t hrow = PAGED ? kvh : (int64_t)b * a.Sk * a.Hkv + kvh;
+    const uint8_t *kg = (const uint8_t *)a.k + hrow * G::ROW;
+    const uint8_t *vg = (const uint8_t *)a.v + hrow * G::ROW;
     const uint32_t grow = (uint32_t)a.Hkv * G::ROW;       // bytes between consecutive keys
     const uint32_t lds0 = lds_addr(lds);
     // chunk (row r, column chunk c) of transfer i; K and V chunks land swizzled
@@ -441,53 +462,69 @@ __global__ __launch_bounds__(kNT, 1) void prefill16_kernel(Prefill16Params p)
     constexpr int FS = Q4 ? 2 : kStages;
     auto kstage = [&](int tl) INL { return lds + (tl & (FS - 1)) * G::TILE; };
     auto vstage = [&](int tl) INL { return lds + (FS + (tl & (FS - 1))) * G::TILE; };
-    // Transfer i of tile tl of K (is_v false) or V into a stage. Tiles past the last one
-    // re-read the last tile (into a stage nobody reads any more), so every loop iteration
-    // issues the same transfers and the wait counts stay fixed; rows past the end of the
-    // sequence repeat the last key.
-    auto dma_one = [&](bool is_v, int stage, int tl, int i) INL {
+    // Where tile tl sits, in tiles of kBN keys from the (b, kv head) base: tl itself, or its
+    // page. Tiles past the last one re-read the last tile (into a stage nobody reads any more),
+    // so every loop iteration issues the same transfers and the wait counts stay fixed.
+    if constexpr (PAGED) {
+        const int32_t *bt = p.block_table + (int64_t)b * p.max_pages;
+        for (int i = t; i < nb; i += kNT)
+            ptab[i] = min(max(bt[i], 0), p.n_pages - 1);
+        __syncthreads();
+    }
+    auto slot = [&](int tl) INL -> int {
+        tl = min(tl, nb - 1);
+        if constexpr (PAGED)
+            return __builtin_amdgcn_readfirstlane(ptab[tl]);
+        else
+            return tl;
+    };
+    // Transfer i of tile tl (at slot sl) of K (is_v false) or V into a stage; rows past the end
+    // of the sequence repeat its last key.
+    auto dma_one = [&](bool is_v, int stage, int tl, int sl, int i) INL {
         tl = min(tl, nb - 1);
         const int k0 = tl * kBN;
-        const uint8_t *gt = (is_v ? vg : kg) + (int64_t)k0 * grow;
-        const uint32_t lastg = (uint32_t)min(kBN - 1, a.Sk - 1 - k0) * grow;
+        const uint8_t *gt = (is_v ? vg : kg) + (int64_t)sl * kBN * grow;
+        const uint32_t lastg = (uint32_t)min(kBN - 1, sk - 1 - k0) * grow;
         dma16(gt, min(rowg[i], lastg) + (is_v ? vc[i] : kc[i]),
               lwave[i] + (uint32_t)(stage * G::TILE));
     };
-    // transfer i of the tiles issued in iteration n: i < NDMA: K(n+4), else V(n+2)
-    auto dma_part = [&](int n, int i) INL {
+    // transfer i of the tiles issued in iteration n: i < NDMA: K(n+4) at slot sk4, else V(n+2)
+    // at slot sv2
+    auto dma_part = [&](int n, int i, int sk4, int sv2) INL {
         if (i < G::NDMA)
-            dma_one(false, (n + 4) & (kStages - 1), n + 4, i);
+            dma_one(false, (n + 4) & (kStages - 1), n + 4, sk4, i);
         else
-            dma_one(true, kStages + ((n + 2) & (kStages - 1)), n + 2, i - G::NDMA);
+            dma_one(true, kStages + ((n + 2) & (kStages - 1)), n + 2, sv2, i - G::NDMA);
     };
 
     // ---- q4_0: raw transfers and the dequantization into the f16 rings ----------------------
     const uint32_t growq = (uint32_t)a.Hkv * QR::ROWB;
-    const uint8_t *kq = (const uint8_t *)a.k + ((int64_t)b * a.Sk * a.Hkv + kvh) * QR::ROWB;
-    const uint8_t *vq = (const uint8_t *)a.v + ((int64_t)b * a.Sk * a.Hkv + kvh) * QR::ROWB;
+    const uint8_t *kq = (const uint8_t *)a.k + hrow * QR::ROWB;
+    const uint8_t *vq = (const uint8_t *)a.v + hrow * QR::ROWB;
     auto rawk = [&](int tl) INL { return lds + 4 * G::TILE + (tl & (QR::KR - 1)) * QR::RAWT; };
     auto rawv = [&](int tl) INL {
         return lds + 4 * G::TILE + QR::KR * QR::RAWT + (tl % QR::VR) * QR::RAWT;
     };
-    // transfer x of raw tile tl (slots 64 x .. 64 x + 63); tiles past the last re-read the last
-    // one, rows past the sequence's end repeat its last key
-    auto dma_raw = [&](bool is_v, int tl, int x) INL {
+    // transfer x of raw tile tl at slot ts (LDS slots 64 x .. 64 x + 63); tiles past the last
+    // re-read the last one, rows past the sequence's end repeat its last key
+    auto dma_raw = [&](bool is_v, int tl, int ts, int x) INL {
         const uint8_t *stg = is_v ? rawv(tl) : rawk(tl);
         tl = min(tl, nb - 1);
         const int64_t k0 = (int64_t)tl * kBN;
         const int sl = 64 * x + lane;
-        const int last = (int)min((int64_t)kBN - 1, (int64_t)a.Sk - 1 - k0);
+        const int last = (int)min((int64_t)kBN - 1, (int64_t)sk - 1 - k0);
         const uint32_t row = (uint32_t)min(sl / QR::CPR, last);
-        dma12((is_v ? vq : kq) + k0 * growq, row * growq + 12u * (uint32_t)(sl % QR::CPR),
+        dma12((is_v ? vq : kq) + (int64_t)ts * kBN * growq,
+              row * growq + 12u * (uint32_t)(sl % QR::CPR),
               __builtin_amdgcn_readfirstlane(lds_addr(stg) + (uint32_t)(1024 * x)));
     };
-    // this wave's m-th transfer of iteration n: raw K(n+4), then raw V(n+2)
-    auto dma_q4 = [&](int n, int m) INL {
+    // this wave's m-th transfer of iteration n: raw K(n+4) at slot sk4, then raw V(n+2) at sv2
+    auto dma_q4 = [&](int n, int m, int sk4, int sv2) INL {
         const int i = min(wave + kNW * m, 2 * QR::NX - 1);
         if (i < QR::NX)
-            dma_raw(false, n + 4, i);
+            dma_raw(false, n + 4, sk4, i);
         else
-            dma_raw(true, n + 2, i - QR::NX);
+            dma_raw(true, n + 2, sv2, i - QR::NX);
     };
     // This thread's (key row, block) item of a tile: at D = 128 one K and one V item, wave w
     // taking the blocks of parity w & 1 (whether a block starts at byte 0 or 6 of its first
@@ -697,6 +734,7 @@ __global__ __launch_bounds__(kNT, 1) void prefill16_kernel(Prefill16Params p)
     // cannot see are masked to -inf and give P = 0).
     auto tile = [&](int n, f32x16 *s0, f32x16 *s1c, f32x16 *s1n) INL {
         const uint8_t *vs = vstage(n - 1), *ks = kstage(n + 1);
+        const int sk4 = slot(n + 4), sv2 = slot(n + 2);     // where this iteration's DMA reads
         u32x4 fb[kRead + 1];
         smfma_drain(s0[0], s0[1], s1c[0], s1c[1]);
         mask(0, s0, n);
@@ -728,9 +766,9 @@ __global__ __launch_bounds__(kNT, 1) void prefill16_kernel(Prefill16Params p)
             units(std::integral_constant<int, NM + i>{});
             if constexpr (Q4) {
                 if constexpr ((i & 3) == 1 && (i >> 2) < QR::NIW)
-                    dma_q4(n, i >> 2);
+                    dma_q4(n, i >> 2, sk4, sv2);
             } else if constexpr ((i & 3) == 1 && (i >> 2) < 2 * G::NDMA) {
-                dma_part(n, i >> 2);
+                dma_part(n, i >> 2, sk4, sv2);
             }
             __builtin_amdgcn_sched_barrier(0);
         });
@@ -767,24 +805,24 @@ __global__ __launch_bounds__(kNT, 1) void prefill16_kernel(Prefill16Params p)
 #pragma unroll
                 for (int x = 0; x < QR::NX; ++x)
                     if (x % kNW == wave)
-                        dma_raw(false, tl, x);
+                        dma_raw(false, tl, slot(tl), x);
 #pragma unroll
             for (int tl = 0; tl < 2; ++tl)
 #pragma unroll
                 for (int x = 0; x < QR::NX; ++x)
                     if (x % kNW == wave)
-                        dma_raw(true, tl, x);
+                        dma_raw(true, tl, slot(tl), x);
         } else {
 #pragma unroll
             for (int tl = 0; tl < 4; ++tl)
 #pragma unroll
                 for (int i = 0; i < G::NDMA; ++i)
-                    dma_one(false, tl, tl, i);
+                    dma_one(false, tl, tl, slot(tl), i);
 #pragma unroll
             for (int tl = 0; tl < 2; ++tl)
 #pragma unroll
                 for (int i = 0; i < G::NDMA; ++i)
-                    dma_one(true, kStages + tl, tl, i);
+                    dma_one(true, kStages + tl, tl, slot(tl), i);
         }
     }
 
@@ -834,7 +872,7 @@ __global__ __launch_bounds__(kNT, 1) void prefill16_kernel(Prefill16Params p)
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
         const float ltot = pair_sum(lsum[j]);
-        if (!wave_on || qi[j] >= a.Sq)
+        if (!wave_on || qi[j] >= sq)
             continue;
         const float inv = ltot > 0.0f ? 1.0f / ltot : 0.0f;
         uint16_t *op = (uint16_t *)a.o + (((int64_t)b * a.Sq + qi[j]) * a.Hq + h) * D;
@@ -853,7 +891,12 @@ __global__ __launch_bounds__(kNT, 1) void prefill16_kernel(Prefill16Params p)
 template <int D, int KVT>
 hipError_t launch16(const Prefill16Params &p, int64_t n_wg, hipStream_t stream)
 {
-    hipLaunchKernelGGL((prefill16_kernel<D, KVT>), dim3((unsigned)n_wg), dim3(kNT), 0, stream, p);
+    if (p.block_table)
+        hipLaunchKernelGGL((prefill16_kernel<D, KVT, true>), dim3((unsigned)n_wg), dim3(kNT), 0,
+                           stream, p);
+    else
+        hipLaunchKernelGGL((prefill16_kernel<D, KVT, false>), dim3((unsigned)n_wg), dim3(kNT), 0,
+                           stream, p);
     return hipGetLastError();
 }
 
@@ -874,15 +917,26 @@ PrefillGrid prefill16_grid(const AttnArgs &a)
 // every cache type takes this kernel (q4_0: raw LDS-DMA, dequantized into its f16 rings)
 PrefillGrid prefill_grid(const AttnArgs &a) { return prefill16_grid(a); }
 
-hipError_t launch_prefill(const AttnArgs &a, hipStream_t stream)
+hipError_t launch_prefill(const AttnArgs &a, hipStream_t stream, const PagedKV *paged,
+                          const int32_t *q_lens)
 {
     const PrefillGrid g = prefill16_grid(a);
-    return g.n_wg == 0 ? hipSuccess : launch_prefill16(a, g, stream);
+    return g.n_wg == 0 ? hipSuccess : launch_prefill16(a, g, stream, paged, q_lens);
 }
 
-hipError_t launch_prefill16(const AttnArgs &a, const PrefillGrid &g, hipStream_t stream)
+hipError_t launch_prefill16(const AttnArgs &a, const PrefillGrid &g, hipStream_t stream,
+                            const PagedKV *paged, const int32_t *q_lens)
 {
-    const Prefill16Params p{a, g.hpw, g.qsub, g.n_qblk, g.n_hchunk};
+    Prefill16Params p{a, g.hpw, g.qsub, g.n_qblk, g.n_hchunk, nullptr, nullptr, nullptr, 0, 0};
+    if (paged) {
+        if (paged->max_pages > kPrefillMaxPages || !paged->block_table || !paged->seq_lens)
+            return hipErrorInvalidValue;
+        p.block_table = paged->block_table;
+        p.seq_lens = paged->seq_lens;
+        p.q_lens = q_lens;
+        p.max_pages = paged->max_pages;
+        p.n_pages = paged->n_pages;
+    }
     if (a.D == 128) {
         if (a.kv == KV_BF16)
             return launch16<128, KV_BF16>(p, g.n_wg, stream);

@@ -123,6 +123,26 @@ int fa_decode_paged(const void *q, const void *k_pages, const void *v_pages, voi
                     int kv_dtype, void *workspace, size_t workspace_bytes, fa_stream_t stream);
 
 /*
+ * Chunked prefill over paged K/V caches: a batch of sequences of different lengths, each
+ * appending a chunk of its own length, as a serving loop runs them. Pages, block_table,
+ * seq_lens and their clamping as fa_decode_paged. Sequence b has q_lens[b] new queries
+ * (clamped to [0, Sq]; q_lens NULL means Sq in every sequence) in rows [0, q_lens[b]) of
+ * Q[b] and O[b]; they are its last q_lens[b] positions: with causal, row i (at position
+ * seq_lens[b] - q_lens[b] + i) sees keys j <= seq_lens[b] - q_lens[b] + i, else all
+ * seq_lens[b] keys. Rows i >= q_lens[b] of O are not written.
+ *   q, o          device pointers, [B, Sq, Hq, D], as fa_prefill
+ *   block_table   device int32 [B, max_pages]; seq_lens, q_lens device int32 [B]; 4-byte
+ *                 aligned
+ *   max_pages     at most 4096 (a sequence's page numbers are held in LDS), else
+ *                 FA_ERR_UNSUPPORTED
+ * Other arguments, limits, errors and asynchrony as fa_prefill.
+ */
+int fa_prefill_paged(const void *q, const void *k_pages, const void *v_pages, void *o,
+                     const int32_t *block_table, const int32_t *seq_lens, const int32_t *q_lens,
+                     int B, int Hq, int Hkv, int Sq, int D, int max_pages, int n_pages,
+                     int causal, float scale, int kv_dtype, fa_stream_t stream);
+
+/*
  * Dequantize n_blocks q4_0 blocks (18 bytes each, 2-byte aligned) with the same device
  * routine the attention kernels use. out_f32 receives the exact values (c - 8) * d as
  * float (n_blocks * 32 floats); out_f16 receives their f16 forms, rounded to nearest even

@@ -168,6 +168,38 @@ def test_decode_paged_rejects():
     assert call(Sq=0) == fa.FA_OK
 
 
+def test_prefill_paged_rejects():
+    d = fa.fa_prefill_paged
+    # (q, k, v, o, table, lens, q_lens, B, Hq, Hkv, Sq, D, max_pages, n_pages, causal, scale,
+    #  kv, stream); every case below must be refused before a launch
+    base = [P, P, P, P, P, P, P, 4, 32, 8, 128, 128, 512, 4096, 1, 0.088, 2, None]
+
+    def call(**kw):
+        names = ["q", "k", "v", "o", "table", "lens", "q_lens", "B", "Hq", "Hkv", "Sq", "D",
+                 "max_pages", "n_pages", "causal", "scale", "kv", "stream"]
+        args = list(base)
+        for key, val in kw.items():
+            args[names.index(key)] = val
+        return d(*args)
+
+    assert call(table=None) == fa.FA_ERR_NULL
+    assert call(lens=None) == fa.FA_ERR_NULL
+    assert call(table=P + 2) == fa.FA_ERR_ALIGN
+    assert call(lens=P + 1) == fa.FA_ERR_ALIGN
+    assert call(q_lens=P + 2) == fa.FA_ERR_ALIGN
+    assert call(q=ODD) == fa.FA_ERR_ALIGN
+    assert call(max_pages=-1) == fa.FA_ERR_SHAPE
+    assert call(n_pages=-1) == fa.FA_ERR_SHAPE
+    assert call(n_pages=0) == fa.FA_ERR_SHAPE              # table entries must name a page
+    assert call(Hq=30) == fa.FA_ERR_SHAPE
+    assert call(max_pages=4097) == fa.FA_ERR_UNSUPPORTED   # page numbers are held in LDS
+    assert call(D=96) == fa.FA_ERR_UNSUPPORTED
+    assert call(kv=7) == fa.FA_ERR_DTYPE
+    assert call(scale=0.0) == fa.FA_ERR_VALUE
+    assert call(B=0) == fa.FA_OK
+    assert call(Sq=0, q_lens=None) == fa.FA_OK
+
+
 def test_quantize_rejects():
     q = fa.fa_quantize_q4_0
     # (x, x_dtype, blocks, n_seq, rows_per_seq, D, x_seq_stride, blocks_seq_stride, stream)

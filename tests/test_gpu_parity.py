@@ -267,6 +267,24 @@ def test_decode_equals_prefill_on_decode_shape():
 # paged decode: shuffled 64-key pages, per-sequence lengths
 # ---------------------------------------------------------------------------------------------
 
+def _scatter_pages(x, B, max_pages, seed):
+    """Cut every sequence of x.k / x.v into 64-key pages and scatter them (and a few unused
+    ones) over a page pool in a seeded random order; returns (k pages, v pages, block table)."""
+    rng = np.random.default_rng(seed)
+    n_pages = B * max_pages + 3
+    order = rng.permutation(n_pages)
+    table = np.empty((B, max_pages), np.int32)
+    kp = np.zeros((n_pages, 64) + x.k.shape[2:], x.k.dtype)
+    vp = np.zeros_like(kp)
+    for b in range(B):
+        for j in range(max_pages):
+            pg = order[b * max_pages + j]
+            table[b, j] = pg
+            kp[pg] = x.k[b, 64 * j:64 * j + 64]
+            vp[pg] = x.v[b, 64 * j:64 * j + 64]
+    return kp, vp, table
+
+
 PAGED = [
     # (name, B, Hq, Hkv, Sq, lens, D, kv, causal, max_pages, seed); the kernels: head groups,
     # wave-owned tiles (Hkv = 2), 8 rows per KV head, 16-bit caches
@@ -285,19 +303,7 @@ def test_decode_paged_matches_oracle(case):
     w = wl(name, B, Hq, Hkv, Sq, max_pages * 64, D, kv, causal, None, seed)
     x = W.generate(w)
     q = to_dev(x.q, w.q_dtype)
-    # cut every sequence into 64-key pages and scatter them (and a few unused ones) at random
-    rng = np.random.default_rng(seed)
-    n_pages = B * max_pages + 3
-    order = rng.permutation(n_pages)
-    table = np.empty((B, max_pages), np.int32)
-    kp = np.zeros((n_pages, 64) + x.k.shape[2:], x.k.dtype)
-    vp = np.zeros_like(kp)
-    for b in range(B):
-        for j in range(max_pages):
-            pg = order[b * max_pages + j]
-            table[b, j] = pg
-            kp[pg] = x.k[b, 64 * j:64 * j + 64]
-            vp[pg] = x.v[b, 64 * j:64 * j + 64]
+    kp, vp, table = _scatter_pages(x, B, max_pages, seed)
     got = fa.decode_paged(q, to_dev(kp, w.kv), to_dev(vp, w.kv),
                           torch.from_numpy(table).cuda(),
                           torch.tensor(lens, dtype=torch.int32, device="cuda"),
@@ -330,3 +336,71 @@ def test_decode_paged_in_order_equals_contiguous():
     torch.cuda.synchronize()
     assert torch.equal(a, b)
 
+
+# ---------------------------------------------------------------------------------------------
+# paged prefill: per-sequence key and query counts over a shuffled page pool
+# ---------------------------------------------------------------------------------------------
+
+PAGED_PREFILL = [
+    # (name, B, Hq, Hkv, Sq, lens, q_lens or None, D, kv, causal, max_pages, seed): ragged
+    # lengths, a chunk of the whole sequence, empty sequences and chunks, a chunk longer than
+    # its sequence (its first rows see no key), a sequence of 71 pages
+    ("pp_f16_gqa4", 3, 16, 4, 160, [700, 160, 1000], [160, 100, 37], 128, "f16", True, 16, 91),
+    ("pp_bf16_noncausal", 3, 8, 2, 96, [333, 64, 0], [96, 50, 20], 128, "bf16", False, 6, 92),
+    ("pp_q4_0_gqa4", 3, 16, 4, 130, [900, 0, 513], [130, 0, 129], 128, "q4_0", True, 15, 93),
+    ("pp_q4_0_d64", 2, 4, 4, 70, [200, 450], [70, 1], 64, "q4_0", True, 8, 94),
+    ("pp_f16_d64_chunk_gt_seq", 2, 8, 8, 100, [40, 300], [100, 100], 64, "f16", True, 5, 95),
+    ("pp_f16_no_qlens", 2, 8, 2, 64, [64, 129], None, 128, "f16", True, 3, 96),
+    ("pp_q4_0_long", 1, 8, 2, 64, [4500], [64], 128, "q4_0", True, 72, 97),
+]
+
+
+@pytest.mark.parametrize("case", PAGED_PREFILL, ids=[c[0] for c in PAGED_PREFILL])
+def test_prefill_paged_matches_oracle(case):
+    name, B, Hq, Hkv, Sq, lens, q_lens, D, kv, causal, max_pages, seed = case
+    say(f"paged prefill {case}")
+    w = wl(name, B, Hq, Hkv, Sq, max_pages * 64, D, kv, causal, None, seed)
+    x = W.generate(w)
+    q = to_dev(x.q, w.q_dtype)
+    kp, vp, table = _scatter_pages(x, B, max_pages, seed)
+    SENTINEL = 7.0
+    out = torch.full_like(q, SENTINEL)
+    ql_dev = None if q_lens is None else torch.tensor(q_lens, dtype=torch.int32, device="cuda")
+    fa.prefill_paged(q, to_dev(kp, w.kv), to_dev(vp, w.kv), torch.from_numpy(table).cuda(),
+                     torch.tensor(lens, dtype=torch.int32, device="cuda"), ql_dev,
+                     causal=causal, scale=w.scale, out=out)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy()
+    for b in range(B):
+        n, m = lens[b], Sq if q_lens is None else q_lens[b]
+        assert np.all(got[b, m:] == SENTINEL), (name, b, "rows past the chunk were written")
+        if m == 0:
+            continue
+        if n == 0:                      # no keys: every row's output is 0
+            assert np.all(got[b, :m] == 0.0), (name, b)
+            continue
+        ref = oracle.attention(x.q[b:b + 1, :m], x.k[b:b + 1, :n], x.v[b:b + 1, :n],
+                               q_dtype=w.q_dtype, kv_dtype=w.kv, causal=causal,
+                               offset=n - m, scale=w.scale)
+        err = float(np.max(np.abs(got[b, :m] - ref[0])))
+        assert err <= TOL[w.kv], (name, b, n, m, err)
+
+
+@pytest.mark.parametrize("wname", ["prefill_16k_f16", "prefill_16k_q4_0"])
+def test_prefill_paged_in_order_equals_contiguous(wname):
+    """The full-size prefill with its cache read as in-order pages gives the same bits as the
+    contiguous call: only where a tile's bytes come from differs."""
+    w = W.WORKLOADS[wname]
+    say(f"paged prefill (in order) vs contiguous {w}")
+    x = W.generate(w)
+    q, k, v = to_dev(x.q, w.q_dtype), to_dev(x.k, w.kv), to_dev(x.v, w.kv)
+    a = fa.prefill(q, k, v, causal=True, offset=w.causal_offset, scale=w.scale)
+    per = w.Sk // 64
+    kp = k.view(w.B * per, 64, w.Hkv, -1)
+    vp = v.view(w.B * per, 64, w.Hkv, -1)
+    table = torch.arange(w.B * per, dtype=torch.int32, device="cuda").view(w.B, per)
+    lens = torch.full((w.B,), w.Sk, dtype=torch.int32, device="cuda")
+    qlens = torch.full((w.B,), w.Sq, dtype=torch.int32, device="cuda")
+    b = fa.prefill_paged(q, kp, vp, table, lens, qlens, causal=True, scale=w.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
