@@ -61,15 +61,39 @@ __device__ __forceinline__ int64_t head_off(const DecodeParams &p, int b, int kv
 // Byte offset from the head's key-0 row to the 64-key tile at key k0 (a multiple of kBN); rows
 // inside a tile are grow bytes apart in both layouts. A page index outside the page array is
 // clamped into it: the result is then wrong, but every load stays inside the buffers.
-__device__ __forceinline__ int64_t tile_off(const DecodeParams &p, int b, int64_t k0,
-                                            uint32_t grow)
-{
-    if (!p.block_table)
-        return k0 * grow;
-    int pg = p.block_table[(int64_t)b * p.max_pages + k0 / kBN];
-    pg = min(max(pg, 0), p.n_pages - 1);
-    return (int64_t)pg * kBN * grow;
-}
+// Paged: the offsets come from a run of up to 64 block-table entries held one per lane,
+// fetched with one vector load when a tile falls outside it (at the first tile, then at most
+// once per 64 table entries); a tile's page is taken with v_readlane, so no memory access
+// sits between a tile's transfers. (A scalar load per tile would either wait in front of the
+// transfers or, left in flight, turn every LDS wait of the compute into a wait for it, since
+// scalar loads complete out of order.)
+struct PageRun {
+    int base = -(1 << 30);  // table index held by lane 0 (wave-uniform); none held yet
+    int v = 0;              // lane l: entry base + l
+    // fetch the run at tile k0 ahead of time (at kernel start, beside the sequence-length read,
+    // so the two latencies overlap instead of adding up)
+    __device__ __forceinline__ void prime(const DecodeParams &p, int b, int64_t k0, int lane)
+    {
+        if (p.block_table && p.max_pages > 0) {
+            base = (int)min(k0 / kBN, (int64_t)p.max_pages - 1);
+            v = p.block_table[(int64_t)b * p.max_pages + min(base + lane, p.max_pages - 1)];
+        }
+    }
+    __device__ __forceinline__ int64_t off(const DecodeParams &p, int b, int64_t k0,
+                                           uint32_t grow, int lane)
+    {
+        if (!p.block_table)
+            return k0 * grow;
+        const int j = (int)min(k0 / kBN, (int64_t)p.max_pages - 1);
+        if (j < base || j >= base + 64) {
+            base = j;
+            v = p.block_table[(int64_t)b * p.max_pages + min(j + lane, p.max_pages - 1)];
+        }
+        int pg = __builtin_amdgcn_readlane(v, j - base);
+        pg = min(max(pg, 0), p.n_pages - 1);
+        return (int64_t)pg * kBN * grow;
+    }
+};
 
 // One 64-key tile of the split: each wave takes 16 keys.
 template <int D, bool BF>
@@ -212,6 +236,8 @@ __global__ __launch_bounds__(kThreads, kDecodeOccupancy<KV>) void decode_split_k
     rest /= a.Hkv;
     const int s = rest % p.n_split;
     const int b = rest / p.n_split;
+    PageRun pr;
+    pr.prime(p, b, (int64_t)s * p.split_len, lane);
     const SeqView sv = seq_view(p, b);
 
     const int64_t ks = (int64_t)s * p.split_len;
@@ -253,7 +279,7 @@ __global__ __launch_bounds__(kThreads, kDecodeOccupancy<KV>) void decode_split_k
     for (int u = 0; u < NSETS; ++u)
         ld[u].init(a.k, a.v, head_off(p, b, kvh, D * 2) / (D * 2), a.Hkv, (int)sv.Sk, t);
     const uint32_t grow = (uint32_t)a.Hkv * D * 2;
-    auto load_set = [&](int u, int k0) { ld[u].load(k0, tile_off(p, b, k0, grow)); };
+    auto load_set = [&](int u, int k0) { ld[u].load(k0, pr.off(p, b, k0, grow, t & 63)); };
     uint16_t *lk = lds, *lv = lds + Geo::kElems;
     int kb0 = 0;
     if (nb >= 2 * NSETS) {
@@ -347,6 +373,8 @@ __global__ __launch_bounds__(kThreads, 2) void decode_q4_kernel(DecodeParams p)
     rest /= a.Hkv;
     const int s = rest % p.n_split;
     const int b = rest / p.n_split;
+    PageRun pr;
+    pr.prime(p, b, (int64_t)s * p.split_len, lane);
     const SeqView sv = seq_view(p, b);
 
     const int64_t ks = (int64_t)s * p.split_len;
@@ -397,7 +425,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_q4_kernel(DecodeParams p)
         const int k0 = (int)ks + kb * kBN;
         const uint32_t last = (uint32_t)min((int64_t)kBN - 1, sv.Sk - 1 - k0);
         const uint32_t stage = raw0 + (uint32_t)((kb % kRS) * 2 * RAW_T);
-        const int64_t toff = tile_off(p, b, k0, grow);
+        const int64_t toff = pr.off(p, b, k0, grow, lane);
 #pragma unroll
         for (int m = 0; m < NIW; ++m) {
             const int i = min(wave + 4 * m, NI - 1);
@@ -836,6 +864,8 @@ __global__ __launch_bounds__(kThreads, Q4G<D>::OCC) void decode_q4g_kernel(Decod
     const int s = rest % p.n_split;
     const int b = rest / p.n_split;
     const int kvh = grp * G::NH + wave;
+    PageRun pr;
+    pr.prime(p, b, (int64_t)s * p.split_len, lane);
     const SeqView sv = seq_view(p, b);
 
     const int64_t ks = (int64_t)s * p.split_len;
@@ -864,7 +894,7 @@ __global__ __launch_bounds__(kThreads, Q4G<D>::OCC) void decode_q4g_kernel(Decod
         const int64_t k0 = ks + (int64_t)kb * kBN;
         const uint32_t last = (uint32_t)min((int64_t)kBN - 1, sv.Sk - 1 - k0);
         const uint32_t st = lds0 + (uint32_t)((kb % NSTG) * G::STAGE);
-        const int64_t toff = tile_off(p, b, k0, grow);
+        const int64_t toff = pr.off(p, b, k0, grow, lane);
 #pragma unroll
         for (int m = 0; m < NIW; ++m) {
             const int i = min(wave + 4 * m, G::NI - 1);
@@ -960,6 +990,8 @@ __global__ __launch_bounds__(kThreads, 2) void decode_q4w_kernel(DecodeParams p)
     rest /= a.Hkv;
     const int s = rest % p.n_split;
     const int b = rest / p.n_split;
+    PageRun pr;
+    pr.prime(p, b, (int64_t)s * p.split_len, lane);
     const SeqView sv = seq_view(p, b);
 
     const int64_t ks = (int64_t)s * p.split_len;
@@ -987,7 +1019,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_q4w_kernel(DecodeParams p)
         const int64_t k0 = ks + (int64_t)(wave + 4 * i) * kBN;
         const uint32_t st = wl0 + (uint32_t)((i & 1) * W::STAGE);
         const int64_t last = min((int64_t)kBN - 1, sv.Sk - 1 - k0);
-        const int64_t toff = tile_off(p, b, k0, grow);
+        const int64_t toff = pr.off(p, b, k0, grow, lane);
         if (last == kBN - 1) {
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt)

@@ -11,7 +11,9 @@ One step = one pass of the whole path over resident inputs:
   * the q4_0 cache writer: fa_quantize_q4_0 of the prefill workload's f16 K and V (16384
     keys x 8 heads x 128) into q4_0 blocks (reported, HBM-bound);
   * the decode over a paged cache: the same 4 x 32768 q4_0 keys as 2048 pages of 64 keys in
-    a shuffled order (fa_decode_paged; reported, HBM-bound).
+    a shuffled order (fa_decode_paged; reported, HBM-bound);
+  * the prefill over a paged cache: the f16 prefill's 16384 keys as 256 shuffled pages
+    (fa_prefill_paged; reported, MFMA-bound).
 Before each call a 1 GiB buffer is read so that neither call finds its inputs in the 256 MB
 last-level cache (the decode working set, 151 MB, would otherwise stay resident). The flush
 reads rather than writes: a written flush leaves up to 256 MB of dirty lines in that cache,
@@ -183,6 +185,17 @@ def main():
     table = table.view(wd.B, per)
     lens = torch.full((wd.B,), wd.Sk, dtype=torch.int32, device=dev)
     do2 = torch.empty_like(dq)
+    # the prefill cache the same way
+    pper = wp.Sk // 64
+    porder = torch.from_numpy(np.random.default_rng(8).permutation(wp.B * pper)).to(dev)
+    pkp = pk.view(wp.B * pper, 64, wp.Hkv, -1)[porder].contiguous()
+    pvp = pv.view(wp.B * pper, 64, wp.Hkv, -1)[porder].contiguous()
+    ptable = torch.empty(wp.B * pper, dtype=torch.int32, device=dev)
+    ptable[porder] = torch.arange(wp.B * pper, dtype=torch.int32, device=dev)
+    ptable = ptable.view(wp.B, pper)
+    plens = torch.full((wp.B,), wp.Sk, dtype=torch.int32, device=dev)
+    pqlens = torch.full((wp.B,), wp.Sq, dtype=torch.int32, device=dev)
+    po2 = torch.empty_like(pq)
     wk = torch.empty(pk.numel() // 32 * 18, dtype=torch.uint8, device=dev)
     wv = torch.empty_like(wk)
     wbytes = (pk.numel() + pv.numel()) * 2 + wk.numel() + wv.numel()
@@ -223,7 +236,12 @@ def main():
         fa.decode_paged(dq, dkp, dvp, table, lens, causal=True, scale=wd.scale, out=do2,
                         workspace=ws, stream=stream)
 
-    calls = [prefill, decode, prefill_q4, prefill_q4_unfused, quantize, decode_paged]
+    def prefill_paged():
+        fa.prefill_paged(pq, pkp, pvp, ptable, plens, pqlens, causal=True, scale=wp.scale,
+                         out=po2, stream=stream)
+
+    calls = [prefill, decode, prefill_q4, prefill_q4_unfused, quantize, decode_paged,
+             prefill_paged]
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * len(calls))]
           for _ in range(args.steps)]
 
@@ -259,6 +277,7 @@ def main():
     u_ms = np.array([e[6].elapsed_time(e[7]) for e in ev])
     w_ms = np.array([e[8].elapsed_time(e[9]) for e in ev])
     g_ms = np.array([e[10].elapsed_time(e[11]) for e in ev])
+    pp_ms = np.array([e[12].elapsed_time(e[13]) for e in ev])
     qflops = W.attention_flops(wq)
     flops = W.attention_flops(wp)
     dbytes = W.algorithmic_bytes(wd)
@@ -321,6 +340,12 @@ def main():
                          "unit": "GB/s", "ms_mean": round(float(g_ms.mean()), 5),
                          "frac_of_hbm_peak": round(dbytes / (float(g_ms.mean()) * 1e-3) / 1e9
                                                    / PEAK_HBM_GBS, 4)},
+        "prefill_paged": {"what": "the prefill workload over its cache as 256 shuffled pages of "
+                                  "64 keys (fa_prefill_paged)",
+                          "tflops": round(flops / (float(pp_ms.mean()) * 1e-3) / 1e12, 3),
+                          "ms_mean": round(float(pp_ms.mean()), 5),
+                          "frac_of_mfma_peak": round(flops / (float(pp_ms.mean()) * 1e-3) / 1e12
+                                                     / PEAK_MFMA_F16_TFLOPS, 4)},
         "quantize_q4_0": {"what": "fa_quantize_q4_0 of f16 K and V [1, 16384, 8, 128] (two "
                                   "launches)",
                           "gbs": round(wbytes / (float(w_ms.mean()) * 1e-3) / 1e9, 1),
