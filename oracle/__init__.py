@@ -44,12 +44,16 @@ def _shapes(q, k, kv_dtype):
     Bk, Sk, Hkv = k.shape[:3]
     if Bk != B:
         raise ValueError("q and k batch sizes disagree")
-    if _code(kv_dtype) == Q4_0:
-        if D % 32 or k.shape[3] != D // 32 * 18:
-            raise ValueError("q4_0 rows must hold D/32 blocks of 18 bytes")
-    elif k.shape[3] != D:
-        raise ValueError("k head dim disagrees with q")
+    _check_rows(k, kv_dtype, D)
     return B, Sq, Hq, Sk, Hkv, D
+
+
+def _check_rows(x, dtype, D):
+    if _code(dtype) == Q4_0:
+        if D % 32 or x.shape[3] != D // 32 * 18:
+            raise ValueError("q4_0 rows must hold D/32 blocks of 18 bytes")
+    elif x.shape[3] != D:
+        raise ValueError("cache head dim disagrees with q")
 
 
 class Oracle:
@@ -60,14 +64,17 @@ class Oracle:
         i64, i32, f32, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_float, ctypes.c_void_p
         lib.orc_attention.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, i32,
                                       i64, f32, vp, i64, vp, i32]
+        lib.orc_attention_kv.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32,
+                                         i32, i32, i64, f32, vp, i64, vp, i32]
         lib.orc_probs.argtypes = [vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, i32, i64,
                                   f32, i64, vp]
         lib.orc_dequant_q4_0.argtypes = [vp, i64, vp, vp]
         lib.orc_half_to_float.argtypes = [vp, i64, vp]
         lib.orc_float_to_half.argtypes = [vp, i64, vp]
         lib.orc_quantize_q4_0.argtypes = [vp, i32, i64, vp]
-        for fn in (lib.orc_attention, lib.orc_probs, lib.orc_dequant_q4_0,
-                   lib.orc_half_to_float, lib.orc_float_to_half, lib.orc_quantize_q4_0):
+        for fn in (lib.orc_attention, lib.orc_attention_kv, lib.orc_probs,
+                   lib.orc_dequant_q4_0, lib.orc_half_to_float, lib.orc_float_to_half,
+                   lib.orc_quantize_q4_0):
             fn.restype = i32
         self.path = path
         self.lib = lib
@@ -75,17 +82,19 @@ class Oracle:
     def attention(self, q: np.ndarray, k: np.ndarray, v: np.ndarray, *, q_dtype, kv_dtype,
                   causal: bool = True, offset: Optional[int] = None,
                   scale: Optional[float] = None, rows: Optional[Sequence[int]] = None,
-                  threads: int = 0) -> np.ndarray:
+                  threads: int = 0, v_dtype=None) -> np.ndarray:
         """Attention output in float32.
 
         Without `rows` the result has q's [B, Sq, Hq, D] shape. With `rows` (flattened indices
         (b * Sq + i) * Hq + h) the result is [len(rows), D]. offset defaults to Sk - Sq and
-        scale to 1/sqrt(D).
+        scale to 1/sqrt(D). kv_dtype is K's cache type and, unless v_dtype is given, V's.
         """
         q, k, v = _c(q), _c(k), _c(v)
         B, Sq, Hq, Sk, Hkv, D = _shapes(q, k, kv_dtype)
-        if v.shape != k.shape:
+        v_dtype = kv_dtype if v_dtype is None else v_dtype
+        if v.shape[:3] != k.shape[:3]:
             raise ValueError("k and v shapes differ")
+        _check_rows(v, v_dtype, D)
         offset = Sk - Sq if offset is None else int(offset)
         scale = 1.0 / np.sqrt(D) if scale is None else float(scale)
         if rows is None:
@@ -96,9 +105,10 @@ class Oracle:
             n_rows = rows_arr.size
             out = np.empty((n_rows, D), np.float32)
             rptr = _ptr(rows_arr)
-        rc = self.lib.orc_attention(_ptr(q), _ptr(k), _ptr(v), _code(q_dtype), _code(kv_dtype),
-                                    B, Hq, Hkv, Sq, Sk, D, int(bool(causal)), offset, scale,
-                                    rptr, n_rows, _ptr(out), int(threads))
+        rc = self.lib.orc_attention_kv(_ptr(q), _ptr(k), _ptr(v), _code(q_dtype),
+                                       _code(kv_dtype), _code(v_dtype), B, Hq, Hkv, Sq, Sk, D,
+                                       int(bool(causal)), offset, scale, rptr, n_rows,
+                                       _ptr(out), int(threads))
         if rc:
             raise ValueError(f"oracle rejected the arguments (code {rc})")
         return out

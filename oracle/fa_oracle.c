@@ -301,8 +301,17 @@ static void row_output(const problem *p, int64_t r, float *prob, float *o)
     }
 }
 
-static int check_args(const void *q, const void *k, const void *v, int q_dtype, int kv_dtype,
-                      int B, int Hq, int Hkv, int Sq, int Sk, int D)
+static int check_cache_dtype(int dtype, int D)
+{
+    if (dtype != ORC_F16 && dtype != ORC_BF16 && dtype != ORC_Q4_0)
+        return ORC_ERR_ARG;
+    if (dtype == ORC_Q4_0 && D % 32)
+        return ORC_ERR_ARG;
+    return ORC_OK;
+}
+
+static int check_args(const void *q, const void *k, const void *v, int q_dtype, int k_dtype,
+                      int v_dtype, int B, int Hq, int Hkv, int Sq, int Sk, int D)
 {
     if (!q || !k || !v)
         return ORC_ERR_ARG;
@@ -310,25 +319,27 @@ static int check_args(const void *q, const void *k, const void *v, int q_dtype, 
         return ORC_ERR_ARG;
     if (q_dtype != ORC_F16 && q_dtype != ORC_BF16)
         return ORC_ERR_ARG;
-    if (kv_dtype != ORC_F16 && kv_dtype != ORC_BF16 && kv_dtype != ORC_Q4_0)
-        return ORC_ERR_ARG;
-    if (kv_dtype == ORC_Q4_0 && D % 32)
+    if (check_cache_dtype(k_dtype, D) || check_cache_dtype(v_dtype, D))
         return ORC_ERR_ARG;
     return ORC_OK;
 }
 
 /*
  * Attention for a list of query rows. Q is [B, Sq, Hq, D] stored as q_dtype; K and V are
- * [B, Sk, Hkv, D] stored as kv_dtype (q4_0: [B, Sk, Hkv, D/32] blocks of 18 bytes).
+ * [B, Sk, Hkv, D] stored as k_dtype and v_dtype (q4_0: [B, Sk, Hkv, D/32] blocks of 18
+ * bytes). The two cache types are independent settings (mi210-llm-stack, "FlashAttention
+ * on gfx90a", sets them with one flag per cache, -ctk and -ctv): each tensor is widened to
+ * f32 by its own type, and nothing after that depends on either type.
  * rows[] holds flattened row indices (b * Sq + i) * Hq + h; with rows == NULL every row is
  * computed in order and `out` takes the [B, Sq, Hq, D] layout. out is f32 [n_rows, D].
  * threads <= 0 lets OpenMP choose.
  */
-int orc_attention(const void *q, const void *k, const void *v, int q_dtype, int kv_dtype,
-                  int B, int Hq, int Hkv, int Sq, int Sk, int D, int causal, int64_t offset,
-                  float scale, const int64_t *rows, int64_t n_rows, float *out, int threads)
+int orc_attention_kv(const void *q, const void *k, const void *v, int q_dtype, int k_dtype,
+                     int v_dtype, int B, int Hq, int Hkv, int Sq, int Sk, int D, int causal,
+                     int64_t offset, float scale, const int64_t *rows, int64_t n_rows,
+                     float *out, int threads)
 {
-    int rc = check_args(q, k, v, q_dtype, kv_dtype, B, Hq, Hkv, Sq, Sk, D);
+    int rc = check_args(q, k, v, q_dtype, k_dtype, v_dtype, B, Hq, Hkv, Sq, Sk, D);
     if (rc)
         return rc;
     if (!out)
@@ -342,8 +353,8 @@ int orc_attention(const void *q, const void *k, const void *v, int q_dtype, int 
 
     problem p = {0};
     p.Q = upcast_rows(q, q_dtype, total, D);
-    p.K = upcast_rows(k, kv_dtype, (int64_t)B * Sk * Hkv, D);
-    p.V = upcast_rows(v, kv_dtype, (int64_t)B * Sk * Hkv, D);
+    p.K = upcast_rows(k, k_dtype, (int64_t)B * Sk * Hkv, D);
+    p.V = upcast_rows(v, v_dtype, (int64_t)B * Sk * Hkv, D);
     rc = (p.Q && p.K && p.V) ? ORC_OK : ORC_ERR_NOMEM;
     p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.Sq = Sq; p.Sk = Sk; p.D = D;
     p.causal = causal; p.offset = offset; p.scale = scale;
@@ -374,12 +385,21 @@ int orc_attention(const void *q, const void *k, const void *v, int q_dtype, int 
     return rc;
 }
 
+/* orc_attention_kv with one type for both caches. */
+int orc_attention(const void *q, const void *k, const void *v, int q_dtype, int kv_dtype,
+                  int B, int Hq, int Hkv, int Sq, int Sk, int D, int causal, int64_t offset,
+                  float scale, const int64_t *rows, int64_t n_rows, float *out, int threads)
+{
+    return orc_attention_kv(q, k, v, q_dtype, kv_dtype, kv_dtype, B, Hq, Hkv, Sq, Sk, D, causal,
+                            offset, scale, rows, n_rows, out, threads);
+}
+
 /* Softmax probabilities of one query row over all Sk keys (zeros for keys it cannot see). */
 int orc_probs(const void *q, const void *k, int q_dtype, int kv_dtype,
               int B, int Hq, int Hkv, int Sq, int Sk, int D, int causal, int64_t offset,
               float scale, int64_t row, float *p_out)
 {
-    int rc = check_args(q, k, k, q_dtype, kv_dtype, B, Hq, Hkv, Sq, Sk, D);
+    int rc = check_args(q, k, k, q_dtype, kv_dtype, kv_dtype, B, Hq, Hkv, Sq, Sk, D);
     if (rc)
         return rc;
     const int64_t total = (int64_t)B * Sq * Hq;

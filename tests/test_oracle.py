@@ -89,14 +89,24 @@ BRUTE_CASES = [
     (2, 2, 2, 5, 7, 32, "q4_0", False, 0),
     (1, 3, 3, 4, 4, 8, "f16", True, 10),
     (1, 6, 2, 3, 8, 8, "bf16", False, 0),
+    # mixed caches: K and V of different types (a tenth entry is V's type); q4_0 K with f16 V
+    # first, so the planted mistake below (V read as K's type) is caught by a case where that
+    # reading stays inside V's buffer (an f16 row holds more bytes than a q4_0 row)
+    (2, 2, 1, 4, 6, 32, "q4_0", False, 0, "f16"),
+    (1, 4, 2, 5, 7, 32, "f16", True, 2, "q4_0"),
 ]
 
 
 def check_brute_force(orc, case):
-    B, Hq, Hkv, Sq, Sk, D, kv, causal, offset = case
+    B, Hq, Hkv, Sq, Sk, D, kv, causal, offset = case[:9]
+    vkv = case[9] if len(case) > 9 else kv
     w, x = make(B, Hq, Hkv, Sq, Sk, D, kv, causal, offset, seed=sum(case[:6]))
-    got = run(orc, w, x)
-    ref = brute_force(decode64(x.q, w.q_dtype, D), decode64(x.k, kv, D), decode64(x.v, kv, D),
+    v = x.v
+    if vkv != kv:                     # V from a workload of V's type (same shape and seed)
+        v = make(B, Hq, Hkv, Sq, Sk, D, vkv, causal, offset, seed=sum(case[:6]) + 1)[1].v
+    got = orc.attention(x.q, x.k, v, q_dtype=w.q_dtype, kv_dtype=kv, v_dtype=vkv, causal=causal,
+                        offset=w.causal_offset, scale=w.scale)
+    ref = brute_force(decode64(x.q, w.q_dtype, D), decode64(x.k, kv, D), decode64(v, vkv, D),
                       causal, w.causal_offset, w.scale)
     np.testing.assert_allclose(got, ref, rtol=0, atol=2e-6)
 
@@ -455,6 +465,9 @@ MUTANTS = [
     ("writer nibbles swapped", "blk[2 + t] = (uint8_t)(c[t] | (c[t + 16] << 4));",
      "blk[2 + t] = (uint8_t)(c[t + 16] | (c[t] << 4));"),
     ("writer clamp at 16", "v = v < 0 ? 0 : (v > 15 ? 15 : v);", "v = v < 0 ? 0 : (v > 16 ? 16 : v);"),
+    # the mixed-cache entry ignoring V's own type (caught by the q4_0-K / f16-V brute-force
+    # case, where V's bytes read as q4_0 stay inside its buffer)
+    ("V widened by K's type", "p.V = upcast_rows(v, v_dtype,", "p.V = upcast_rows(v, k_dtype,"),
 ]
 
 
