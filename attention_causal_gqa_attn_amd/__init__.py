@@ -21,6 +21,7 @@ from typing import Optional
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 
 FA_KV_F16, FA_KV_BF16, FA_KV_Q4_0 = 0, 1, 2
+FA_KV_F16_Q4_0, FA_KV_Q4_0_F16 = 3, 4          # mixed caches: (K type, V type)
 FA_SRC_F32, FA_SRC_F16, FA_SRC_BF16 = 0, 1, 2
 Q4_0_BYTES = 18
 
@@ -142,15 +143,38 @@ def _torch():
     return torch
 
 
-def _kv_code(k) -> int:
+def _one_code(t) -> int:
     torch = _torch()
-    if k.dtype == torch.float16:
+    if t.dtype == torch.float16:
         return FA_KV_F16
-    if k.dtype == torch.bfloat16:
+    if t.dtype == torch.bfloat16:
         return FA_KV_BF16
-    if k.dtype == torch.uint8:
+    if t.dtype == torch.uint8:
         return FA_KV_Q4_0
-    raise TypeError(f"unsupported K/V dtype {k.dtype}")
+    raise TypeError(f"unsupported K/V dtype {t.dtype}")
+
+
+def _kv_code(k, v=None) -> int:
+    """The cache code of K and V (float16, bfloat16, or uint8 q4_0 blocks); K and V of
+    different types give a mixed code (f16 with q4_0 only)."""
+    ck = _one_code(k)
+    cv = ck if v is None else _one_code(v)
+    if ck == cv:
+        return ck
+    pair = {(FA_KV_F16, FA_KV_Q4_0): FA_KV_F16_Q4_0, (FA_KV_Q4_0, FA_KV_F16): FA_KV_Q4_0_F16}
+    if (ck, cv) not in pair:
+        raise TypeError(f"unsupported K/V dtype pair {k.dtype}, {v.dtype}")
+    return pair[(ck, cv)]
+
+
+def _row_width(code, D) -> int:
+    return D // 32 * Q4_0_BYTES if code == FA_KV_Q4_0 else D
+
+
+def _kv_parts(kv):
+    """(K type, V type) of a cache code."""
+    return {FA_KV_F16_Q4_0: (FA_KV_F16, FA_KV_Q4_0),
+            FA_KV_Q4_0_F16: (FA_KV_Q4_0, FA_KV_F16)}.get(kv, (kv, kv))
 
 
 def _stream(t, stream) -> int:
@@ -164,23 +188,27 @@ def _sizes(q, k, v, kv):
         raise ValueError("q, k, v must be 4-d: [B, S, H, D] (q4_0: [B, S, H, D/32*18] bytes)")
     if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
         raise ValueError("q, k, v must be contiguous")
-    if k.shape != v.shape:
+    if k.shape[:3] != v.shape[:3]:
         raise ValueError("k and v shapes differ")
     B, Sq, Hq, D = q.shape
-    Bk, Sk, Hkv, Dk = k.shape
+    Bk, Sk, Hkv, _ = k.shape
     if Bk != B:
         raise ValueError("batch sizes differ")
-    want = D // 32 * Q4_0_BYTES if kv == FA_KV_Q4_0 else D
-    if Dk != want:
-        raise ValueError(f"k/v last dim {Dk}, expected {want}")
+    _check_widths(k, v, kv, D)
     return B, Hq, Hkv, Sq, Sk, D
+
+
+def _check_widths(k, v, kv, D):
+    for name, t, code in (("k", k, _kv_parts(kv)[0]), ("v", v, _kv_parts(kv)[1])):
+        if t.shape[-1] != _row_width(code, D):
+            raise ValueError(f"{name} last dim {t.shape[-1]}, expected {_row_width(code, D)}")
 
 
 def prefill(q, k, v, *, causal: bool = True, offset: Optional[int] = None,
             scale: Optional[float] = None, out=None, stream=None):
     """O = softmax(scale * Q K^T + causal mask) V via fa_prefill. K/V dtype selects the cache
     type (float16, bfloat16, or uint8 q4_0 blocks). offset defaults to Sk - Sq."""
-    kv = _kv_code(k)
+    kv = _kv_code(k, v)
     B, Hq, Hkv, Sq, Sk, D = _sizes(q, k, v, kv)
     offset = Sk - Sq if offset is None else int(offset)
     scale = D ** -0.5 if scale is None else float(scale)
@@ -202,7 +230,7 @@ def decode(q, k, v, *, causal: bool = True, offset: Optional[int] = None,
     """Split-K decode via fa_decode (Sq * Hq / Hkv <= 16). A workspace tensor of
     decode_workspace_bytes(...) bytes is allocated when none is given."""
     torch = _torch()
-    kv = _kv_code(k)
+    kv = _kv_code(k, v)
     B, Hq, Hkv, Sq, Sk, D = _sizes(q, k, v, kv)
     offset = Sk - Sq if offset is None else int(offset)
     scale = D ** -0.5 if scale is None else float(scale)
@@ -232,9 +260,11 @@ def _paged_sizes(q, k_pages, v_pages, block_table, seq_lens, q_lens=None):
         raise ValueError("q and the pages must be contiguous")
     B, Sq, Hq, D = q.shape
     n_pages, _, Hkv, _ = k_pages.shape
-    if (block_table.shape[0] != B or seq_lens.numel() != B or v_pages.shape != k_pages.shape
+    if (block_table.shape[0] != B or seq_lens.numel() != B
+            or v_pages.shape[:3] != k_pages.shape[:3]
             or (q_lens is not None and q_lens.numel() != B)):
         raise ValueError("block_table, seq_lens, q_lens and pages disagree with q")
+    _check_widths(k_pages, v_pages, _kv_code(k_pages, v_pages), D)
     return B, Hq, Hkv, Sq, D, block_table.shape[1], n_pages
 
 
@@ -245,7 +275,7 @@ def prefill_paged(q, k_pages, v_pages, block_table, seq_lens, q_lens=None, *,
     [0, q_lens[b]) of q[b], its last q_lens[b] positions; rows past them of out are not
     written (out defaults to zeros)."""
     torch = _torch()
-    kv = _kv_code(k_pages)
+    kv = _kv_code(k_pages, v_pages)
     B, Hq, Hkv, Sq, D, max_pages, n_pages = _paged_sizes(q, k_pages, v_pages, block_table,
                                                          seq_lens, q_lens)
     scale = D ** -0.5 if scale is None else float(scale)
@@ -266,7 +296,7 @@ def decode_paged(q, k_pages, v_pages, block_table, seq_lens, *, causal: bool = T
     Hkv, D] (q4_0: uint8 [n_pages, 64, Hkv, D/32*18]); block_table: int32 [B, max_pages];
     seq_lens: int32 [B]. Sequence b's Sq queries are its last Sq positions."""
     torch = _torch()
-    kv = _kv_code(k_pages)
+    kv = _kv_code(k_pages, v_pages)
     B, Hq, Hkv, Sq, D, max_pages, n_pages = _paged_sizes(q, k_pages, v_pages, block_table,
                                                          seq_lens)
     scale = D ** -0.5 if scale is None else float(scale)

@@ -5,6 +5,7 @@
 #include <cstdint>
 
 #include "../../include/fa.h"
+#include "fa_device.h"
 #include "fa_kernels.h"
 
 namespace {
@@ -32,7 +33,8 @@ int check_attention(const void *q, const void *k, const void *v, void *o, int B,
                     int Sq, int Sk, int D, int causal, int64_t offset, float scale, int kv_dtype,
                     fa::AttnArgs &a)
 {
-    if (kv_dtype != FA_KV_F16 && kv_dtype != FA_KV_BF16 && kv_dtype != FA_KV_Q4_0)
+    if (kv_dtype != FA_KV_F16 && kv_dtype != FA_KV_BF16 && kv_dtype != FA_KV_Q4_0 &&
+        kv_dtype != FA_KV_F16_Q4_0 && kv_dtype != FA_KV_Q4_0_F16)
         return FA_ERR_DTYPE;
     if (B < 0 || Sq < 0 || Sk < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || Hq % Hkv != 0)
         return FA_ERR_SHAPE;
@@ -49,8 +51,10 @@ int check_attention(const void *q, const void *k, const void *v, void *o, int B,
         return FA_ERR_UNSUPPORTED;
     if ((nq > 0 && (!q || !o)) || (nk > 0 && (!k || !v)))
         return FA_ERR_NULL;
-    const uintptr_t kv_align = kv_dtype == FA_KV_Q4_0 ? 4 : 16;
-    if (!aligned(q, 16) || !aligned(o, 16) || !aligned(k, kv_align) || !aligned(v, kv_align))
+    // q4_0 blocks need 4-byte alignment, 16-bit caches 16
+    const uintptr_t k_align = fa::kv_k(kv_dtype) == fa::KV_Q4_0 ? 4 : 16;
+    const uintptr_t v_align = fa::kv_v(kv_dtype) == fa::KV_Q4_0 ? 4 : 16;
+    if (!aligned(q, 16) || !aligned(o, 16) || !aligned(k, k_align) || !aligned(v, v_align))
         return FA_ERR_ALIGN;
 
     // offsets beyond these bounds change nothing: every key visible, or none

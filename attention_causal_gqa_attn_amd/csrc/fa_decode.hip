@@ -277,9 +277,13 @@ __global__ __launch_bounds__(kThreads, kDecodeOccupancy<KV>) void decode_split_k
     TileLoader<D, KV> ld[NSETS];
 #pragma unroll
     for (int u = 0; u < NSETS; ++u)
-        ld[u].init(a.k, a.v, head_off(p, b, kvh, D * 2) / (D * 2), a.Hkv, (int)sv.Sk, t);
-    const uint32_t grow = (uint32_t)a.Hkv * D * 2;
-    auto load_set = [&](int u, int k0) { ld[u].load(k0, pr.off(p, b, k0, grow, t & 63)); };
+        ld[u].init(a.k, a.v, head_off(p, b, kvh, 1), a.Hkv, (int)sv.Sk, t);
+    // bytes between consecutive keys of K and of V (they differ for mixed caches)
+    const uint32_t growk = (uint32_t)a.Hkv * kv_row_bytes(kv_k(KV), D);
+    const uint32_t growv = (uint32_t)a.Hkv * kv_row_bytes(kv_v(KV), D);
+    auto load_set = [&](int u, int k0) {
+        ld[u].load(k0, pr.off(p, b, k0, growk, lane), pr.off(p, b, k0, growv, lane));
+    };
     uint16_t *lk = lds, *lv = lds + Geo::kElems;
     int kb0 = 0;
     if (nb >= 2 * NSETS) {
@@ -1272,12 +1276,20 @@ hipError_t launch_decode(const AttnArgs &a, const DecodeGrid &g, void *workspace
             return launch<128, KV_F16>(p, g.n_wg, stream);
         if (a.kv == KV_BF16)
             return launch<128, KV_BF16>(p, g.n_wg, stream);
+        if (a.kv == KV_F16_Q4_0)
+            return launch<128, KV_F16_Q4_0>(p, g.n_wg, stream);
+        if (a.kv == KV_Q4_0_F16)
+            return launch<128, KV_Q4_0_F16>(p, g.n_wg, stream);
         return launch<128, KV_Q4_0>(p, g.n_wg, stream);
     }
     if (a.kv == KV_F16)
         return launch<64, KV_F16>(p, g.n_wg, stream);
     if (a.kv == KV_BF16)
         return launch<64, KV_BF16>(p, g.n_wg, stream);
+    if (a.kv == KV_F16_Q4_0)
+        return launch<64, KV_F16_Q4_0>(p, g.n_wg, stream);
+    if (a.kv == KV_Q4_0_F16)
+        return launch<64, KV_Q4_0_F16>(p, g.n_wg, stream);
     return launch<64, KV_Q4_0>(p, g.n_wg, stream);
 }
 

@@ -23,7 +23,22 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 
-enum { KV_F16 = 0, KV_BF16 = 1, KV_Q4_0 = 2 };
+// cache types; the last two are mixed (K type, V type): f16 K with q4_0 V and the reverse
+enum { KV_F16 = 0, KV_BF16 = 1, KV_Q4_0 = 2, KV_F16_Q4_0 = 3, KV_Q4_0_F16 = 4 };
+// K's and V's own types (KV_F16, KV_BF16 or KV_Q4_0)
+__host__ __device__ constexpr int kv_k(int kv)
+{
+    return kv == KV_F16_Q4_0 ? KV_F16 : kv == KV_Q4_0_F16 ? KV_Q4_0 : kv;
+}
+__host__ __device__ constexpr int kv_v(int kv)
+{
+    return kv == KV_F16_Q4_0 ? KV_Q4_0 : kv == KV_Q4_0_F16 ? KV_F16 : kv;
+}
+// bytes of one key row of one head: D 16-bit values, or D/32 q4_0 blocks of 18 bytes
+__host__ __device__ constexpr int kv_row_bytes(int t, int D)
+{
+    return t == KV_Q4_0 ? D / 32 * 18 : 2 * D;
+}
 
 // Softmax works in base 2: scores are multiplied by scale*log2(e) and exponentiated with
 // v_exp_f32. The rescale margin of 10 natural-log units becomes 10*log2(e).

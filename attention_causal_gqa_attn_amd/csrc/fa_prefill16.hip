@@ -20,7 +20,8 @@
 //  * a q4_0 cache arrives raw (12-byte LDS-DMA chunks, K 4 tiles and V 2 tiles ahead) and the
 //    waves dequantize it into 2-stage f16 K and V rings of the same layout, one tile of each per
 //    iteration (K two tiles ahead of its scores, V one ahead of its P.V), so everything after
-//    the dequantization is the f16 kernel;
+//    the dequantization is the f16 kernel; with one q4_0 and one f16 cache (mixed K/V types)
+//    the f16 tensor keeps the direct 4-stage ring and only the q4_0 one takes the raw path;
 //  * a paged cache (64-key pages, a block table and per-sequence lengths) differs only in where
 //    a tile's bytes start and where a sequence ends: the workgroup copies its sequence's page
 //    numbers into LDS once, and each iteration reads the two it needs (K n+4, V n+2) at its
@@ -153,6 +154,7 @@ struct Q4Raw {
     static constexpr int RAWT = kBN * CPR * 16;        // one tensor's raw tile in LDS
     static constexpr int NX = CPR;                     // wave-wide transfers per tensor tile
     static constexpr int NIW = (2 * NX + kNW - 1) / kNW;   // per wave per iteration, K + V
+    static constexpr int NIW1 = (NX + kNW - 1) / kNW;      // the same for one tensor
     static constexpr int KR = 4, VR = 3;
     static constexpr int LDS = 4 * Geom16<D>::TILE + (KR + VR) * RAWT;
 };
@@ -343,16 +345,28 @@ struct Plans {
     static_assert(schedule_ok<NDT, NST, NM>(sc), "softmax units placed in time");
 };
 
-template <int D, int KVT, bool PAGED>
+template <int D, int KT, int VT, bool PAGED>
 __global__ __launch_bounds__(kNT, 1) void prefill16_kernel(Prefill16Params p)
 {
-    constexpr bool BF = KVT == KV_BF16;
-    constexpr bool Q4 = KVT == KV_Q4_0;
+    static_assert(KT == VT || (KT != KV_BF16 && VT != KV_BF16), "bf16 caches are not mixed");
+    constexpr bool BF = KT == KV_BF16;
+    constexpr bool QK = KT == KV_Q4_0, QV = VT == KV_Q4_0;     // which tensors arrive raw
+    constexpr bool Q4 = QK && QV, ANYQ = QK || QV;
     using G = Geom16<D>;
     using QR = Q4Raw<D>;
     using PL = Plans<D>;
     constexpr int NDT = PL::NDT, NST = PL::NST, NM = PL::NM;
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[Q4 ? QR::LDS : G::LDS];
+    // f16 K and V rings (2 stages for a tensor that arrives raw, else 4), then the raw rings
+    constexpr int FSK = QK ? 2 : kStages, FSV = QV ? 2 : kStages;
+    constexpr int RAW0 = (FSK + FSV) * G::TILE;
+    constexpr int LDSB = RAW0 + ((QK ? QR::KR : 0) + (QV ? QR::VR : 0)) * QR::RAWT;
+    static_assert(!Q4 || LDSB == QR::LDS, "q4_0 layout");
+    static_assert(ANYQ || LDSB == G::LDS, "16-bit layout");
+    // transfers per wave per iteration: K(n+4) then V(n+2)
+    constexpr int TK = QK ? QR::NIW1 : G::NDMA, TV = QV ? QR::NIW1 : G::NDMA;
+    constexpr int TI = Q4 ? QR::NIW : TK + TV;
+    static_assert(4 * TI <= NM, "every transfer has a slot");
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[LDSB];
     __shared__ int32_t ptab[PAGED ? kPrefillMaxPages : 1];     // the sequence's page numbers
     typedef __attribute__((address_space(3))) s16x4_t lds_s16x4;
 
@@ -457,11 +471,10 @@ __global__ __launch_bounds__(kNT, 1) void prefill16_kernel(Prefill16Params p)
         vc[i] = vcol(i);
         lwave[i] = __builtin_amdgcn_readfirstlane(lds0 + (uint32_t)((i * kNW + wave) * 1024));
     }
-    // K stages [0, kStages), V stages [kStages, 2*kStages); tile j lives in stage j % kStages
-    // (q4_0: f16 K stages [0, 2), V stages [2, 4), then the raw stages)
-    constexpr int FS = Q4 ? 2 : kStages;
-    auto kstage = [&](int tl) INL { return lds + (tl & (FS - 1)) * G::TILE; };
-    auto vstage = [&](int tl) INL { return lds + (FS + (tl & (FS - 1))) * G::TILE; };
+    // K stages [0, FSK), V stages [FSK, FSK + FSV), then the raw stages; tile j lives in K
+    // stage j % FSK and V stage j % FSV
+    auto kstage = [&](int tl) INL { return lds + (tl & (FSK - 1)) * G::TILE; };
+    auto vstage = [&](int tl) INL { return lds + (FSK + (tl & (FSV - 1))) * G::TILE; };
     // Where tile tl sits, in tiles of kBN keys from the (b, kv head) base: tl itself, or its
     // page. Tiles past the last one re-read the last tile (into a stage nobody reads any more),
     // so every loop iteration issues the same transfers and the wait counts stay fixed.
@@ -492,18 +505,18 @@ __global__ __launch_bounds__(kNT, 1) void prefill16_kernel(Prefill16Params p)
     // at slot sv2
     auto dma_part = [&](int n, int i, int sk4, int sv2) INL {
         if (i < G::NDMA)
-            dma_one(false, (n + 4) & (kStages - 1), n + 4, sk4, i);
+            dma_one(false, (n + 4) & (FSK - 1), n + 4, sk4, i);
         else
-            dma_one(true, kStages + ((n + 2) & (kStages - 1)), n + 2, sv2, i - G::NDMA);
+            dma_one(true, FSK + ((n + 2) & (FSV - 1)), n + 2, sv2, i - G::NDMA);
     };
 
     // ---- q4_0: raw transfers and the dequantization into the f16 rings ----------------------
     const uint32_t growq = (uint32_t)a.Hkv * QR::ROWB;
     const uint8_t *kq = (const uint8_t *)a.k + hrow * QR::ROWB;
     const uint8_t *vq = (const uint8_t *)a.v + hrow * QR::ROWB;
-    auto rawk = [&](int tl) INL { return lds + 4 * G::TILE + (tl & (QR::KR - 1)) * QR::RAWT; };
+    auto rawk = [&](int tl) INL { return lds + RAW0 + (tl & (QR::KR - 1)) * QR::RAWT; };
     auto rawv = [&](int tl) INL {
-        return lds + 4 * G::TILE + QR::KR * QR::RAWT + (tl % QR::VR) * QR::RAWT;
+        return lds + RAW0 + (QK ? QR::KR * QR::RAWT : 0) + (tl % QR::VR) * QR::RAWT;
     };
     // transfer x of raw tile tl at slot ts (LDS slots 64 x .. 64 x + 63); tiles past the last
     // re-read the last one, rows past the sequence's end repeat its last key
@@ -525,6 +538,22 @@ __global__ __launch_bounds__(kNT, 1) void prefill16_kernel(Prefill16Params p)
             dma_raw(false, n + 4, sk4, i);
         else
             dma_raw(true, n + 2, sv2, i - QR::NX);
+    };
+    // mixed caches: this wave's m-th transfer, the TK of K(n+4) then the TV of V(n+2); the raw
+    // tensor's NX wave-wide transfers are dealt to the waves (surplus ones repeat the last)
+    auto dma_mixed = [&](int n, int m, int sk4, int sv2) INL {
+        if (m < TK) {
+            if constexpr (QK)
+                dma_raw(false, n + 4, sk4, min(wave + kNW * m, QR::NX - 1));
+            else
+                dma_one(false, (n + 4) & (FSK - 1), n + 4, sk4, m);
+        } else {
+            const int mv = m - TK;
+            if constexpr (QV)
+                dma_raw(true, n + 2, sv2, min(wave + kNW * mv, QR::NX - 1));
+            else
+                dma_one(true, FSK + ((n + 2) & (FSV - 1)), n + 2, sv2, mv);
+        }
     };
     // This thread's (key row, block) item of a tile: at D = 128 one K and one V item, wave w
     // taking the blocks of parity w & 1 (whether a block starts at byte 0 or 6 of its first
@@ -569,6 +598,10 @@ __global__ __launch_bounds__(kNT, 1) void prefill16_kernel(Prefill16Params p)
     auto dequant_k = [&](int tl) INL {
         if (D == 128 || wave < 2)
             dq_store(dq_load(rawk(tl)), kstage(tl), false);
+    };
+    auto dequant_v = [&](int tl) INL {
+        if (D == 128 || wave >= 2)
+            dq_store(dq_load(rawv(tl)), vstage(tl), true);
     };
     // K tile tk and V tile tv together: both raw reads are issued before either item's stores
     // (the compiler cannot move a read of the raw stages past a store into the f16 rings)
@@ -767,6 +800,9 @@ __global__ __launch_bounds__(kNT, 1) void prefill16_kernel(Prefill16Params p)
             if constexpr (Q4) {
                 if constexpr ((i & 3) == 1 && (i >> 2) < QR::NIW)
                     dma_q4(n, i >> 2, sk4, sv2);
+            } else if constexpr (ANYQ) {
+                if constexpr ((i & 3) == 1 && (i >> 2) < TI)
+                    dma_mixed(n, i >> 2, sk4, sv2);
             } else if constexpr ((i & 3) == 1 && (i >> 2) < 2 * G::NDMA) {
                 dma_part(n, i >> 2, sk4, sv2);
             }
@@ -774,11 +810,16 @@ __global__ __launch_bounds__(kNT, 1) void prefill16_kernel(Prefill16Params p)
         });
         static_for<PL::sc.first[2 * NM], kNU>([&](auto ic) INL { run_unit(ic, s0, s1c); });
         apply_rescale(1);
-        if constexpr (Q4) {
+        if constexpr (ANYQ) {
             // K(n+2) and V(n) into the stages of K(n) and V(n-2), read in iteration n-1 (at the
             // end of the tile, where the last score MFMAs are still executing)
             __builtin_amdgcn_sched_barrier(0);
-            dequant_kv(n + 2, n);
+            if constexpr (Q4)
+                dequant_kv(n + 2, n);
+            else if constexpr (QK)
+                dequant_k(n + 2);
+            else
+                dequant_v(n);
             __builtin_amdgcn_sched_barrier(0);
         }
     };
@@ -799,13 +840,21 @@ __global__ __launch_bounds__(kNT, 1) void prefill16_kernel(Prefill16Params p)
     };
     // prologue: K(0..3), V(0..1) (q4_0: raw, the transfers dealt round-robin to the waves)
     if (nb > 0) {
-        if constexpr (Q4) {
+        if constexpr (QK) {
 #pragma unroll
             for (int tl = 0; tl < 4; ++tl)
 #pragma unroll
                 for (int x = 0; x < QR::NX; ++x)
                     if (x % kNW == wave)
                         dma_raw(false, tl, slot(tl), x);
+        } else {
+#pragma unroll
+            for (int tl = 0; tl < 4; ++tl)
+#pragma unroll
+                for (int i = 0; i < G::NDMA; ++i)
+                    dma_one(false, tl, tl, slot(tl), i);
+        }
+        if constexpr (QV) {
 #pragma unroll
             for (int tl = 0; tl < 2; ++tl)
 #pragma unroll
@@ -814,20 +863,15 @@ __global__ __launch_bounds__(kNT, 1) void prefill16_kernel(Prefill16Params p)
                         dma_raw(true, tl, slot(tl), x);
         } else {
 #pragma unroll
-            for (int tl = 0; tl < 4; ++tl)
-#pragma unroll
-                for (int i = 0; i < G::NDMA; ++i)
-                    dma_one(false, tl, tl, slot(tl), i);
-#pragma unroll
             for (int tl = 0; tl < 2; ++tl)
 #pragma unroll
                 for (int i = 0; i < G::NDMA; ++i)
-                    dma_one(true, kStages + tl, tl, slot(tl), i);
+                    dma_one(true, FSK + tl, tl, slot(tl), i);
         }
     }
 
     // The V stage of tile -1 holds zeros, so that P.V of tile -1 adds nothing (P is zero too);
-    // tile kStages-1 (q4_0: tile 1) is written into it only after barrier 1
+    // tile FSV-1 is written into it only after barrier 1 (by a transfer or the dequantization)
     {
         uint8_t *z = vstage(-1);
         for (int o = t * 16; o < G::TILE; o += kNT * 16)
@@ -837,10 +881,11 @@ __global__ __launch_bounds__(kNT, 1) void prefill16_kernel(Prefill16Params p)
     }
     f32x16 s0[2], s1a[2], s1b[2];
     auto iteration = [&](int n, f32x16 *s1c, f32x16 *s1n) INL {
-        if constexpr (Q4) {
+        if constexpr (ANYQ) {
             // raw K(n+2) and V(n) landed: only iteration n-1's transfers may be in flight
+            // (with one f16 tensor its tiles landed earlier still)
             if (n >= 1)
-                __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(QR::NIW));
+                __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(TI));
             else
                 __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
             asm volatile("s_barrier" ::: "memory");
@@ -851,7 +896,7 @@ __global__ __launch_bounds__(kNT, 1) void prefill16_kernel(Prefill16Params p)
     };
     if (nb > 0) {
         wait_tiles(0);           // K(0) resident; also orders the zero fill before its reads
-        if constexpr (Q4) {
+        if constexpr (QK) {
             dequant_k(0);
             dequant_k(1);
             wait_tiles(0);
@@ -888,16 +933,33 @@ __global__ __launch_bounds__(kNT, 1) void prefill16_kernel(Prefill16Params p)
     }
 }
 
-template <int D, int KVT>
+template <int D, int KT, int VT>
 hipError_t launch16(const Prefill16Params &p, int64_t n_wg, hipStream_t stream)
 {
     if (p.block_table)
-        hipLaunchKernelGGL((prefill16_kernel<D, KVT, true>), dim3((unsigned)n_wg), dim3(kNT), 0,
-                           stream, p);
+        hipLaunchKernelGGL((prefill16_kernel<D, KT, VT, true>), dim3((unsigned)n_wg), dim3(kNT),
+                           0, stream, p);
     else
-        hipLaunchKernelGGL((prefill16_kernel<D, KVT, false>), dim3((unsigned)n_wg), dim3(kNT), 0,
-                           stream, p);
+        hipLaunchKernelGGL((prefill16_kernel<D, KT, VT, false>), dim3((unsigned)n_wg), dim3(kNT),
+                           0, stream, p);
     return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch16_kv(const Prefill16Params &p, int64_t n_wg, hipStream_t stream)
+{
+    switch (p.a.kv) {
+    case KV_BF16:
+        return launch16<D, KV_BF16, KV_BF16>(p, n_wg, stream);
+    case KV_Q4_0:
+        return launch16<D, KV_Q4_0, KV_Q4_0>(p, n_wg, stream);
+    case KV_F16_Q4_0:
+        return launch16<D, KV_F16, KV_Q4_0>(p, n_wg, stream);
+    case KV_Q4_0_F16:
+        return launch16<D, KV_Q4_0, KV_F16>(p, n_wg, stream);
+    default:
+        return launch16<D, KV_F16, KV_F16>(p, n_wg, stream);
+    }
 }
 
 }  // namespace
@@ -937,18 +999,7 @@ hipError_t launch_prefill16(const AttnArgs &a, const PrefillGrid &g, hipStream_t
         p.max_pages = paged->max_pages;
         p.n_pages = paged->n_pages;
     }
-    if (a.D == 128) {
-        if (a.kv == KV_BF16)
-            return launch16<128, KV_BF16>(p, g.n_wg, stream);
-        if (a.kv == KV_Q4_0)
-            return launch16<128, KV_Q4_0>(p, g.n_wg, stream);
-        return launch16<128, KV_F16>(p, g.n_wg, stream);
-    }
-    if (a.kv == KV_BF16)
-        return launch16<64, KV_BF16>(p, g.n_wg, stream);
-    if (a.kv == KV_Q4_0)
-        return launch16<64, KV_Q4_0>(p, g.n_wg, stream);
-    return launch16<64, KV_F16>(p, g.n_wg, stream);
+    return a.D == 128 ? launch16_kv<128>(p, g.n_wg, stream) : launch16_kv<64>(p, g.n_wg, stream);
 }
 
 #undef INL

@@ -12,6 +12,8 @@
 //   16-bit V: KPT = D/32 consecutive keys x one 16-byte chunk per thread; the KPT rows are
 //             transposed in registers with byte permutes and written as KPT-key runs.
 //   q4_0:     one item = 2 consecutive keys x 1 block; threads [0, D) take K, [D, 2D) take V.
+//   mixed (one f16 and one q4_0 cache): the f16 loader's half for the f16 tensor, the q4_0
+//             loader's threads for the other.
 // Key indices past the end of the sequence are clamped to the last key: those slots are
 // masked out of the softmax, and clamping keeps every load in bounds and every value finite.
 #pragma once
@@ -118,6 +120,12 @@ struct TileLoader {
         load_k(k0, toff);
         load_v(k0, toff);
     }
+    // K and V tile offsets apart (they differ when the two caches have different row sizes)
+    __device__ __forceinline__ void load(int k0, int64_t tk, int64_t tv)
+    {
+        load_k(k0, tk);
+        load_v(k0, tv);
+    }
 
     __device__ __forceinline__ void store_k(uint16_t *lk) const
     {
@@ -167,15 +175,19 @@ struct TileLoader<D, KV_Q4_0, NT> {
     const uint8_t *base;                        // K or V, first byte of (b, key 0, kvh)
     uint32_t row;                               // bytes between consecutive keys
     int Sk, tensor, kp, blk, mis;
+    bool active;
     uint32_t off[2];                            // byte offsets of this thread's 2 key rows
+    uint32_t bo;                                // its block's offset in a row, rounded to 4
     uint32_t w[2][5];
 
-    __device__ __forceinline__ bool busy() const { return kAllBusy || tensor < 2; }
+    __device__ __forceinline__ bool busy() const { return active; }
 
+    // only: -1 both tensors, 0 K only, 1 V only (the other tensor's threads stay idle)
     __device__ void init(const void *k, const void *v, int64_t head_off_rows, int64_t row_rows,
-                         int Sk_, int t)
+                         int Sk_, int t, int only = -1)
     {
         tensor = t / D;                         // 0: K, 1: V, >= 2: idle
+        active = only < 0 ? (kAllBusy || tensor < 2) : tensor == only;
         const int u = t % D;
         kp = u % 32;
         if constexpr (D == 128) {
@@ -195,6 +207,7 @@ struct TileLoader<D, KV_Q4_0, NT> {
 #pragma unroll
         for (int r = 0; r < 2; ++r)
             off[r] = (uint32_t)(2 * kp + r) * row + (uint32_t)(boff & ~3);
+        bo = (uint32_t)(boff & ~3);
     }
 
     // The raw tile is copied into LDS by 12-byte LDS-DMA
@@ -207,6 +220,24 @@ struct TileLoader<D, KV_Q4_0, NT> {
     static constexpr int RAW_STRIDE = RAW_CPR | 1;
     static constexpr int RAW_SLOTS = 64 * RAW_STRIDE;          // slots of one tensor's tile
     static_assert(ROWB % 12 == 0, "key rows split into 12-byte chunks");
+    // The same 5-dword windows from global memory: the tile at key k0, whose key-0 row is toff
+    // bytes past the head's (4-byte aligned: rows are a multiple of 4 bytes and a window
+    // starts at its block's byte offset rounded down to 4; it never passes the row's end)
+    __device__ __forceinline__ void load(int k0, int64_t toff)
+    {
+        if (!busy())
+            return;
+        const uint8_t *tb = base + toff;
+        const int last = Sk - 1 - k0;
+#pragma unroll
+        for (int rr = 0; rr < 2; ++rr) {
+            const uint32_t o = (uint32_t)min(2 * kp + rr, last) * row + bo;
+#pragma unroll
+            for (int i = 0; i < 5; ++i)
+                w[rr][i] = *(const uint32_t *)(tb + o + 4 * i);
+        }
+    }
+
     __device__ __forceinline__ void load_raw(const uint8_t *rk, const uint8_t *rv)
     {
         if (!busy())
@@ -271,5 +302,44 @@ struct TileLoader<D, KV_Q4_0, NT> {
         }
     }
 };
+
+// mixed caches ---------------------------------------------------------------------------
+// QK: K is the q4_0 tensor (V f16), else V is (K f16). Both loaders take the same key-row
+// index of the head; each scales it by its own row size.
+template <int D, bool QK, int NT>
+struct MixedLoader {
+    TileLoader<D, KV_F16, NT> f;
+    TileLoader<D, KV_Q4_0, NT> q;
+    __device__ void init(const void *k, const void *v, int64_t head_off_rows, int64_t row_rows,
+                         int Sk, int t)
+    {
+        f.init(k, v, head_off_rows, row_rows, Sk, t);
+        q.init(k, v, head_off_rows, row_rows, Sk, t, QK ? 0 : 1);
+    }
+    __device__ __forceinline__ void load(int k0, int64_t tk, int64_t tv)
+    {
+        if constexpr (QK) {
+            q.load(k0, tk);
+            f.load_v(k0, tv);
+        } else {
+            f.load_k(k0, tk);
+            q.load(k0, tv);
+        }
+    }
+    __device__ __forceinline__ void store(uint16_t *lk, uint16_t *lv) const
+    {
+        if constexpr (QK) {
+            q.store(lk, lv);
+            f.store_v(lv);
+        } else {
+            f.store_k(lk);
+            q.store(lk, lv);
+        }
+    }
+};
+template <int D, int NT>
+struct TileLoader<D, KV_F16_Q4_0, NT> : MixedLoader<D, false, NT> {};
+template <int D, int NT>
+struct TileLoader<D, KV_Q4_0_F16, NT> : MixedLoader<D, true, NT> {};
 
 }  // namespace fa

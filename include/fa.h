@@ -17,9 +17,11 @@
  *
  * Layouts (all contiguous, row-major, no padding):
  *   Q, O : [B, Sq, Hq, D]  elements of the Q type
- *   K, V : [B, Sk, Hkv, D] elements of the K/V type, or for FA_KV_Q4_0
- *          [B, Sk, Hkv, D/32] blocks of 18 bytes
- * The Q/O type is bf16 when kv_dtype is FA_KV_BF16 and f16 otherwise (f16 and q4_0 caches).
+ *   K, V : [B, Sk, Hkv, D] elements of the K/V type, or for a q4_0 cache
+ *          [B, Sk, Hkv, D/32] blocks of 18 bytes (each tensor by its own type when
+ *          kv_dtype is mixed)
+ * The Q/O type is bf16 when kv_dtype is FA_KV_BF16 and f16 otherwise (f16, q4_0 and mixed
+ * caches).
  *
  * q4_0 block (the KV-cache type "-ctk q4_0 -ctv q4_0" of the mi210-llm-stack page
  * "FlashAttention on gfx90a"; the page names it but does not define it, so this is the
@@ -48,9 +50,13 @@ extern "C" {
 typedef struct ihipStream_t *fa_stream_t;
 
 enum fa_kv_dtype {
-    FA_KV_F16 = 0,   /* K/V f16,  Q/O f16  */
-    FA_KV_BF16 = 1,  /* K/V bf16, Q/O bf16 */
-    FA_KV_Q4_0 = 2,  /* K/V q4_0, Q/O f16  */
+    FA_KV_F16 = 0,       /* K/V f16,  Q/O f16  */
+    FA_KV_BF16 = 1,      /* K/V bf16, Q/O bf16 */
+    FA_KV_Q4_0 = 2,      /* K/V q4_0, Q/O f16  */
+    /* mixed caches (mi210-llm-stack, "FlashAttention on gfx90a", sets the K and V cache
+       types with separate flags, -ctk and -ctv) */
+    FA_KV_F16_Q4_0 = 3,  /* K f16, V q4_0, Q/O f16 */
+    FA_KV_Q4_0_F16 = 4,  /* K q4_0, V f16, Q/O f16 */
 };
 
 enum fa_status {
@@ -60,7 +66,7 @@ enum fa_status {
     FA_ERR_DTYPE = -3,        /* kv_dtype (x_dtype) not one of enum fa_kv_dtype (fa_src_dtype) */
     FA_ERR_UNSUPPORTED = -4,  /* valid but not built: D not in {64, 128}; decode rows > 16 */
     FA_ERR_WORKSPACE = -5,    /* decode workspace missing or smaller than required */
-    FA_ERR_ALIGN = -6,        /* Q/O/K/V not 16-byte aligned (q4_0 K/V: 4-byte aligned) */
+    FA_ERR_ALIGN = -6,        /* Q/O/K/V not 16-byte aligned (a q4_0 K or V: 4-byte aligned) */
     FA_ERR_HIP = -7,          /* the HIP runtime reported an error at launch */
     FA_ERR_VALUE = -8,        /* scale not finite and > 0 */
 };

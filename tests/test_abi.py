@@ -64,7 +64,7 @@ def decode(**kw):
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(kv_dtype=3), fa.FA_ERR_DTYPE),
+    (dict(kv_dtype=5), fa.FA_ERR_DTYPE),
     (dict(kv_dtype=-1), fa.FA_ERR_DTYPE),
     (dict(Hq=30), fa.FA_ERR_SHAPE),
     (dict(Hkv=0), fa.FA_ERR_SHAPE),
@@ -87,6 +87,11 @@ def decode(**kw):
     (dict(k=P + 4), fa.FA_ERR_ALIGN),
     (dict(v=P + 4, kv_dtype=1), fa.FA_ERR_ALIGN),
     (dict(v=ODD, kv_dtype=2), fa.FA_ERR_ALIGN),
+    # mixed caches: each tensor aligned by its own type (f16 16 bytes, q4_0 4)
+    (dict(k=P + 4, kv_dtype=3), fa.FA_ERR_ALIGN),
+    (dict(v=ODD, kv_dtype=3), fa.FA_ERR_ALIGN),
+    (dict(k=ODD, kv_dtype=4), fa.FA_ERR_ALIGN),
+    (dict(v=P + 4, kv_dtype=4), fa.FA_ERR_ALIGN),
     (dict(B=1 << 30, Sq=1 << 30, Hq=1 << 20, Hkv=1 << 20), fa.FA_ERR_SHAPE),
 ])
 def test_prefill_rejects(kw, code):

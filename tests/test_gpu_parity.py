@@ -275,7 +275,7 @@ def _scatter_pages(x, B, max_pages, seed):
     order = rng.permutation(n_pages)
     table = np.empty((B, max_pages), np.int32)
     kp = np.zeros((n_pages, 64) + x.k.shape[2:], x.k.dtype)
-    vp = np.zeros_like(kp)
+    vp = np.zeros((n_pages, 64) + x.v.shape[2:], x.v.dtype)
     for b in range(B):
         for j in range(max_pages):
             pg = order[b * max_pages + j]
@@ -404,3 +404,125 @@ def test_prefill_paged_in_order_equals_contiguous(wname):
     b = fa.prefill_paged(q, kp, vp, table, lens, qlens, causal=True, scale=w.scale)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+# ---------------------------------------------------------------------------------------------
+# mixed caches: K and V of different types (f16 with q4_0)
+# ---------------------------------------------------------------------------------------------
+
+def _mixed(w, kt, vt):
+    """Inputs of w's shape with K of type kt and V of type vt: Q and K drawn as kt, V drawn
+    as vt with another seed."""
+    xk = W.generate(w.with_(kv=kt))
+    xv = W.generate(w.with_(kv=vt, seed=w.seed + 1000))
+    return xk.q, xk.k, xv.v
+
+
+def _mixed_oracle(w, q, k, v, kt, vt, rows=None):
+    return oracle.attention(q, k, v, q_dtype="f16", kv_dtype=kt, v_dtype=vt, causal=w.causal,
+                            offset=w.causal_offset, scale=w.scale, rows=rows)
+
+
+MIXED_PREFILL = [
+    # (name, B, Hq, Hkv, Sq, Sk, D, K type, V type, causal, offset, seed)
+    ("mix_f16k_q4v", 2, 8, 2, 100, 300, 128, "f16", "q4_0", True, 200, 41),
+    ("mix_q4k_f16v", 2, 8, 2, 100, 300, 128, "q4_0", "f16", True, 200, 42),
+    ("mix_f16k_q4v_d64", 1, 8, 2, 130, 200, 64, "f16", "q4_0", True, 70, 43),
+    ("mix_q4k_f16v_d64_noncausal", 1, 4, 4, 70, 150, 64, "q4_0", "f16", False, 0, 44),
+    ("mix_q4k_f16v_long", 1, 8, 2, 64, 1000, 128, "q4_0", "f16", True, 936, 45),
+]
+
+
+@pytest.mark.parametrize("case", MIXED_PREFILL, ids=[c[0] for c in MIXED_PREFILL])
+def test_prefill_mixed_matches_oracle(case):
+    name, B, Hq, Hkv, Sq, Sk, D, kt, vt, causal, offset, seed = case
+    say(f"mixed prefill {case}")
+    w = wl(name, B, Hq, Hkv, Sq, Sk, D, "f16", causal, offset, seed)
+    q, k, v = _mixed(w, kt, vt)
+    got = fa.prefill(to_dev(q, "f16"), to_dev(k, kt), to_dev(v, vt), causal=causal,
+                     offset=w.causal_offset, scale=w.scale)
+    torch.cuda.synchronize()
+    err = float(np.max(np.abs(got.float().cpu().numpy() - _mixed_oracle(w, q, k, v, kt, vt))))
+    say(f"  max|err| = {err:.3e}")
+    assert err <= TOL["q4_0"], (name, err)
+
+
+MIXED_DECODE = [
+    # (name, B, Hq, Hkv, Sq, Sk, D, K type, V type, causal, offset, seed)
+    ("dmix_f16k_q4v", 4, 32, 8, 1, 5000, 128, "f16", "q4_0", True, 4999, 51),
+    ("dmix_q4k_f16v_sq2_d64", 2, 16, 4, 2, 3000, 64, "q4_0", "f16", True, 2998, 52),
+    ("dmix_q4k_f16v_noncausal", 1, 8, 8, 3, 700, 128, "q4_0", "f16", False, 0, 53),
+]
+
+
+@pytest.mark.parametrize("case", MIXED_DECODE, ids=[c[0] for c in MIXED_DECODE])
+def test_decode_mixed_matches_oracle(case):
+    name, B, Hq, Hkv, Sq, Sk, D, kt, vt, causal, offset, seed = case
+    say(f"mixed decode {case}")
+    w = wl(name, B, Hq, Hkv, Sq, Sk, D, "f16", causal, offset, seed)
+    q, k, v = _mixed(w, kt, vt)
+    got = fa.decode(to_dev(q, "f16"), to_dev(k, kt), to_dev(v, vt), causal=causal,
+                    offset=w.causal_offset, scale=w.scale)
+    torch.cuda.synchronize()
+    err = float(np.max(np.abs(got.float().cpu().numpy() - _mixed_oracle(w, q, k, v, kt, vt))))
+    say(f"  max|err| = {err:.3e}")
+    assert err <= TOL["q4_0"], (name, err)
+
+
+@pytest.mark.parametrize("kt,vt", [("f16", "q4_0"), ("q4_0", "f16")])
+def test_mixed_equals_dequantized_f16(kt, vt):
+    """At full size (2048 queries x 16384 keys prefill, 4 x 32768 keys decode): a mixed cache
+    gives the same bits as the f16 kernels on that cache with its q4_0 tensor dequantized by
+    fa_dequant_q4_0 (the kernels dequantize with the same routine into the same f16 tiles),
+    and sampled prefill rows agree with the oracle."""
+    for w, call in ((W.WORKLOADS["prefill_16k_f16"], fa.prefill),
+                    (W.WORKLOADS["decode_q4_0"].with_(kv="f16"), fa.decode)):
+        say(f"mixed {kt}/{vt} vs dequantized f16 {w}")
+        q, k, v = _mixed(w, kt, vt)
+        qd, kd, vd = to_dev(q, "f16"), to_dev(k, kt), to_dev(v, vt)
+        shape = (w.B, w.Sk, w.Hkv, w.D)
+        kf = fa.dequant_q4_0(kd.reshape(-1))[1].view(shape) if kt == "q4_0" else kd
+        vf = fa.dequant_q4_0(vd.reshape(-1))[1].view(shape) if vt == "q4_0" else vd
+        mixed = call(qd, kd, vd, causal=True, offset=w.causal_offset, scale=w.scale)
+        plain = call(qd, kf, vf, causal=True, offset=w.causal_offset, scale=w.scale)
+        torch.cuda.synchronize()
+        assert torch.equal(mixed, plain), w.name
+        if call is fa.prefill:
+            rows = sample_rows(w, 256, seed=9)
+            got = mixed.float().cpu().numpy().reshape(-1, w.D)[rows]
+            err = float(np.max(np.abs(got - _mixed_oracle(w, q, k, v, kt, vt, rows=rows))))
+            say(f"  sampled rows: max|err| = {err:.3e}")
+            assert err <= TOL["q4_0"], err
+
+
+def test_paged_mixed_matches_oracle():
+    """Mixed caches through the paged entry points: prefill (K q4_0, V f16) and decode
+    (K f16, V q4_0) over shuffled pages."""
+    for kt, vt, Sq, q_lens, call in (("q4_0", "f16", 96, [96, 40], "prefill"),
+                                     ("f16", "q4_0", 1, None, "decode")):
+        B, Hq, Hkv, D, max_pages, lens = 2, 8, 2, 128, 8, [500, 77]
+        w = wl(f"paged_mix_{call}", B, Hq, Hkv, Sq, max_pages * 64, D, "f16", True, None, 71)
+        say(f"paged mixed {call} {kt}/{vt}")
+        q, k, v = _mixed(w, kt, vt)
+
+        class KV:
+            pass
+        kv = KV()
+        kv.k, kv.v = k, v
+        kp, vp, table = _scatter_pages(kv, B, max_pages, 72)
+        args = (to_dev(q, "f16"), to_dev(kp, kt), to_dev(vp, vt), torch.from_numpy(table).cuda(),
+                torch.tensor(lens, dtype=torch.int32, device="cuda"))
+        if call == "prefill":
+            got = fa.prefill_paged(*args, torch.tensor(q_lens, dtype=torch.int32, device="cuda"),
+                                   causal=True, scale=w.scale)
+        else:
+            got = fa.decode_paged(*args, causal=True, scale=w.scale)
+        torch.cuda.synchronize()
+        got = got.float().cpu().numpy()
+        for b in range(B):
+            n, m = lens[b], Sq if q_lens is None else q_lens[b]
+            ref = oracle.attention(q[b:b + 1, :m], k[b:b + 1, :n], v[b:b + 1, :n], q_dtype="f16",
+                                   kv_dtype=kt, v_dtype=vt, causal=True, offset=n - m,
+                                   scale=w.scale)
+            err = float(np.max(np.abs(got[b, :m] - ref[0])))
+            assert err <= TOL["q4_0"], (call, b, err)
