@@ -13,7 +13,9 @@ One step = one pass of the whole path over resident inputs:
   * the decode over a paged cache: the same 4 x 32768 q4_0 keys as 2048 pages of 64 keys in
     a shuffled order (fa_decode_paged; reported, HBM-bound);
   * the prefill over a paged cache: the f16 prefill's 16384 keys as 256 shuffled pages
-    (fa_prefill_paged; reported, MFMA-bound).
+    (fa_prefill_paged; reported, MFMA-bound);
+  * mixed caches (f16 K, q4_0 V): the prefill workload and the decode workload's shape with
+    those types (reported).
 Before each call a 1 GiB buffer is read so that neither call finds its inputs in the 256 MB
 last-level cache (the decode working set, 151 MB, would otherwise stay resident). The flush
 reads rather than writes: a written flush leaves up to 256 MB of dirty lines in that cache,
@@ -196,6 +198,11 @@ def main():
     plens = torch.full((wp.B,), wp.Sk, dtype=torch.int32, device=dev)
     pqlens = torch.full((wp.B,), wp.Sq, dtype=torch.int32, device=dev)
     po2 = torch.empty_like(pq)
+    # mixed caches: f16 K with q4_0 V (the q4_0 prefill's V; a decode-shaped f16 K)
+    po3 = torch.empty_like(pq)
+    dkf = to_dev(W.generate(wd.with_(kv="f16")).k, "f16")
+    do3 = torch.empty_like(dq)
+    mbytes = dkf.numel() * 2 + dv.numel() + 2 * dq.numel() * 2
     wk = torch.empty(pk.numel() // 32 * 18, dtype=torch.uint8, device=dev)
     wv = torch.empty_like(wk)
     wbytes = (pk.numel() + pv.numel()) * 2 + wk.numel() + wv.numel()
@@ -240,8 +247,16 @@ def main():
         fa.prefill_paged(pq, pkp, pvp, ptable, plens, pqlens, causal=True, scale=wp.scale,
                          out=po2, stream=stream)
 
+    def prefill_mixed():
+        fa.prefill(pq, pk, qv, causal=True, offset=wp.causal_offset, scale=wp.scale, out=po3,
+                   stream=stream)
+
+    def decode_mixed():
+        fa.decode(dq, dkf, dv, causal=True, offset=wd.causal_offset, scale=wd.scale, out=do3,
+                  workspace=ws, stream=stream)
+
     calls = [prefill, decode, prefill_q4, prefill_q4_unfused, quantize, decode_paged,
-             prefill_paged]
+             prefill_paged, prefill_mixed, decode_mixed]
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * len(calls))]
           for _ in range(args.steps)]
 
@@ -278,6 +293,8 @@ def main():
     w_ms = np.array([e[8].elapsed_time(e[9]) for e in ev])
     g_ms = np.array([e[10].elapsed_time(e[11]) for e in ev])
     pp_ms = np.array([e[12].elapsed_time(e[13]) for e in ev])
+    pm_ms = np.array([e[14].elapsed_time(e[15]) for e in ev])
+    dm_ms = np.array([e[16].elapsed_time(e[17]) for e in ev])
     qflops = W.attention_flops(wq)
     flops = W.attention_flops(wp)
     dbytes = W.algorithmic_bytes(wd)
@@ -346,6 +363,19 @@ def main():
                           "ms_mean": round(float(pp_ms.mean()), 5),
                           "frac_of_mfma_peak": round(flops / (float(pp_ms.mean()) * 1e-3) / 1e12
                                                      / PEAK_MFMA_F16_TFLOPS, 4)},
+        "prefill_mixed": {"what": "the prefill workload with f16 K and q4_0 V "
+                                  "(FA_KV_F16_Q4_0)",
+                          "tflops": round(flops / (float(pm_ms.mean()) * 1e-3) / 1e12, 3),
+                          "ms_mean": round(float(pm_ms.mean()), 5),
+                          "frac_of_mfma_peak": round(flops / (float(pm_ms.mean()) * 1e-3) / 1e12
+                                                     / PEAK_MFMA_F16_TFLOPS, 4)},
+        "decode_mixed": {"what": "4 x 1 query against 32768 keys, f16 K and q4_0 V "
+                                 "(FA_KV_F16_Q4_0, split + merge)",
+                         "value": round(mbytes / (float(dm_ms.mean()) * 1e-3) / 1e9, 1),
+                         "unit": "GB/s", "bytes": int(mbytes),
+                         "ms_mean": round(float(dm_ms.mean()), 5),
+                         "frac_of_hbm_peak": round(mbytes / (float(dm_ms.mean()) * 1e-3) / 1e9
+                                                   / PEAK_HBM_GBS, 4)},
         "quantize_q4_0": {"what": "fa_quantize_q4_0 of f16 K and V [1, 16384, 8, 128] (two "
                                   "launches)",
                           "gbs": round(wbytes / (float(w_ms.mean()) * 1e-3) / 1e9, 1),
