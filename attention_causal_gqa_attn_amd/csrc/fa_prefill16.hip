@@ -175,7 +175,7 @@ __device__ __forceinline__ void static_for(F &&f)
 // ---- compile-time placement of the softmax work over the MFMA slots of a tile ---------------
 // A tile is 2*NM MFMA slots: slots [0, NM) are half 1 (P.V), [NM, 2*NM) half 2 (scores). The
 // softmax of each block j is cut into short units:
-//   M0..M7  partial maxima of the 32 scores (m8[i] = max of 4)
+//   M0..M7  partial maxima of the 32 scores (m8[i] = max of 4: v_max3 + v_max)
 //   T1, T2  the rest of the lane's max;  P  the lane-pair max (the row max)
 //   F1, F2  frame update: alpha, new frame, lsum *= alpha, whether any lane rescales
 //   E0..E15 two scores to P values (exp2(s*c - frame)); Cu packs E u's pair into P chunk
@@ -198,8 +198,8 @@ constexpr int unit_cost(int kind)
 {
     switch (kind) {
     case UM: return 8;
-    case UT1: return 16;
-    case UT2: return 12;
+    case UT1: return 12;
+    case UT2: return 4;
     case UP: return 24;
     case UF1: return 12;
     case UF2: return 28;
@@ -669,17 +669,17 @@ __global__ __launch_bounds__(kNT, 1) void prefill16_kernel(Prefill16Params p)
         f32x16 *s = j == 0 ? s0 : s1;
         if constexpr (x.kind == UM) {
             constexpr int u = x.idx;
-            m8[j][u] = fmaxf(fmaxf(s[0][2 * u], s[0][2 * u + 1]),
-                             fmaxf(s[1][2 * u], s[1][2 * u + 1]));
+            m8[j][u] = vmax(vmax3(s[0][2 * u], s[0][2 * u + 1], s[1][2 * u]), s[1][2 * u + 1]);
             pin(m8[j][u]);
         } else if constexpr (x.kind == UT1) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                m8[j][i] = fmaxf(m8[j][i], m8[j][i + 4]);
-                pin(m8[j][i]);
-            }
+            m8[j][0] = vmax3(m8[j][0], m8[j][1], m8[j][2]);
+            m8[j][3] = vmax3(m8[j][3], m8[j][4], m8[j][5]);
+            m8[j][6] = vmax(m8[j][6], m8[j][7]);
+            pin(m8[j][0]);
+            pin(m8[j][3]);
+            pin(m8[j][6]);
         } else if constexpr (x.kind == UT2) {
-            m8[j][0] = fmaxf(fmaxf(m8[j][0], m8[j][2]), fmaxf(m8[j][1], m8[j][3]));
+            m8[j][0] = vmax3(m8[j][0], m8[j][3], m8[j][6]);
             pin(m8[j][0]);
         } else if constexpr (x.kind == UP) {
             mx[j] = pair_max(m8[j][0]);
