@@ -16,7 +16,8 @@
 //  * tiles keep their row-major [key][d] layout in LDS with 16-byte chunks XOR-swizzled per
 //    row, so K fragment reads (16 bytes) and V^T transpose reads (ds_read_b64_tr_b16) are free
 //    of bank conflicts; K runs 4 tiles ahead of its use and V 2 tiles, through 4-stage rings,
-//    so every tile has three loop iterations to arrive;
+//    so every tile has three loop iterations to arrive (16-bit caches at D = 64: 8-stage rings,
+//    K 7 tiles ahead and V 5, and one barrier per pair of tiles);
 //  * a q4_0 cache arrives raw (12-byte LDS-DMA chunks, K 4 tiles and V 2 tiles ahead) and the
 //    waves dequantize it into 2-stage f16 K and V rings of the same layout, one tile of each per
 //    iteration (K two tiles ahead of its scores, V one ahead of its P.V), so everything after
@@ -356,12 +357,19 @@ __global__ __launch_bounds__(kNT, 1) void prefill16_kernel(Prefill16Params p)
     using QR = Q4Raw<D>;
     using PL = Plans<D>;
     constexpr int NDT = PL::NDT, NST = PL::NST, NM = PL::NM;
-    // f16 K and V rings (2 stages for a tensor that arrives raw, else 4), then the raw rings
-    constexpr int FSK = QK ? 2 : kStages, FSV = QV ? 2 : kStages;
+    // PAIR (16-bit caches at D = 64, whose 8 KB tiles leave room for 8-stage rings): K runs 7
+    // tiles ahead and V 5, and only even iterations wait and meet at a barrier, which halves
+    // the barriers of a tile with half the MFMA work of D = 128
+    constexpr bool PAIR = D == 64 && !ANYQ;
+    constexpr int LK = PAIR ? 7 : 4, LV = PAIR ? 5 : 2;      // tiles ahead: K, V
+    // f16 K and V rings (2 stages for a tensor that arrives raw, else 4 or 8), then the raw
+    // rings
+    constexpr int FS16 = PAIR ? 8 : kStages;
+    constexpr int FSK = QK ? 2 : FS16, FSV = QV ? 2 : FS16;
     constexpr int RAW0 = (FSK + FSV) * G::TILE;
     constexpr int LDSB = RAW0 + ((QK ? QR::KR : 0) + (QV ? QR::VR : 0)) * QR::RAWT;
     static_assert(!Q4 || LDSB == QR::LDS, "q4_0 layout");
-    static_assert(ANYQ || LDSB == G::LDS, "16-bit layout");
+    static_assert(ANYQ || PAIR || LDSB == G::LDS, "16-bit layout");
     // transfers per wave per iteration: K(n+4) then V(n+2)
     constexpr int TK = QK ? QR::NIW1 : G::NDMA, TV = QV ? QR::NIW1 : G::NDMA;
     constexpr int TI = Q4 ? QR::NIW : TK + TV;
@@ -501,13 +509,14 @@ __global__ __launch_bounds__(kNT, 1) void prefill16_kernel(Prefill16Params p)
         dma16(gt, min(rowg[i], lastg) + (is_v ? vc[i] : kc[i]),
               lwave[i] + (uint32_t)(stage * G::TILE));
     };
-    // transfer i of the tiles issued in iteration n: i < NDMA: K(n+4) at slot sk4, else V(n+2)
-    // at slot sv2
+    // transfer i of the tiles issued in iteration n: i < NDMA: K(n+LK) at slot sk4, else
+    // V(n+LV) at slot sv2 (into the stages of K(n+LK-FSK) and V(n+LV-FSV), whose last reader
+    // ran before the latest barrier)
     auto dma_part = [&](int n, int i, int sk4, int sv2) INL {
         if (i < G::NDMA)
-            dma_one(false, (n + 4) & (FSK - 1), n + 4, sk4, i);
+            dma_one(false, (n + LK) & (FSK - 1), n + LK, sk4, i);
         else
-            dma_one(true, FSK + ((n + 2) & (FSV - 1)), n + 2, sv2, i - G::NDMA);
+            dma_one(true, FSK + ((n + LV) & (FSV - 1)), n + LV, sv2, i - G::NDMA);
     };
 
     // ---- q4_0: raw transfers and the dequantization into the f16 rings ----------------------
@@ -767,7 +776,7 @@ __global__ __launch_bounds__(kNT, 1) void prefill16_kernel(Prefill16Params p)
     // cannot see are masked to -inf and give P = 0).
     auto tile = [&](int n, f32x16 *s0, f32x16 *s1c, f32x16 *s1n) INL {
         const uint8_t *vs = vstage(n - 1), *ks = kstage(n + 1);
-        const int sk4 = slot(n + 4), sv2 = slot(n + 2);     // where this iteration's DMA reads
+        const int sk4 = slot(n + LK), sv2 = slot(n + LV);   // where this iteration's DMA reads
         u32x4 fb[kRead + 1];
         smfma_drain(s0[0], s0[1], s1c[0], s1c[1]);
         mask(0, s0, n);
@@ -849,7 +858,7 @@ __global__ __launch_bounds__(kNT, 1) void prefill16_kernel(Prefill16Params p)
                         dma_raw(false, tl, slot(tl), x);
         } else {
 #pragma unroll
-            for (int tl = 0; tl < 4; ++tl)
+            for (int tl = 0; tl < LK; ++tl)
 #pragma unroll
                 for (int i = 0; i < G::NDMA; ++i)
                     dma_one(false, tl, tl, slot(tl), i);
@@ -863,7 +872,7 @@ __global__ __launch_bounds__(kNT, 1) void prefill16_kernel(Prefill16Params p)
                         dma_raw(true, tl, slot(tl), x);
         } else {
 #pragma unroll
-            for (int tl = 0; tl < 2; ++tl)
+            for (int tl = 0; tl < LV; ++tl)
 #pragma unroll
                 for (int i = 0; i < G::NDMA; ++i)
                     dma_one(true, FSK + tl, tl, slot(tl), i);
@@ -889,6 +898,19 @@ __global__ __launch_bounds__(kNT, 1) void prefill16_kernel(Prefill16Params p)
             else
                 __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
             asm volatile("s_barrier" ::: "memory");
+        } else if constexpr (PAIR) {
+            // even n: K(n+1), K(n+2), V(n-1), V(n) resident (issued by iteration n-5 or the
+            // prologue), so iterations n-4 .. n-1 may have transfers in flight; odd n relies
+            // on the barrier of n-1
+            if ((n & 1) == 0) {
+                if (n >= 4)
+                    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(4 * 2 * G::NDMA));
+                else if (n >= 2)
+                    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(2 * 2 * G::NDMA));
+                else
+                    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+                asm volatile("s_barrier" ::: "memory");
+            }
         } else {
             wait_tiles(2 * min(n, 2));
         }
