@@ -15,7 +15,9 @@ One step = one pass of the whole path over resident inputs:
   * the prefill over a paged cache: the f16 prefill's 16384 keys as 256 shuffled pages
     (fa_prefill_paged; reported, MFMA-bound);
   * mixed caches (f16 K, q4_0 V): the prefill workload and the decode workload's shape with
-    those types (reported).
+    those types (reported);
+  * head dim 64: the prefill workload at D = 64, and the B=2, S=512, 8-head D=64 causal
+    self-attention check shape (reported; the latter is launch- and latency-bound).
 Before each call a 1 GiB buffer is read so that neither call finds its inputs in the 256 MB
 last-level cache (the decode working set, 151 MB, would otherwise stay resident). The flush
 reads rather than writes: a written flush leaves up to 256 MB of dirty lines in that cache,
@@ -203,6 +205,15 @@ def main():
     dkf = to_dev(W.generate(wd.with_(kv="f16")).k, "f16")
     do3 = torch.empty_like(dq)
     mbytes = dkf.numel() * 2 + dv.numel() + 2 * dq.numel() * 2
+    # head dim 64
+    w64 = wp.with_(D=64)
+    x64 = W.generate(w64)
+    q64, k64, v64 = to_dev(x64.q, "f16"), to_dev(x64.k, "f16"), to_dev(x64.v, "f16")
+    o64 = torch.empty_like(q64)
+    wsm = W.WORKLOADS["p2check"]
+    xsm = W.generate(wsm)
+    qsm, ksm, vsm = to_dev(xsm.q, "f16"), to_dev(xsm.k, "f16"), to_dev(xsm.v, "f16")
+    osm = torch.empty_like(qsm)
     wk = torch.empty(pk.numel() // 32 * 18, dtype=torch.uint8, device=dev)
     wv = torch.empty_like(wk)
     wbytes = (pk.numel() + pv.numel()) * 2 + wk.numel() + wv.numel()
@@ -255,8 +266,16 @@ def main():
         fa.decode(dq, dkf, dv, causal=True, offset=wd.causal_offset, scale=wd.scale, out=do3,
                   workspace=ws, stream=stream)
 
+    def prefill_d64():
+        fa.prefill(q64, k64, v64, causal=True, offset=w64.causal_offset, scale=w64.scale,
+                   out=o64, stream=stream)
+
+    def check_d64():
+        fa.prefill(qsm, ksm, vsm, causal=True, offset=wsm.causal_offset, scale=wsm.scale,
+                   out=osm, stream=stream)
+
     calls = [prefill, decode, prefill_q4, prefill_q4_unfused, quantize, decode_paged,
-             prefill_paged, prefill_mixed, decode_mixed]
+             prefill_paged, prefill_mixed, decode_mixed, prefill_d64, check_d64]
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * len(calls))]
           for _ in range(args.steps)]
 
@@ -295,6 +314,10 @@ def main():
     pp_ms = np.array([e[12].elapsed_time(e[13]) for e in ev])
     pm_ms = np.array([e[14].elapsed_time(e[15]) for e in ev])
     dm_ms = np.array([e[16].elapsed_time(e[17]) for e in ev])
+    d64_ms = np.array([e[18].elapsed_time(e[19]) for e in ev])
+    sm_ms = np.array([e[20].elapsed_time(e[21]) for e in ev])
+    f64 = W.attention_flops(w64)
+    fsm = W.attention_flops(wsm)
     qflops = W.attention_flops(wq)
     flops = W.attention_flops(wp)
     dbytes = W.algorithmic_bytes(wd)
@@ -376,6 +399,14 @@ def main():
                          "ms_mean": round(float(dm_ms.mean()), 5),
                          "frac_of_hbm_peak": round(mbytes / (float(dm_ms.mean()) * 1e-3) / 1e9
                                                    / PEAK_HBM_GBS, 4)},
+        "prefill_d64": {"what": "the prefill workload at head dim 64 (2048 x 16384, GQA 32/8, f16)",
+                        "tflops": round(f64 / (float(d64_ms.mean()) * 1e-3) / 1e12, 3),
+                        "ms_mean": round(float(d64_ms.mean()), 5),
+                        "frac_of_mfma_peak": round(f64 / (float(d64_ms.mean()) * 1e-3) / 1e12
+                                                   / PEAK_MFMA_F16_TFLOPS, 4)},
+        "check_d64": {"what": "causal self-attention B=2, S=512, Hq=Hkv=8, D=64, f16 (one call)",
+                      "us_mean": round(float(sm_ms.mean()) * 1e3, 2),
+                      "tflops": round(fsm / (float(sm_ms.mean()) * 1e-3) / 1e12, 3)},
         "quantize_q4_0": {"what": "fa_quantize_q4_0 of f16 K and V [1, 16384, 8, 128] (two "
                                   "launches)",
                           "gbs": round(wbytes / (float(w_ms.mean()) * 1e-3) / 1e9, 1),
