@@ -355,7 +355,7 @@ def main():
                    "kernels": "decode_q4g_kernel + decode_merge_kernel"},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 3), "peak": PEAK_MFMA_F16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK_MFMA_F16_TFLOPS, 4),
-                     "traffic": traffic, "kernel": "prefill16_kernel<128, f16>",
+                     "traffic": traffic, "kernel": "prefill16_kernel<128, f16, f16, contiguous>",
                      "algorithmic_flops_per_launch": flops},
         "roofline_decode": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                             "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
@@ -367,7 +367,7 @@ def main():
                          "ms_median": round(float(np.median(q_ms)), 5),
                          "frac_of_mfma_peak": round(qflops / (float(q_ms.mean()) * 1e-3) / 1e12
                                                     / PEAK_MFMA_F16_TFLOPS, 4),
-                         "kernel": "prefill16_kernel<128, q4_0>"},
+                         "kernel": "prefill16_kernel<128, q4_0, q4_0, contiguous>"},
         "prefill_q4_0_unfused": {"tflops": round(qflops / (float(u_ms.mean()) * 1e-3) / 1e12, 3),
                                  "ms_mean": round(float(u_ms.mean()), 5),
                                  "ms_median": round(float(np.median(u_ms)), 5),
