@@ -521,6 +521,37 @@ __device__ __forceinline__ float rowpair_max(float x)
     return fmaxf(a, b);
 }
 
+// max / sum over the 64 lanes of a wave, the result in every lane: DPP row rotates inside the
+// 16-lane rows, then v_permlane16_swap and v_permlane32_swap across them (no LDS round trips)
+__device__ __forceinline__ float wave_max(float x)
+{
+    x = vmax(x, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x),
+                                                                   0x121, 0xF, 0xF, false)));
+    x = vmax(x, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x),
+                                                                   0x122, 0xF, 0xF, false)));
+    x = vmax(x, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x),
+                                                                   0x124, 0xF, 0xF, false)));
+    x = vmax(x, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x),
+                                                                   0x128, 0xF, 0xF, false)));
+    float a = x, b = x;
+    asm("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+    return pair_max(vmax(a, b));
+}
+__device__ __forceinline__ float wave_sum(float x)
+{
+    x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x121,
+                                                            0xF, 0xF, false));
+    x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x122,
+                                                            0xF, 0xF, false));
+    x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x124,
+                                                            0xF, 0xF, false));
+    x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x128,
+                                                            0xF, 0xF, false));
+    float a = x, b = x;
+    asm("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+    return pair_sum(a + b);
+}
+
 // Wait until at most N vector-memory operations of this wave are outstanding; also a compiler
 // memory fence, so no LDS read of the landed data moves above it.
 template <int N>
@@ -1106,9 +1137,12 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeParams p)
 
     if (p.n_split <= 64) {
         // One memory round trip: every split's outputs (E per lane), frames and sums are
-        // loaded at once; split u's weight is lane u's, read back with v_readlane.
+        // loaded at once, the frame and sum first so that the weights are formed while the
+        // outputs are in flight; split u's weight is lane u's, read back with v_readlane.
         constexpr int E = D / 64;
         const int ns = p.n_split;
+        const bool on = lane < ns;
+        const f32x2 fl = *(const f32x2 *)(base + (int64_t)min(lane, ns - 1) * stride + D);
         float x[64][E];
 #pragma unroll
         for (int u = 0; u < 64; ++u) {
@@ -1121,18 +1155,11 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeParams p)
                 x[u][0] = *src;
             }
         }
-        const bool on = lane < ns;
-        const float f = on ? base[(int64_t)lane * stride + D] : -INFINITY;
-        const float l = on ? base[(int64_t)lane * stride + D + 1] : 0.0f;
-        float F = f;
-#pragma unroll
-        for (int m = 32; m >= 1; m >>= 1)
-            F = fmaxf(F, __shfl_xor(F, m, 64));
+        const float f = on ? fl[0] : -INFINITY;
+        const float l = on ? fl[1] : 0.0f;
+        const float F = wave_max(f);
         const float w = (F == -INFINITY || !on) ? 0.0f : exp2_fast(f - F);
-        float L = w * l;
-#pragma unroll
-        for (int m = 32; m >= 1; m >>= 1)
-            L += __shfl_xor(L, m, 64);
+        const float L = wave_sum(w * l);
         const float inv = L > 0.0f ? 1.0f / L : 0.0f;
         float o[E];
 #pragma unroll
@@ -1155,19 +1182,15 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeParams p)
 
     float F = -INFINITY;
     for (int s = lane; s < p.n_split; s += 64)
-        F = fmaxf(F, base[(int64_t)s * stride + D]);
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1)
-        F = fmaxf(F, __shfl_xor(F, m, 64));
+        F = vmax(F, base[(int64_t)s * stride + D]);
+    F = wave_max(F);
     float L = 0.0f;
     for (int s = lane; s < p.n_split; s += 64) {
         const float w = F == -INFINITY ? 0.0f : exp2_fast(base[(int64_t)s * stride + D] - F);
         wts[s] = w;
         L += w * base[(int64_t)s * stride + D + 1];
     }
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1)
-        L += __shfl_xor(L, m, 64);
+    L = wave_sum(L);
     __syncthreads();
     const float inv = L > 0.0f ? 1.0f / L : 0.0f;
 
