@@ -53,6 +53,8 @@ PEAK_HBM_GBS = 8000.0              # MI355X HBM3E, published
 PAGES_PREFILL_16K_TFLOPS = 1.20    # the pages' fixed kernel at 16K keys (Radeon 8060S, gfx1151)
 FLUSH_BYTES = 1 << 30
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_16k_f16_traffic.txt")
+DECODE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_q4_0_traffic.txt")
+MFMA_UTIL_FILE = os.path.join(ROOT, "profiles", "prefill_16k_mfma_util.txt")
 CLOCK_WARMUP_S = 0.25
 
 
@@ -66,13 +68,13 @@ def source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def stored_traffic():
-    """HBM bytes per prefill launch from the committed counter summary, if it was taken on the
-    current kernel sources."""
-    if not os.path.exists(TRAFFIC_FILE):
+def stored_traffic(path=TRAFFIC_FILE):
+    """HBM bytes per launch from a committed counter summary, if it was taken on the current
+    kernel sources."""
+    if not os.path.exists(path):
         return None
     kv = {}
-    for line in open(TRAFFIC_FILE):
+    for line in open(path):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
@@ -92,6 +94,80 @@ def calibrate_copy(torch):
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"calibrate_copy_bytes_read": n, "calibrate_copy_bytes_written": n}), flush=True)
+
+
+def stored_mfma_util():
+    """(MFMA busy %, clock MHz) of the f16 prefill kernel from the committed counter summary, if
+    it was taken on the current kernel sources."""
+    if not os.path.exists(MFMA_UTIL_FILE):
+        return None
+    text = open(MFMA_UTIL_FILE).read()
+    if f"source_hash {source_hash()}" not in text:
+        return None
+    for line in text.splitlines():
+        if line.startswith("prefill16_kernel<128/0/0/false>,"):
+            f = [x.strip() for x in line.split(",")]
+            return float(f[3]), float(f[2])
+    return None
+
+
+class ClockSampler:
+    """Samples the GPU's current shader-clock DPM level (the marked line of the amdgpu driver's
+    pp_dpm_sclk) every 10 ms on a host thread; None where the file is not readable. This is the
+    level the driver set, not the average clock under load, which the counter summary gives."""
+
+    def __init__(self):
+        import glob
+        import threading
+        self.paths = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+        self.mhz = []
+        self.stop = threading.Event()
+        self.thread = threading.Thread(target=self.run, daemon=True)
+
+    def read(self):
+        for path in self.paths:
+            try:
+                for line in open(path):
+                    if "*" in line:
+                        return float(line.split(":")[1].strip().lower().split("mhz")[0])
+            except (OSError, ValueError, IndexError):
+                continue
+        return None
+
+    def run(self):
+        while not self.stop.wait(0.01):
+            v = self.read()
+            if v is not None:
+                self.mhz.append(v)
+
+    def __enter__(self):
+        if self.paths:
+            self.thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self.stop.set()
+        if self.thread.is_alive():
+            self.thread.join()
+
+    def summary(self):
+        if not self.mhz:
+            return None
+        import numpy as np
+        a = np.array(self.mhz)
+        return {"samples": int(a.size), "median_mhz": float(np.median(a)),
+                "min_mhz": float(a.min()), "max_mhz": float(a.max()),
+                "source": "pp_dpm_sclk (the DPM level set), every 10 ms during the timed steps"}
+
+
+def host_cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def cpu_baseline(w, x, seconds: float):
@@ -124,6 +200,7 @@ def cpu_baseline(w, x, seconds: float):
     n_big = int(min(total, max(n, n * seconds / max(dt, 1e-3))))
     dt, flops, n = run(n_big)
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "cpu_model": host_cpu_model(), "nproc": os.cpu_count(),
             "sample": f"{n} of {total} query rows of the 2Kx16K f16 prefill (uniform random), "
                       f"{flops / 1e9:.1f} GFLOP in {dt:.1f} s, {threads} OpenMP threads",
             "seconds": dt}
@@ -299,11 +376,12 @@ def main():
     for k in range(args.warmup):
         step(None, k)
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(i, i)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    with ClockSampler() as clocks:
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            step(i, i)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
 
     p_ms = np.array([e[0].elapsed_time(e[1]) for e in ev])
     d_ms = np.array([e[2].elapsed_time(e[3]) for e in ev])
@@ -327,6 +405,8 @@ def main():
     gbs = dbytes / d_s / 1e9
 
     traffic = stored_traffic()
+    dtraffic = stored_traffic(DECODE_TRAFFIC_FILE)
+    util = stored_mfma_util()
     line = {
         "metric": METRIC,
         "value": round(tflops, 3),
@@ -348,16 +428,28 @@ def main():
                    "cache_flush_bytes_read_before_each_call": FLUSH_BYTES},
         "prefill": {"tflops": round(tflops, 3), "ms_mean": round(float(p_ms.mean()), 5),
                     "ms_median": round(float(np.median(p_ms)), 5),
-                    "ms_min": round(float(p_ms.min()), 5), "gflop": round(flops / 1e9, 3)},
+                    "ms_min": round(float(p_ms.min()), 5),
+                    "ms_p90": round(float(np.percentile(p_ms, 90)), 5),
+                    "gflop": round(flops / 1e9, 3)},
         "decode": {"value": round(gbs, 1), "unit": "GB/s", "ms_mean": round(float(d_ms.mean()), 5),
                    "ms_median": round(float(np.median(d_ms)), 5),
-                   "ms_min": round(float(d_ms.min()), 5), "algorithmic_bytes": dbytes,
+                   "ms_min": round(float(d_ms.min()), 5),
+                   "ms_p90": round(float(np.percentile(d_ms, 90)), 5),
+                   "algorithmic_bytes": dbytes,
                    "kernels": "decode_q4g_kernel + decode_merge_kernel"},
+        "gpu_clock": clocks.summary(),
         "roofline": {"bound": "mfma", "achieved": round(tflops, 3), "peak": PEAK_MFMA_F16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK_MFMA_F16_TFLOPS, 4),
                      "traffic": traffic, "kernel": "prefill16_kernel<128, f16, f16, contiguous>",
-                     "algorithmic_flops_per_launch": flops},
+                     "algorithmic_flops_per_launch": flops,
+                     # from profiles/prefill_16k_mfma_util.txt (rocprofv3 counters), if current
+                     "mfma_busy_pct_counters": util[0] if util else None,
+                     "clock_mhz_counters": util[1] if util else None,
+                     "frac_of_clock_corrected_peak": (
+                         round(tflops / (PEAK_MFMA_F16_TFLOPS * util[1] / 2400.0), 4)
+                         if util else None)},
         "roofline_decode": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                            "traffic": dtraffic,
                             "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
                             "algorithmic_bytes_per_call": dbytes},
         "prefill_q4_0": {"workload": "prefill_16k_q4_0 (the prefill workload against a q4_0 "
