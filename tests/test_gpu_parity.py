@@ -526,3 +526,72 @@ def test_paged_mixed_matches_oracle():
                                    scale=w.scale)
             err = float(np.max(np.abs(got[b, :m] - ref[0])))
             assert err <= TOL["q4_0"], (call, b, err)
+
+
+# ---------------------------------------------------------------------------------------------
+# paged limits: long logical sequences over a small page pool (a block table may name one
+# physical page many times), so the table and the runs of it the kernels hold are exercised
+# at full length while the buffers stay small
+# ---------------------------------------------------------------------------------------------
+
+def _pool(rng, n_pages, Hkv, D, kv):
+    x = rng.standard_normal((n_pages, 64, Hkv, D), dtype=np.float32)
+    if kv == "q4_0":
+        return W.quantize_q4_0(x.reshape(-1, D)).reshape(n_pages, 64, Hkv, D // 32 * 18)
+    return x.astype(np.float16)
+
+
+def _gather(pool, table_row, n):
+    pages = pool[table_row[:(n + 63) // 64]]
+    return pages.reshape((-1,) + pool.shape[2:])[:n][None]
+
+
+@pytest.mark.parametrize("kv,B,Hq,Hkv", [("f16", 64, 8, 8), ("q4_0", 256, 8, 2)])
+def test_decode_paged_long_splits(kv, B, Hq, Hkv):
+    """Splits of 67 tiles (B x Hkv = 512 key ranges, so one split each): the run of 64 table
+    entries a wave holds is fetched again inside the split. f16: the 16-bit split kernel;
+    q4_0 with Hkv = 2: the kernel whose waves take every 4th tile."""
+    rng = np.random.default_rng(111)
+    D, n_pages, max_pages = 64, 16, 67
+    lens = rng.integers(64 * 65, 64 * 67 + 1, size=B).astype(np.int32)
+    lens[:3] = [64 * 67, 64 * 66 + 1, 64 * 65 - 7]
+    kp, vp = _pool(rng, n_pages, Hkv, D, kv), _pool(rng, n_pages, Hkv, D, kv)
+    table = rng.integers(0, n_pages, size=(B, max_pages)).astype(np.int32)
+    q = rng.standard_normal((B, 1, Hq, D), dtype=np.float32).astype(np.float16)
+    say(f"paged decode, long splits: {kv} B={B} Hq={Hq} Hkv={Hkv}")
+    got = fa.decode_paged(torch.from_numpy(q).cuda(), to_dev(kp, kv), to_dev(vp, kv),
+                          torch.from_numpy(table).cuda(), torch.from_numpy(lens).cuda(),
+                          causal=True, scale=D ** -0.5)
+    torch.cuda.synchronize()
+    got = got.float().cpu().numpy()
+    for b in (0, 1, 2, B // 2, B - 1):
+        n = int(lens[b])
+        ref = oracle.attention(q[b:b + 1], _gather(kp, table[b], n), _gather(vp, table[b], n),
+                               q_dtype="f16", kv_dtype=kv, causal=True, offset=n - 1,
+                               scale=D ** -0.5)
+        err = float(np.max(np.abs(got[b] - ref[0])))
+        assert err <= TOL[kv], (kv, b, n, err)
+
+
+def test_prefill_paged_full_page_table():
+    """A sequence of 4096 pages (262144 keys), the most the prefill kernel's LDS page table
+    holds, with a 64-query chunk at its end; and one of 4095 pages plus a partial last page."""
+    rng = np.random.default_rng(112)
+    B, Hq, Hkv, D, Sq, n_pages, max_pages = 2, 4, 1, 64, 64, 32, 4096
+    lens = np.array([64 * 4096, 64 * 4095 + 5], np.int32)
+    kp, vp = _pool(rng, n_pages, Hkv, D, "f16"), _pool(rng, n_pages, Hkv, D, "f16")
+    table = rng.integers(0, n_pages, size=(B, max_pages)).astype(np.int32)
+    q = rng.standard_normal((B, Sq, Hq, D), dtype=np.float32).astype(np.float16)
+    say("paged prefill, 4096-page table")
+    got = fa.prefill_paged(torch.from_numpy(q).cuda(), to_dev(kp, "f16"), to_dev(vp, "f16"),
+                           torch.from_numpy(table).cuda(), torch.from_numpy(lens).cuda(),
+                           causal=True, scale=D ** -0.5)
+    torch.cuda.synchronize()
+    got = got.float().cpu().numpy()
+    for b in range(B):
+        n = int(lens[b])
+        ref = oracle.attention(q[b:b + 1], _gather(kp, table[b], n), _gather(vp, table[b], n),
+                               q_dtype="f16", kv_dtype="f16", causal=True, offset=n - Sq,
+                               scale=D ** -0.5)
+        err = float(np.max(np.abs(got[b] - ref[0])))
+        assert err <= TOL["f16"], (b, n, err)
