@@ -217,7 +217,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for "
+        print(f"bench.py measures one GPU: the library has no multi-GPU path (asked for "
               f"--gpus {args.gpus}); run with --gpus 1", file=sys.stderr, flush=True)
         sys.exit(2)
 
