@@ -17,7 +17,8 @@ One step = one pass of the whole path over resident inputs:
   * mixed caches (f16 K, q4_0 V): the prefill workload and the decode workload's shape with
     those types (reported);
   * head dim 64: the prefill workload at D = 64, and the B=2, S=512, 8-head D=64 causal
-    self-attention check shape (reported; the latter is launch- and latency-bound).
+    self-attention check shape (reported; the latter is launch- and latency-bound);
+  * the decode workload's shape with an f16 cache (537 MB; the 16-bit split kernel).
 Before each call a 1 GiB buffer is read so that neither call finds its inputs in the 256 MB
 last-level cache (the decode working set, 151 MB, would otherwise stay resident). The flush
 reads rather than writes: a written flush leaves up to 256 MB of dirty lines in that cache,
@@ -282,6 +283,10 @@ def main():
     dkf = to_dev(W.generate(wd.with_(kv="f16")).k, "f16")
     do3 = torch.empty_like(dq)
     mbytes = dkf.numel() * 2 + dv.numel() + 2 * dq.numel() * 2
+    # the decode shape with an f16 cache (K from the mixed leg's f16 draw, V its own)
+    dvf = to_dev(W.generate(wd.with_(kv="f16", seed=wd.seed + 1)).v, "f16")
+    do4 = torch.empty_like(dq)
+    fbytes = (dkf.numel() + dvf.numel()) * 2 + 2 * dq.numel() * 2
     # head dim 64
     w64 = wp.with_(D=64)
     x64 = W.generate(w64)
@@ -351,8 +356,12 @@ def main():
         fa.prefill(qsm, ksm, vsm, causal=True, offset=wsm.causal_offset, scale=wsm.scale,
                    out=osm, stream=stream)
 
+    def decode_f16():
+        fa.decode(dq, dkf, dvf, causal=True, offset=wd.causal_offset, scale=wd.scale, out=do4,
+                  workspace=ws, stream=stream)
+
     calls = [prefill, decode, prefill_q4, prefill_q4_unfused, quantize, decode_paged,
-             prefill_paged, prefill_mixed, decode_mixed, prefill_d64, check_d64]
+             prefill_paged, prefill_mixed, decode_mixed, prefill_d64, check_d64, decode_f16]
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * len(calls))]
           for _ in range(args.steps)]
 
@@ -394,6 +403,7 @@ def main():
     dm_ms = np.array([e[16].elapsed_time(e[17]) for e in ev])
     d64_ms = np.array([e[18].elapsed_time(e[19]) for e in ev])
     sm_ms = np.array([e[20].elapsed_time(e[21]) for e in ev])
+    df_ms = np.array([e[22].elapsed_time(e[23]) for e in ev])
     f64 = W.attention_flops(w64)
     fsm = W.attention_flops(wsm)
     qflops = W.attention_flops(wq)
@@ -499,6 +509,12 @@ def main():
         "check_d64": {"what": "causal self-attention B=2, S=512, Hq=Hkv=8, D=64, f16 (one call)",
                       "us_mean": round(float(sm_ms.mean()) * 1e3, 2),
                       "tflops": round(fsm / (float(sm_ms.mean()) * 1e-3) / 1e12, 3)},
+        "decode_f16": {"what": "4 x 1 query against 32768 keys, f16 K and V (split + merge)",
+                       "value": round(fbytes / (float(df_ms.mean()) * 1e-3) / 1e9, 1),
+                       "unit": "GB/s", "bytes": int(fbytes),
+                       "ms_mean": round(float(df_ms.mean()), 5),
+                       "frac_of_hbm_peak": round(fbytes / (float(df_ms.mean()) * 1e-3) / 1e9
+                                                 / PEAK_HBM_GBS, 4)},
         "quantize_q4_0": {"what": "fa_quantize_q4_0 of f16 K and V [1, 16384, 8, 128] (two "
                                   "launches)",
                           "gbs": round(wbytes / (float(w_ms.mean()) * 1e-3) / 1e9, 1),
