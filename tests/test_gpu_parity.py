@@ -235,6 +235,11 @@ DECODE = [
     wl("decode_q4_0_before_keys", 1, 8, 2, 1, 300, 128, "q4_0", True, -5, seed=55),
     # one KV head: more than 64 splits, the merge kernel's looped path
     wl("decode_many_splits", 1, 4, 1, 1, 10000, 128, "f16", True, 9999, seed=56),
+    # head-group q4_0 kernel with 157 splits per head group: the merge kernel's looped path
+    # behind that kernel, ragged last split
+    wl("decode_q4_0_many_splits", 1, 32, 8, 1, 20000, 128, "q4_0", True, 19999, seed=57),
+    # 1100 head groups of one split each (a large batch of short sequences), D = 64
+    wl("decode_q4_0_large_batch", 1100, 16, 4, 1, 100, 64, "q4_0", True, 99, seed=58),
 ]
 
 
