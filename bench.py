@@ -18,7 +18,10 @@ One step = one pass of the whole path over resident inputs:
     those types (reported);
   * head dim 64: the prefill workload at D = 64, and the B=2, S=512, 8-head D=64 causal
     self-attention check shape (reported; the latter is launch- and latency-bound);
-  * the decode workload's shape with an f16 cache (537 MB; the 16-bit split kernel).
+  * the decode workload's shape with an f16 cache (537 MB; the 16-bit split kernel);
+  * the rest of the chunked-prefill configuration: 2048 queries at the end of 2048 and 8192
+    keys (f16 and bf16), bf16 at 16384 keys, and the score-ramp variant at 16384 keys (f16 and
+    bf16), under `prefill_sweep` (reported).
 Before each call a 1 GiB buffer is read so that neither call finds its inputs in the 256 MB
 last-level cache (the decode working set, 151 MB, would otherwise stay resident). The flush
 reads rather than writes: a written flush leaves up to 256 MB of dirty lines in that cache,
@@ -33,7 +36,7 @@ HIP events on the launch stream); the decode HBM GB/s figure sits in `decode`. `
 for the prefill kernel, `roofline_decode` for the decode pair. `cpu_baseline` times the CPU
 oracle on a bounded sample of the prefill workload's rows.
 
-    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--no-sweep]
     python bench.py --calibrate-copy     # a plain 256 MiB device copy, for HBM counter scaling
 """
 from __future__ import annotations
@@ -57,6 +60,9 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_16k_f16_traffic.txt")
 DECODE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_q4_0_traffic.txt")
 MFMA_UTIL_FILE = os.path.join(ROOT, "profiles", "prefill_16k_mfma_util.txt")
 CLOCK_WARMUP_S = 0.25
+# the chunked-prefill configuration's other key counts, dtypes and the score ramp
+SWEEP = ["prefill_2k_f16", "prefill_8k_f16", "prefill_2k_bf16", "prefill_8k_bf16",
+         "prefill_16k_bf16", "prefill_16k_f16_ramp", "prefill_16k_bf16_ramp"]
 
 
 def source_hash() -> str:
@@ -215,6 +221,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--calibrate-copy", action="store_true")
+    # leave out the prefill sweep, whose f16 legs run the headline prefill's kernel at other
+    # sizes: a kernel-trace profile of the run then averages only the headline launches
+    ap.add_argument("--no-sweep", action="store_true")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -301,6 +310,13 @@ def main():
     wbytes = (pk.numel() + pv.numel()) * 2 + wk.numel() + wv.numel()
     ws = torch.empty(max(16, fa.decode_workspace_bytes(wd.B, wd.Hq, wd.Hkv, wd.Sq, wd.Sk, wd.D)),
                      dtype=torch.uint8, device=dev)
+    sweep = []
+    for name in ([] if args.no_sweep else SWEEP):
+        w = W.WORKLOADS[name]
+        x = W.generate(w)
+        sq_ = to_dev(x.q, w.q_dtype)
+        sweep.append((w, sq_, to_dev(x.k, w.kv), to_dev(x.v, w.kv), torch.empty_like(sq_)))
+        del x
     # float32, so sum() is one reduction kernel that only reads (an int32 sum would first
     # write an int64 copy)
     flush = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
@@ -360,8 +376,16 @@ def main():
         fa.decode(dq, dkf, dvf, causal=True, offset=wd.causal_offset, scale=wd.scale, out=do4,
                   workspace=ws, stream=stream)
 
+    def sweep_call(w, q_, k_, v_, o_):
+        def call():
+            fa.prefill(q_, k_, v_, causal=True, offset=w.causal_offset, scale=w.scale, out=o_,
+                       stream=stream)
+        return call
+
     calls = [prefill, decode, prefill_q4, prefill_q4_unfused, quantize, decode_paged,
              prefill_paged, prefill_mixed, decode_mixed, prefill_d64, check_d64, decode_f16]
+    n_fixed = len(calls)
+    calls += [sweep_call(*c) for c in sweep]
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * len(calls))]
           for _ in range(args.steps)]
 
@@ -404,6 +428,17 @@ def main():
     d64_ms = np.array([e[18].elapsed_time(e[19]) for e in ev])
     sm_ms = np.array([e[20].elapsed_time(e[21]) for e in ev])
     df_ms = np.array([e[22].elapsed_time(e[23]) for e in ev])
+    prefill_sweep = {}
+    for j, (w, *_rest) in enumerate(sweep):
+        c = n_fixed + j
+        ms = np.array([e[2 * c].elapsed_time(e[2 * c + 1]) for e in ev])
+        tf = W.attention_flops(w) / (float(ms.mean()) * 1e-3) / 1e12
+        prefill_sweep[w.name] = {
+            "shape": f"B={w.B} Sq={w.Sq} Sk={w.Sk} Hq={w.Hq} Hkv={w.Hkv} D={w.D} {w.kv}"
+                     + (f", score ramp +{w.ramp} per key" if w.ramp else ""),
+            "tflops": round(tf, 3), "ms_mean": round(float(ms.mean()), 5),
+            "ms_median": round(float(np.median(ms)), 5),
+            "frac_of_mfma_peak": round(tf / PEAK_MFMA_F16_TFLOPS, 4)}
     f64 = W.attention_flops(w64)
     fsm = W.attention_flops(wsm)
     qflops = W.attention_flops(wq)
@@ -522,6 +557,7 @@ def main():
                           "bytes": int(wbytes),
                           "frac_of_hbm_peak": round(wbytes / (float(w_ms.mean()) * 1e-3) / 1e9
                                                     / PEAK_HBM_GBS, 4)},
+        "prefill_sweep": prefill_sweep,
         "source_hash": source_hash(),
     }
     if not args.no_cpu_baseline:
