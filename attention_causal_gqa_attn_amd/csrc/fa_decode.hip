@@ -1118,7 +1118,8 @@ __global__ __launch_bounds__(kThreads, 2) void decode_q4w_kernel(DecodeParams p)
                      kvh, s, t);
 }
 
-// One wave per (b, KV head, row): log-sum-exp merge of the row's n_split partials.
+// More than 64 splits: one wave per (b, KV head, row), log-sum-exp merge of the row's n_split
+// partials in a loop.
 template <int D, bool BF>
 __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeParams p)
 {
@@ -1134,51 +1135,6 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeParams p)
     const float *base = p.part + ((int64_t)b * a.Hkv + kvh) * p.n_split * stride + rr * (D + 2);
     const int qi = rr / a.G, hl = rr % a.G;
     uint16_t *op = (uint16_t *)a.o + (((int64_t)b * a.Sq + qi) * a.Hq + kvh * a.G + hl) * D;
-
-    if (p.n_split <= 64) {
-        // One memory round trip: every split's outputs (E per lane), frames and sums are
-        // loaded at once, the frame and sum first so that the weights are formed while the
-        // outputs are in flight; split u's weight is lane u's, read back with v_readlane.
-        constexpr int E = D / 64;
-        const int ns = p.n_split;
-        const bool on = lane < ns;
-        const f32x2 fl = *(const f32x2 *)(base + (int64_t)min(lane, ns - 1) * stride + D);
-        float x[64][E];
-#pragma unroll
-        for (int u = 0; u < 64; ++u) {
-            const float *src = base + (int64_t)min(u, ns - 1) * stride + E * lane;
-            if constexpr (E == 2) {
-                const f32x2 v2 = *(const f32x2 *)src;
-                x[u][0] = v2[0];
-                x[u][1] = v2[1];
-            } else {
-                x[u][0] = *src;
-            }
-        }
-        const float f = on ? fl[0] : -INFINITY;
-        const float l = on ? fl[1] : 0.0f;
-        const float F = wave_max(f);
-        const float w = (F == -INFINITY || !on) ? 0.0f : exp2_fast(f - F);
-        const float L = wave_sum(w * l);
-        const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-        float o[E];
-#pragma unroll
-        for (int e = 0; e < E; ++e)
-            o[e] = 0.0f;
-#pragma unroll
-        for (int u = 0; u < 64; ++u) {
-            const float wu = __builtin_bit_cast(
-                float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), u));
-#pragma unroll
-            for (int e = 0; e < E; ++e)
-                o[e] += wu * x[u][e];
-        }
-        if constexpr (E == 2)
-            *(uint32_t *)(op + 2 * lane) = pack2<BF>(o[0] * inv, o[1] * inv);
-        else
-            op[lane] = (uint16_t)(pack2<BF>(o[0] * inv, 0.0f) & 0xFFFFu);
-        return;
-    }
 
     float F = -INFINITY;
     for (int s = lane; s < p.n_split; s += 64)
@@ -1218,6 +1174,77 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeParams p)
     }
 }
 
+// At most 64 splits: four waves per (b, KV head, row). Every split's output row, frame and
+// sum is loaded in one round (wave w holds splits w, w + 4, ..., 16 per lane, so a lane has
+// 16 loads in flight instead of 64), the frames and sums first so that the weights are formed
+// while the outputs are in flight; split u's weight is lane u's, read back with v_readlane;
+// the four waves' partial rows meet in LDS.
+template <int D, bool BF>
+__global__ __launch_bounds__(256) void decode_merge4_kernel(DecodeParams p)
+{
+    constexpr int E = D / 64;
+    __shared__ float part[3][D];
+    const AttnArgs &a = p.a;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    int rest = blockIdx.x;
+    const int rr = rest % p.rows;
+    rest /= p.rows;
+    const int kvh = rest % a.Hkv;
+    const int b = rest / a.Hkv;
+    const int stride = p.rows * (D + 2);
+    const float *base = p.part + ((int64_t)b * a.Hkv + kvh) * p.n_split * stride + rr * (D + 2);
+    const int ns = p.n_split;
+    const bool on = lane < ns;
+    const f32x2 fl = *(const f32x2 *)(base + (int64_t)min(lane, ns - 1) * stride + D);
+    float x[16][E];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+        const float *src = base + (int64_t)min(wave + 4 * u, ns - 1) * stride + E * lane;
+        if constexpr (E == 2) {
+            const f32x2 v2 = *(const f32x2 *)src;
+            x[u][0] = v2[0];
+            x[u][1] = v2[1];
+        } else {
+            x[u][0] = *src;
+        }
+    }
+    const float f = on ? fl[0] : -INFINITY;
+    const float l = on ? fl[1] : 0.0f;
+    const float F = wave_max(f);
+    const float w = (F == -INFINITY || !on) ? 0.0f : exp2_fast(f - F);
+    const float L = wave_sum(w * l);
+    float o[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+        o[e] = 0.0f;
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+        const float wu = __builtin_bit_cast(
+            float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), wave + 4 * u));
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+            o[e] += wu * x[u][e];
+    }
+    if (wave > 0)
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+            part[wave - 1][E * lane + e] = o[e];
+    __syncthreads();
+    if (wave > 0)
+        return;
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+        o[e] += part[0][E * lane + e] + part[1][E * lane + e] + part[2][E * lane + e];
+    const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+    const int qi = rr / a.G, hl = rr % a.G;
+    uint16_t *op = (uint16_t *)a.o + (((int64_t)b * a.Sq + qi) * a.Hq + kvh * a.G + hl) * D;
+    if constexpr (E == 2)
+        *(uint32_t *)(op + 2 * lane) = pack2<BF>(o[0] * inv, o[1] * inv);
+    else
+        op[lane] = (uint16_t)(pack2<BF>(o[0] * inv, 0.0f) & 0xFFFFu);
+}
+
 template <int D, int KV>
 hipError_t launch(const DecodeParams &p, int64_t n_wg, hipStream_t stream)
 {
@@ -1239,8 +1266,12 @@ hipError_t launch(const DecodeParams &p, int64_t n_wg, hipStream_t stream)
     if (e != hipSuccess)
         return e;
     const int64_t n_rows = (int64_t)p.a.B * p.a.Hkv * p.rows;
-    hipLaunchKernelGGL((decode_merge_kernel<D, KV == KV_BF16>), dim3((unsigned)n_rows), dim3(64),
-                       0, stream, p);
+    if (p.n_split <= 64)
+        hipLaunchKernelGGL((decode_merge4_kernel<D, KV == KV_BF16>), dim3((unsigned)n_rows),
+                           dim3(256), 0, stream, p);
+    else
+        hipLaunchKernelGGL((decode_merge_kernel<D, KV == KV_BF16>), dim3((unsigned)n_rows),
+                           dim3(64), 0, stream, p);
     return hipGetLastError();
 }
 
