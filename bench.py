@@ -481,7 +481,7 @@ def main():
                    "ms_min": round(float(d_ms.min()), 5),
                    "ms_p90": round(float(np.percentile(d_ms, 90)), 5),
                    "algorithmic_bytes": dbytes,
-                   "kernels": "decode_q4g_kernel + decode_merge_kernel"},
+                   "kernels": "decode_q4g_kernel + decode_merge4_kernel"},
         "gpu_clock": clocks.summary(),
         "roofline": {"bound": "mfma", "achieved": round(tflops, 3), "peak": PEAK_MFMA_F16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK_MFMA_F16_TFLOPS, 4),
