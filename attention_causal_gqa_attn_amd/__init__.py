@@ -6,11 +6,11 @@ the stream argument, and a non-zero status becomes an FAError. Every step of the
 runs in the HIP kernels of libfa.so; there is no Python or CPU fallback, and if the library is
 missing every call raises.
 
-Raw entry points with the C names (pointers and ints): fa_prefill, fa_decode,
-fa_decode_paged, fa_prefill_paged, fa_decode_workspace_bytes, fa_dequant_q4_0,
-fa_quantize_q4_0, fa_strerror, fa_version.
-Tensor helpers: prefill, prefill_paged, decode, decode_paged, decode_workspace_bytes,
-dequant_q4_0, quantize_q4_0.
+Raw entry points with the C names (pointers and ints): fa_prefill, fa_prefill_split,
+fa_prefill_workspace_bytes, fa_decode, fa_decode_paged, fa_prefill_paged,
+fa_decode_workspace_bytes, fa_dequant_q4_0, fa_quantize_q4_0, fa_strerror, fa_version.
+Tensor helpers: prefill, prefill_split, prefill_workspace_bytes, prefill_paged, decode,
+decode_paged, decode_workspace_bytes, dequant_q4_0, quantize_q4_0.
 """
 from __future__ import annotations
 
@@ -35,9 +35,9 @@ FA_ERR_ALIGN = -6
 FA_ERR_HIP = -7
 FA_ERR_VALUE = -8
 
-EXPORTS = ("fa_prefill", "fa_decode", "fa_decode_paged", "fa_prefill_paged",
-           "fa_decode_workspace_bytes", "fa_dequant_q4_0", "fa_quantize_q4_0", "fa_strerror",
-           "fa_version")
+EXPORTS = ("fa_prefill", "fa_prefill_split", "fa_prefill_workspace_bytes", "fa_decode",
+           "fa_decode_paged", "fa_prefill_paged", "fa_decode_workspace_bytes", "fa_dequant_q4_0",
+           "fa_quantize_q4_0", "fa_strerror", "fa_version")
 PAGE_KEYS = 64
 
 
@@ -63,6 +63,10 @@ def load() -> ctypes.CDLL:
         attn = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i64, f32, i32]
         lib.fa_prefill.argtypes = attn + [vp]
         lib.fa_prefill.restype = i32
+        lib.fa_prefill_split.argtypes = attn + [vp, sz, vp]
+        lib.fa_prefill_split.restype = i32
+        lib.fa_prefill_workspace_bytes.argtypes = [i32] * 7 + [i64, i32]
+        lib.fa_prefill_workspace_bytes.restype = sz
         lib.fa_decode.argtypes = attn + [vp, sz, vp]
         lib.fa_decode.restype = i32
         lib.fa_decode_paged.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
@@ -91,6 +95,17 @@ def fa_prefill(q, k, v, o, B, Hq, Hkv, Sq, Sk, D, causal, causal_offset, scale, 
                stream) -> int:
     return load().fa_prefill(q, k, v, o, B, Hq, Hkv, Sq, Sk, D, causal, causal_offset, scale,
                              kv_dtype, stream)
+
+
+def fa_prefill_split(q, k, v, o, B, Hq, Hkv, Sq, Sk, D, causal, causal_offset, scale, kv_dtype,
+                     workspace, workspace_bytes, stream) -> int:
+    return load().fa_prefill_split(q, k, v, o, B, Hq, Hkv, Sq, Sk, D, causal, causal_offset,
+                                   scale, kv_dtype, workspace, workspace_bytes, stream)
+
+
+def fa_prefill_workspace_bytes(B, Hq, Hkv, Sq, Sk, D, causal, causal_offset, kv_dtype) -> int:
+    return load().fa_prefill_workspace_bytes(B, Hq, Hkv, Sq, Sk, D, causal, causal_offset,
+                                             kv_dtype)
 
 
 def fa_decode(q, k, v, o, B, Hq, Hkv, Sq, Sk, D, causal, causal_offset, scale, kv_dtype,
@@ -218,6 +233,38 @@ def prefill(q, k, v, *, causal: bool = True, offset: Optional[int] = None,
                     Sk, D, int(bool(causal)), offset, scale, kv, _stream(q, stream))
     if rc != FA_OK:
         raise FAError(rc, "fa_prefill")
+    return out
+
+
+def prefill_workspace_bytes(q, k, v, *, causal: bool = True, offset: Optional[int] = None) -> int:
+    """Workspace bytes fa_prefill_split needs for these tensors (0: nothing to split)."""
+    kv = _kv_code(k, v)
+    B, Hq, Hkv, Sq, Sk, D = _sizes(q, k, v, kv)
+    offset = Sk - Sq if offset is None else int(offset)
+    return fa_prefill_workspace_bytes(B, Hq, Hkv, Sq, Sk, D, int(bool(causal)), offset, kv)
+
+
+def prefill_split(q, k, v, *, causal: bool = True, offset: Optional[int] = None,
+                  scale: Optional[float] = None, out=None, workspace=None, stream=None):
+    """Causal prefill balanced across workgroups via fa_prefill_split. A zero-filled
+    workspace of prefill_workspace_bytes(...) bytes is allocated when none is given; a
+    workspace passed in must have had its first 4096 bytes zero before its first use (every
+    call leaves them zero)."""
+    torch = _torch()
+    kv = _kv_code(k, v)
+    B, Hq, Hkv, Sq, Sk, D = _sizes(q, k, v, kv)
+    offset = Sk - Sq if offset is None else int(offset)
+    scale = D ** -0.5 if scale is None else float(scale)
+    if out is None:
+        out = torch.empty_like(q)
+    if workspace is None:
+        nbytes = fa_prefill_workspace_bytes(B, Hq, Hkv, Sq, Sk, D, int(bool(causal)), offset, kv)
+        workspace = torch.zeros(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    rc = fa_prefill_split(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, Hq, Hkv,
+                          Sq, Sk, D, int(bool(causal)), offset, scale, kv, workspace.data_ptr(),
+                          workspace.numel() * workspace.element_size(), _stream(q, stream))
+    if rc != FA_OK:
+        raise FAError(rc, "fa_prefill_split")
     return out
 
 

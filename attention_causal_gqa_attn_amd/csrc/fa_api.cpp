@@ -113,6 +113,42 @@ int fa_prefill(const void *q, const void *k, const void *v, void *o, int B, int 
     return hip_status(fa::launch_prefill(a, (hipStream_t)stream));
 }
 
+size_t fa_prefill_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Sk, int D, int causal,
+                                  int64_t causal_offset, int kv_dtype)
+{
+    fa::AttnArgs a;
+    // sizes only: any non-null, aligned stand-in pointers pass the checks
+    const void *nz = (const void *)(uintptr_t)4096;
+    if (check_attention(nz, nz, nz, (void *)nz, B, Hq, Hkv, Sq, Sk, D, causal, causal_offset,
+                        1.0f, kv_dtype, a) != FA_OK)
+        return 0;
+    return fa::prefill_split_plan(a).workspace_bytes;
+}
+
+int fa_prefill_split(const void *q, const void *k, const void *v, void *o, int B, int Hq,
+                     int Hkv, int Sq, int Sk, int D, int causal, int64_t causal_offset,
+                     float scale, int kv_dtype, void *workspace, size_t workspace_bytes,
+                     fa_stream_t stream)
+{
+    fa::AttnArgs a;
+    const int rc = check_attention(q, k, v, o, B, Hq, Hkv, Sq, Sk, D, causal, causal_offset,
+                                   scale, kv_dtype, a);
+    if (rc != FA_OK)
+        return rc;
+    if ((int64_t)B * Sq == 0)
+        return FA_OK;
+    const fa::PrefillSplit sp = fa::prefill_split_plan(a);
+    if (fa::prefill_grid(a).n_wg + sp.n_tail > kMaxWorkgroups)
+        return FA_ERR_UNSUPPORTED;
+    if (sp.workspace_bytes > 0) {
+        if (!workspace || workspace_bytes < sp.workspace_bytes)
+            return FA_ERR_WORKSPACE;
+        if (!aligned(workspace, 16))
+            return FA_ERR_ALIGN;
+    }
+    return hip_status(fa::launch_prefill_split(a, sp, workspace, (hipStream_t)stream));
+}
+
 size_t fa_decode_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Sk, int D)
 {
     if (B <= 0 || Hq <= 0 || Hkv <= 0 || Sq <= 0 || Sk < 0 || Hq % Hkv != 0 ||

@@ -249,6 +249,47 @@ __device__ __forceinline__ void q4_split_block(const uint32_t w[5], uint32_t mis
     }
 }
 
+// Data that another workgroup reads in the same launch moves by device-scope (sc1) accesses,
+// which bypass the non-coherent per-CU and per-XCD caches: a store is complete once it has
+// reached the device's coherence point, and a load reads from there. A workgroup then only
+// has to wait for its stores to complete before it counts itself in (arrive_last); no
+// whole-L2 write-back or invalidate is needed. Pairs of floats (8-byte aligned) move as one
+// 8-byte access.
+__device__ __forceinline__ void store_through2(float *p, float x, float y)
+{
+    const uint64_t v = (uint64_t)__builtin_bit_cast(uint32_t, x) |
+                       ((uint64_t)__builtin_bit_cast(uint32_t, y) << 32);
+    __hip_atomic_store((uint64_t *)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ f32x2 load_through2(const float *p)
+{
+    const uint64_t v =
+        __hip_atomic_load((const uint64_t *)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return f32x2{__builtin_bit_cast(float, (uint32_t)v),
+                 __builtin_bit_cast(float, (uint32_t)(v >> 32))};
+}
+
+// Called by every thread of the workgroup after its store_through2 writes; true, in all of
+// them, for the workgroup that is the n-th to arrive at counter c, which also returns the
+// counter to zero. No workgroup waits for another.
+__device__ __forceinline__ bool arrive_last(uint32_t *c, uint32_t n, uint32_t *flag)
+{
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's stores are complete
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const uint32_t old =
+            __hip_atomic_fetch_add(c, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const uint32_t last = old + 1 == n ? 1u : 0u;
+        if (last)
+            __hip_atomic_store(c, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        *flag = last;
+    }
+    __syncthreads();
+    const bool last = *flag != 0;
+    asm volatile("" ::: "memory");
+    return last;
+}
+
 // Grid remap so that consecutive logical workgroups run on the same XCD: the hardware deals
 // workgroup ids round-robin over the 8 XCDs, so id -> (id % 8) * (n / 8) + id / 8 hands each
 // XCD one contiguous slice of the logical order (and so of K/V heads, which share its L2).

@@ -36,6 +36,20 @@ hipError_t launch_prefill16(const AttnArgs &a, const PrefillGrid &g, hipStream_t
                             const PagedKV *paged = nullptr, const int32_t *q_lens = nullptr);
 // the paged prefill keeps a sequence's page numbers in LDS: at most this many per sequence
 constexpr int kPrefillMaxPages = 4096;
+// Balanced causal prefill (fa_prefill_split, contiguous f16/bf16 caches): units holding more
+// than `cap` tiles run their tiles past the cap in a tail workgroup, and the two parts are
+// merged through a caller workspace: kSplitCounterBytes of arrival counters (zero between
+// calls), then the parts' partial rows. n_tail = 0: nothing to split (plain prefill).
+constexpr size_t kSplitCounterBytes = 4096;
+constexpr int kSplitCUs = 256;      // workgroups resident at once (one per CU)
+struct PrefillSplit {
+    int q_split, cap;
+    int64_t n_main, n_tail;
+    size_t workspace_bytes;
+};
+PrefillSplit prefill_split_plan(const AttnArgs &a);
+hipError_t launch_prefill_split(const AttnArgs &a, const PrefillSplit &sp, void *workspace,
+                                hipStream_t stream);
 
 // Decode: n_split key ranges per (b, KV head); rows = G * Sq query rows per KV head (<= 16).
 struct DecodeGrid {

@@ -30,6 +30,8 @@
 #include <cstdlib>
 #include <utility>
 
+#include <algorithm>
+
 #include "fa_kernels.h"
 #include "fa_tiles.h"
 
@@ -52,7 +54,16 @@ struct Prefill16Params {
     // paged caches only (see PagedKV); q_lens may be null (Sq queries in every sequence)
     const int32_t *block_table, *seq_lens, *q_lens;
     int max_pages, n_pages;
+    // balanced causal prefill (SPLIT instances): the units (b, kv head, head chunk, query block)
+    // of query block >= q_split hold more than `cap` tiles; the first n_main workgroups run every
+    // unit's tiles [0, cap), the n_tail after them the split units' tiles [cap, end), and the
+    // two parts of a unit are merged through the workspace
+    int q_split, cap, n_main, n_tail;
+    uint32_t *cnt;     // arrival counters, one per split unit, zero between calls
+    float *part;       // partial rows [split unit][part][wave][64 rows][kPartRow floats]
 };
+// a partial row: D unnormalised outputs, frame, sum, padding to 16 bytes
+constexpr int kPartRow = 132;
 
 // s_waitcnt immediate: wait until at most `vm` vector-memory ops are outstanding and all LDS
 // ops are done (expcnt left unconstrained).
@@ -346,9 +357,10 @@ struct Plans {
     static_assert(schedule_ok<NDT, NST, NM>(sc), "softmax units placed in time");
 };
 
-template <int D, int KT, int VT, bool PAGED>
+template <int D, int KT, int VT, bool PAGED, bool SPLIT = false>
 __global__ __launch_bounds__(kNT, 1) void prefill16_kernel(Prefill16Params p)
 {
+    static_assert(!SPLIT || (!PAGED && KT == VT && KT != KV_Q4_0), "split: contiguous 16-bit");
     static_assert(KT == VT || (KT != KV_BF16 && VT != KV_BF16), "bf16 caches are not mixed");
     constexpr bool BF = KT == KV_BF16;
     constexpr bool QK = KT == KV_Q4_0, QV = VT == KV_Q4_0;     // which tensors arrive raw
@@ -384,9 +396,21 @@ __global__ __launch_bounds__(kNT, 1) void prefill16_kernel(Prefill16Params p)
     const int half = lane >> 5, col = lane & 31;
 
     // ---- which (b, kv head, head chunk, query block) this workgroup owns -------------------
-    int rest = xcd_remap(blockIdx.x, gridDim.x);
-    const int qbl = rest % p.n_qblk;
-    rest /= p.n_qblk;
+    // (SPLIT: part 0 of every unit, then part 1 of the split units, heaviest first in each)
+    int rest, part = 0;
+    if constexpr (SPLIT) {
+        if ((int)blockIdx.x < p.n_main) {
+            rest = xcd_remap(blockIdx.x, p.n_main);
+        } else {
+            part = 1;
+            rest = xcd_remap(blockIdx.x - p.n_main, p.n_tail);
+        }
+    } else {
+        rest = xcd_remap(blockIdx.x, gridDim.x);
+    }
+    const int nqb = part ? p.n_qblk - p.q_split : p.n_qblk;   // query blocks of this set
+    const int qbl = rest % nqb;
+    rest /= nqb;
     const int hc = rest % p.n_hchunk;
     rest /= p.n_hchunk;
     const int kvh = rest % a.Hkv;
@@ -417,7 +441,18 @@ __global__ __launch_bounds__(kNT, 1) void prefill16_kernel(Prefill16Params p)
     if (a.causal)
         kend = min((int64_t)sk, (int64_t)qlast_wg + off + 1);
     kend = max(kend, (int64_t)0);
-    const int nb = (int)((kend + kBN - 1) / kBN);
+    // this workgroup's tiles: [t0, t0 + nb) of the unit's
+    const int nb_unit = (int)((kend + kBN - 1) / kBN);
+    int t0 = 0, nb = nb_unit;
+    const bool split_unit = SPLIT && qblk >= p.q_split;
+    if (split_unit) {
+        if (part == 0) {
+            nb = min(nb_unit, p.cap);
+        } else {
+            t0 = p.cap;
+            nb = max(nb_unit - p.cap, 0);
+        }
+    }
 
     // per block: this lane's row, its last visible key, and the block's most limited row's
     int qi[2];
@@ -497,13 +532,13 @@ __global__ __launch_bounds__(kNT, 1) void prefill16_kernel(Prefill16Params p)
         if constexpr (PAGED)
             return __builtin_amdgcn_readfirstlane(ptab[tl]);
         else
-            return tl;
+            return t0 + tl;
     };
     // Transfer i of tile tl (at slot sl) of K (is_v false) or V into a stage; rows past the end
     // of the sequence repeat its last key.
     auto dma_one = [&](bool is_v, int stage, int tl, int sl, int i) INL {
         tl = min(tl, nb - 1);
-        const int k0 = tl * kBN;
+        const int k0 = (t0 + tl) * kBN;
         const uint8_t *gt = (is_v ? vg : kg) + (int64_t)sl * kBN * grow;
         const uint32_t lastg = (uint32_t)min(kBN - 1, sk - 1 - k0) * grow;
         dma16(gt, min(rowg[i], lastg) + (is_v ? vc[i] : kc[i]),
@@ -532,7 +567,7 @@ __global__ __launch_bounds__(kNT, 1) void prefill16_kernel(Prefill16Params p)
     auto dma_raw = [&](bool is_v, int tl, int ts, int x) INL {
         const uint8_t *stg = is_v ? rawv(tl) : rawk(tl);
         tl = min(tl, nb - 1);
-        const int64_t k0 = (int64_t)tl * kBN;
+        const int64_t k0 = (int64_t)(t0 + tl) * kBN;
         const int sl = 64 * x + lane;
         const int last = (int)min((int64_t)kBN - 1, (int64_t)sk - 1 - k0);
         const uint32_t row = (uint32_t)min(sl / QR::CPR, last);
@@ -660,7 +695,7 @@ __global__ __launch_bounds__(kNT, 1) void prefill16_kernel(Prefill16Params p)
     bool need[2];
     float pv2[2][16][2];                           // P values between an E unit and its C unit
     auto mask = [&](int j, f32x16 *s, int n) INL {
-        const int k0 = n * kBN;
+        const int k0 = (t0 + n) * kBN;
         if ((int64_t)k0 + kBN - 1 > klim_min[j]) {
             const int lim = (int)max(min(klim[j] - k0, (int64_t)kBN), (int64_t)-1) - 8 * half;
 #pragma unroll
@@ -936,6 +971,81 @@ __global__ __launch_bounds__(kNT, 1) void prefill16_kernel(Prefill16Params p)
         pv_all(vstage(nb - 1));
 
     // ---- epilogue ----------------------------------------------------------------------------
+    if constexpr (SPLIT) {
+        if (split_unit) {
+            // This part's rows (unnormalised O, frame, sum) go to the workspace; the later of
+            // the unit's two parts merges them: F = max f, O = sum 2^(f - F) O_f / sum 2^(f - F)
+            // l_f. Rows pass through LDS (the tile rings, free once every wave is past its
+            // last tile) so that the workspace is written and read in contiguous runs, one
+            // 32-row block of a wave (32 x kPartRow floats) at a time.
+            static_assert(LDSB >= kNW * 32 * kPartRow * 4, "staging fits the tile rings");
+            constexpr int RUN = 32 * kPartRow;              // floats of one wave's block
+            const int64_t su = (((int64_t)b * a.Hkv + kvh) * p.n_hchunk + hc) *
+                                   (p.n_qblk - p.q_split) + (qblk - p.q_split);
+            float *mine = p.part + ((su * 2 + part) * kNW + wave) * (int64_t)(2 * RUN);
+            const float *other = p.part + ((su * 2 + (1 - part)) * kNW + wave) * (int64_t)(2 * RUN);
+            float *stg = (float *)lds + wave * RUN;
+            float *row = stg + col * kPartRow;
+            float ltot[2];
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                ltot[j] = pair_sum(lsum[j]);
+                __syncthreads();
+#pragma unroll
+                for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+                    for (int ii = 0; ii < 4; ++ii)
+                        *(f32x4 *)(row + 32 * dt + 8 * ii + 4 * half) =
+                            f32x4{acc[j][dt][4 * ii + 0], acc[j][dt][4 * ii + 1],
+                                  acc[j][dt][4 * ii + 2], acc[j][dt][4 * ii + 3]};
+                if (half == 0)
+                    *(f32x2 *)(row + D) = f32x2{frame[j], ltot[j]};
+                __syncthreads();
+#pragma unroll
+                for (int e = 2 * lane; e < RUN; e += 128)
+                    store_through2(mine + j * RUN + e, stg[e], stg[e + 1]);
+            }
+            __shared__ uint32_t arrived;
+            if (!arrive_last(p.cnt + su, 2u, &arrived))
+                return;
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                f32x2 in[(RUN + 127) / 128];
+#pragma unroll
+                for (int u = 0; u < (RUN + 127) / 128; ++u)
+                    in[u] = load_through2(other + j * RUN + min(2 * lane + 128 * u, RUN - 2));
+                __syncthreads();
+#pragma unroll
+                for (int u = 0; u < (RUN + 127) / 128; ++u)
+                    if (2 * lane + 128 * u < RUN)
+                        *(f32x2 *)(stg + 2 * lane + 128 * u) = in[u];
+                __syncthreads();
+                const f32x2 fl = *(const f32x2 *)(row + D);
+                const float F = fmaxf(frame[j], fl[0]);
+                const float wm = F == -INFINITY ? 0.0f : exp2_fast(frame[j] - F);
+                const float wo = F == -INFINITY ? 0.0f : exp2_fast(fl[0] - F);
+                const float L = wm * ltot[j] + wo * fl[1];
+                if (!wave_on || qi[j] >= sq)
+                    continue;
+                const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+                uint16_t *op = (uint16_t *)a.o + (((int64_t)b * a.Sq + qi[j]) * a.Hq + h) * D;
+#pragma unroll
+                for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+                    for (int ii = 0; ii < 4; ++ii) {
+                        const f32x4 x = *(const f32x4 *)(row + 32 * dt + 8 * ii + 4 * half);
+                        const f32x16 &c = acc[j][dt];
+                        u32x2 w;
+                        w[0] = pack2<BF>((wm * c[4 * ii + 0] + wo * x[0]) * inv,
+                                         (wm * c[4 * ii + 1] + wo * x[1]) * inv);
+                        w[1] = pack2<BF>((wm * c[4 * ii + 2] + wo * x[2]) * inv,
+                                         (wm * c[4 * ii + 3] + wo * x[3]) * inv);
+                        *(u32x2 *)(op + 32 * dt + 8 * ii + 4 * half) = w;
+                    }
+            }
+            return;
+        }
+    }
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
         const float ltot = pair_sum(lsum[j]);
@@ -958,6 +1068,13 @@ __global__ __launch_bounds__(kNT, 1) void prefill16_kernel(Prefill16Params p)
 template <int D, int KT, int VT>
 hipError_t launch16(const Prefill16Params &p, int64_t n_wg, hipStream_t stream)
 {
+    if constexpr (KT == VT && KT != KV_Q4_0) {
+        if (p.cnt) {
+            hipLaunchKernelGGL((prefill16_kernel<D, KT, VT, false, true>),
+                               dim3((unsigned)(p.n_main + p.n_tail)), dim3(kNT), 0, stream, p);
+            return hipGetLastError();
+        }
+    }
     if (p.block_table)
         hipLaunchKernelGGL((prefill16_kernel<D, KT, VT, true>), dim3((unsigned)n_wg), dim3(kNT),
                            0, stream, p);
@@ -986,6 +1103,48 @@ hipError_t launch16_kv(const Prefill16Params &p, int64_t n_wg, hipStream_t strea
 
 }  // namespace
 
+// Balanced causal split: the units' tile counts grow with the query block; the cap is the
+// average per unit (or per CU when there are fewer units than CUs) plus kSplitBias tiles,
+// and every unit above it gives its tiles past the cap to a tail workgroup. A tail pays a
+// workgroup's start (Q and its first tiles from memory) and the merge before and after its
+// own tiles, about 6-8 tiles' time measured on the box, and tails reach the CUs that free
+// first only in the dispatcher's order; a bias of 6 tiles timed best among 0, 3, 6 and 9.
+constexpr int kSplitBias = 6;
+PrefillSplit prefill_split_plan(const AttnArgs &a)
+{
+    PrefillSplit sp{};
+    const int kv = a.kv;
+    if (!a.causal || (kv != KV_F16 && kv != KV_BF16) || (int64_t)a.B * a.Sq == 0)
+        return sp;
+    const PrefillGrid g = prefill16_grid(a);
+    const int bmq = kQW * g.qsub;
+    auto tiles = [&](int qblk) -> int64_t {
+        const int64_t qlast = std::min((int64_t)qblk * bmq + bmq, (int64_t)a.Sq) - 1;
+        int64_t kend = std::min((int64_t)a.Sk, qlast + a.offset + 1);
+        kend = kend < 0 ? 0 : kend;
+        return (kend + kBN - 1) / kBN;
+    };
+    int64_t total = 0;
+    for (int q = 0; q < g.n_qblk; ++q)
+        total += tiles(q);
+    const int64_t per = (int64_t)g.n_hchunk * a.Hkv * a.B;       // units per query block
+    const int64_t units = (int64_t)g.n_qblk * per;
+    const int64_t slots = units > kSplitCUs ? units : kSplitCUs;
+    const int64_t cap = (total * per + slots - 1) / slots + kSplitBias;
+    int q_split = g.n_qblk;
+    while (q_split > 0 && tiles(q_split - 1) > cap)              // tiles grow with the block
+        --q_split;
+    const int64_t n_split = (int64_t)(g.n_qblk - q_split) * per;
+    if (n_split == 0 || n_split * sizeof(uint32_t) > kSplitCounterBytes || cap < 1)
+        return sp;
+    sp.q_split = q_split;
+    sp.cap = (int)cap;
+    sp.n_main = units;
+    sp.n_tail = n_split;
+    sp.workspace_bytes = kSplitCounterBytes + (size_t)n_split * 2 * kNW * kQW * kPartRow * 4;
+    return sp;
+}
+
 PrefillGrid prefill16_grid(const AttnArgs &a)
 {
     PrefillGrid g;
@@ -1006,6 +1165,24 @@ hipError_t launch_prefill(const AttnArgs &a, hipStream_t stream, const PagedKV *
 {
     const PrefillGrid g = prefill16_grid(a);
     return g.n_wg == 0 ? hipSuccess : launch_prefill16(a, g, stream, paged, q_lens);
+}
+
+hipError_t launch_prefill_split(const AttnArgs &a, const PrefillSplit &sp, void *workspace,
+                                hipStream_t stream)
+{
+    const PrefillGrid g = prefill16_grid(a);
+    if (g.n_wg == 0)
+        return hipSuccess;
+    if (sp.n_tail == 0)
+        return launch_prefill16(a, g, stream);
+    Prefill16Params p{a, g.hpw, g.qsub, g.n_qblk, g.n_hchunk, nullptr, nullptr, nullptr, 0, 0};
+    p.q_split = sp.q_split;
+    p.cap = sp.cap;
+    p.n_main = (int)sp.n_main;
+    p.n_tail = (int)sp.n_tail;
+    p.cnt = (uint32_t *)workspace;
+    p.part = (float *)((uint8_t *)workspace + kSplitCounterBytes);
+    return a.D == 128 ? launch16_kv<128>(p, g.n_wg, stream) : launch16_kv<64>(p, g.n_wg, stream);
 }
 
 hipError_t launch_prefill16(const AttnArgs &a, const PrefillGrid &g, hipStream_t stream,

@@ -21,7 +21,8 @@ One step = one pass of the whole path over resident inputs:
   * the decode workload's shape with an f16 cache (537 MB; the 16-bit split kernel);
   * the rest of the chunked-prefill configuration: 2048 queries at the end of 2048 and 8192
     keys (f16 and bf16), bf16 at 16384 keys, and the score-ramp variant at 16384 keys (f16 and
-    bf16), under `prefill_sweep` (reported).
+    bf16), and the balanced causal prefill (fa_prefill_split) at 2048, 8192 and 16384 keys,
+    under `prefill_sweep` (reported).
 Before each call a 1 GiB buffer is read so that neither call finds its inputs in the 256 MB
 last-level cache (the decode working set, 151 MB, would otherwise stay resident). The flush
 reads rather than writes: a written flush leaves up to 256 MB of dirty lines in that cache,
@@ -63,6 +64,8 @@ CLOCK_WARMUP_S = 0.25
 # the chunked-prefill configuration's other key counts, dtypes and the score ramp
 SWEEP = ["prefill_2k_f16", "prefill_8k_f16", "prefill_2k_bf16", "prefill_8k_bf16",
          "prefill_16k_bf16", "prefill_16k_f16_ramp", "prefill_16k_bf16_ramp"]
+# the balanced causal prefill (fa_prefill_split) beside fa_prefill at these shapes
+SWEEP_SPLIT = ["prefill_16k_f16", "prefill_2k_f16", "prefill_8k_f16"]
 
 
 def source_hash() -> str:
@@ -317,6 +320,16 @@ def main():
         sq_ = to_dev(x.q, w.q_dtype)
         sweep.append((w, sq_, to_dev(x.k, w.kv), to_dev(x.v, w.kv), torch.empty_like(sq_)))
         del x
+    split_legs = []
+    if not args.no_sweep:
+        have = {w.name: (w, q_, k_, v_) for w, q_, k_, v_, _o in sweep}
+        have[wp.name] = (wp, pq, pk, pv)
+        for name in SWEEP_SPLIT:
+            w, q_, k_, v_ = have[name]
+            nb_ = fa.prefill_workspace_bytes(q_, k_, v_, offset=w.causal_offset)
+            # zero-filled once: every call leaves its arrival counters at zero again
+            ws_ = torch.zeros(max(16, nb_), dtype=torch.uint8, device=dev)
+            split_legs.append((w, q_, k_, v_, torch.empty_like(q_), ws_))
     # float32, so sum() is one reduction kernel that only reads (an int32 sum would first
     # write an int64 copy)
     flush = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
@@ -384,8 +397,15 @@ def main():
 
     calls = [prefill, decode, prefill_q4, prefill_q4_unfused, quantize, decode_paged,
              prefill_paged, prefill_mixed, decode_mixed, prefill_d64, check_d64, decode_f16]
+    def split_call(w, q_, k_, v_, o_, ws_):
+        def call():
+            fa.prefill_split(q_, k_, v_, causal=True, offset=w.causal_offset, scale=w.scale,
+                             out=o_, workspace=ws_, stream=stream)
+        return call
+
     n_fixed = len(calls)
     calls += [sweep_call(*c) for c in sweep]
+    calls += [split_call(*c) for c in split_legs]
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * len(calls))]
           for _ in range(args.steps)]
 
@@ -436,6 +456,16 @@ def main():
         prefill_sweep[w.name] = {
             "shape": f"B={w.B} Sq={w.Sq} Sk={w.Sk} Hq={w.Hq} Hkv={w.Hkv} D={w.D} {w.kv}"
                      + (f", score ramp +{w.ramp} per key" if w.ramp else ""),
+            "tflops": round(tf, 3), "ms_mean": round(float(ms.mean()), 5),
+            "ms_median": round(float(np.median(ms)), 5),
+            "frac_of_mfma_peak": round(tf / PEAK_MFMA_F16_TFLOPS, 4)}
+    for j, (w, *_rest) in enumerate(split_legs):
+        c = n_fixed + len(sweep) + j
+        ms = np.array([e[2 * c].elapsed_time(e[2 * c + 1]) for e in ev])
+        tf = W.attention_flops(w) / (float(ms.mean()) * 1e-3) / 1e12
+        prefill_sweep[w.name + "_split"] = {
+            "shape": f"B={w.B} Sq={w.Sq} Sk={w.Sk} Hq={w.Hq} Hkv={w.Hkv} D={w.D} {w.kv}, "
+                     f"fa_prefill_split (balanced causal prefill)",
             "tflops": round(tf, 3), "ms_mean": round(float(ms.mean()), 5),
             "ms_median": round(float(np.median(ms)), 5),
             "frac_of_mfma_peak": round(tf / PEAK_MFMA_F16_TFLOPS, 4)}

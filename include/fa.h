@@ -65,7 +65,7 @@ enum fa_status {
     FA_ERR_SHAPE = -2,        /* negative size, Hq % Hkv != 0, or an index that overflows */
     FA_ERR_DTYPE = -3,        /* kv_dtype (x_dtype) not one of enum fa_kv_dtype (fa_src_dtype) */
     FA_ERR_UNSUPPORTED = -4,  /* valid but not built: D not in {64, 128}; decode rows > 16 */
-    FA_ERR_WORKSPACE = -5,    /* decode workspace missing or smaller than required */
+    FA_ERR_WORKSPACE = -5,    /* workspace missing or smaller than required */
     FA_ERR_ALIGN = -6,        /* Q/O/K/V not 16-byte aligned (a q4_0 K or V: 4-byte aligned) */
     FA_ERR_HIP = -7,          /* the HIP runtime reported an error at launch */
     FA_ERR_VALUE = -8,        /* scale not finite and > 0 */
@@ -87,6 +87,34 @@ int fa_prefill(const void *q, const void *k, const void *v, void *o,
                int B, int Hq, int Hkv, int Sq, int Sk, int D,
                int causal, int64_t causal_offset, float scale, int kv_dtype,
                fa_stream_t stream);
+
+/*
+ * Causal prefill with the work balanced across workgroups. In a causal chunk the later query
+ * blocks see more keys, so the workgroups that own them hold more 64-key tiles and the call
+ * waits for them (at 2048 queries against 2048 keys the tiles per workgroup run from 1 to
+ * 32). fa_prefill_split gives every (b, KV head, 64-row query block) unit that holds more
+ * tiles than the average (over units, or over the 256 CUs when units are fewer) a second
+ * workgroup for its tiles past the average; the second workgroups run after the first ones,
+ * and the later of a unit's two parts to finish merges them (log-sum-exp of the two partial
+ * softmax states) and writes the unit's rows. No workgroup waits for another.
+ * Arguments as fa_prefill, plus the caller-owned workspace:
+ *   workspace   >= fa_prefill_workspace_bytes(...) bytes, 16-byte aligned. Its first 4096
+ *               bytes are arrival counters that must be zero before the first call that uses
+ *               the workspace (allocate it zero-filled, or clear it once); every call returns
+ *               them to zero when it completes, so the workspace can be reused for any later
+ *               call without clearing. The rest holds the split units' partial rows. Non-zero
+ *               counter bytes give wrong output rows, never an access outside the workspace.
+ *               Calls that share a workspace must be ordered on one stream.
+ * Only contiguous f16 and bf16 caches split; for other cache types, non-causal calls, or
+ * shapes with nothing to split (fa_prefill_workspace_bytes returns 0) the call is fa_prefill
+ * and the workspace may be NULL. Errors as fa_prefill, plus FA_ERR_WORKSPACE.
+ */
+size_t fa_prefill_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Sk, int D, int causal,
+                                  int64_t causal_offset, int kv_dtype);
+int fa_prefill_split(const void *q, const void *k, const void *v, void *o,
+                     int B, int Hq, int Hkv, int Sq, int Sk, int D,
+                     int causal, int64_t causal_offset, float scale, int kv_dtype,
+                     void *workspace, size_t workspace_bytes, fa_stream_t stream);
 
 /*
  * Bytes of workspace fa_decode needs for these sizes (0 when nothing is needed).

@@ -98,6 +98,52 @@ def test_prefill_rejects(kw, code):
     assert prefill(**kw) == code
 
 
+def prefill_split(**kw):
+    args = dict(q=P, k=P, v=P, o=P, B=1, Hq=32, Hkv=8, Sq=2048, Sk=16384, D=128, causal=1,
+                causal_offset=14336, scale=0.088, kv_dtype=0, workspace=P, workspace_bytes=0,
+                stream=None)
+    args.update(kw)
+    return fa.fa_prefill_split(*args.values())
+
+
+def test_prefill_workspace_bytes():
+    # 2048 queries at the end of 16384 keys, GQA 32/8: query block q of 64 rows holds 225 + q
+    # tiles, 240.5 on average over the 256 units; with the cap at 241 + 6 the 9 blocks above
+    # 247 (q = 23..31) of each of the 8 KV heads split: 72 units, 2 parts x 4 waves x 64 rows
+    # x 132 floats each, after 4096 bytes of counters
+    n = fa.fa_prefill_workspace_bytes(1, 32, 8, 2048, 16384, 128, 1, 14336, 0)
+    assert n == 4096 + 72 * 2 * 4 * 64 * 132 * 4
+    assert fa.fa_prefill_workspace_bytes(1, 32, 8, 2048, 16384, 128, 1, 14336, 1) == n   # bf16
+    # nothing splits: q4_0 or mixed caches, non-causal, one small query block, empty calls
+    assert fa.fa_prefill_workspace_bytes(1, 32, 8, 2048, 16384, 128, 1, 14336, 2) == 0
+    assert fa.fa_prefill_workspace_bytes(1, 32, 8, 2048, 16384, 128, 1, 14336, 3) == 0
+    assert fa.fa_prefill_workspace_bytes(1, 32, 8, 2048, 16384, 128, 0, 0, 0) == 0
+    assert fa.fa_prefill_workspace_bytes(1, 2, 2, 128, 128, 64, 1, 0, 0) == 0
+    assert fa.fa_prefill_workspace_bytes(0, 32, 8, 2048, 16384, 128, 1, 14336, 0) == 0
+    # invalid sizes give 0 too
+    assert fa.fa_prefill_workspace_bytes(1, 30, 8, 2048, 16384, 128, 1, 14336, 0) == 0
+    assert fa.fa_prefill_workspace_bytes(1, 32, 8, 2048, 16384, 96, 1, 14336, 0) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(workspace=None, workspace_bytes=1 << 30), fa.FA_ERR_WORKSPACE),
+    (dict(workspace_bytes=4096), fa.FA_ERR_WORKSPACE),
+    (dict(workspace=P + 8, workspace_bytes=1 << 30), fa.FA_ERR_ALIGN),
+    (dict(kv_dtype=9), fa.FA_ERR_DTYPE),
+    (dict(scale=0.0), fa.FA_ERR_VALUE),
+    (dict(q=None), fa.FA_ERR_NULL),
+    (dict(D=80), fa.FA_ERR_UNSUPPORTED),
+])
+def test_prefill_split_rejects(kw, code):
+    assert prefill_split(**kw) == code
+
+
+def test_prefill_split_short_workspace_refused():
+    n = fa.fa_prefill_workspace_bytes(1, 32, 8, 2048, 16384, 128, 1, 14336, 0)
+    assert prefill_split(workspace_bytes=n - 1) == fa.FA_ERR_WORKSPACE
+    assert prefill_split(B=0, q=None, o=None, workspace=None) == fa.FA_OK   # empty: no-op
+
+
 def test_prefill_empty_is_a_no_op():
     # nothing to compute: accepted without touching the device, even with NULL data
     assert prefill(B=0, q=None, o=None, k=None, v=None) == fa.FA_OK

@@ -8,8 +8,8 @@ import torch
 import attention_causal_gqa_attn_amd as fa
 import oracle
 import workloads as W
-from gpu_cases import (TOL, compare, gpu_decode, gpu_prefill, oracle_out, sample_rows, say,
-                       to_dev)
+from gpu_cases import (TOL, compare, device_inputs, gpu_decode, gpu_prefill, oracle_out,
+                       sample_rows, say, to_dev, to_host)
 
 pytestmark = pytest.mark.gpu
 
@@ -600,3 +600,105 @@ def test_prefill_paged_full_page_table():
                                scale=D ** -0.5)
         err = float(np.max(np.abs(got[b] - ref[0])))
         assert err <= TOL["f16"], (b, n, err)
+
+# ---------------------------------------------------------------------------------------------
+# balanced causal prefill (fa_prefill_split): units above the average tile count run their
+# later tiles in a second workgroup, merged by whichever of the two finishes last
+# ---------------------------------------------------------------------------------------------
+
+def gpu_prefill_split(w, x, workspace=None):
+    q, k, v = device_inputs(w, x)
+    o = fa.prefill_split(q, k, v, causal=w.causal, offset=w.causal_offset, scale=w.scale,
+                         workspace=workspace)
+    torch.cuda.synchronize()
+    return to_host(o)
+
+
+SPLIT_SMALL = [
+    W.WORKLOADS["p2check"],
+    # GQA 4 with a ragged query tail, a chunk at the end of longer keys, two sequences
+    wl("split_gqa_ragged", 2, 16, 4, 300, 1000, 128, "f16", True, 700, seed=91),
+    wl("split_bf16_d64", 1, 8, 2, 640, 640, 64, "bf16", True, 0, seed=92),
+    # one KV head: 24 query blocks on 256 CUs, the cap is the per-CU average (tiles / 256)
+    wl("split_one_head", 1, 4, 1, 1500, 1500, 128, "f16", True, 0, seed=93),
+    # queries before the keys: early rows see nothing
+    wl("split_negative_offset", 1, 8, 2, 1200, 1000, 128, "f16", True, -100, seed=94),
+    # GQA 3 (head chunks of 3 of 4 waves) and G = 8 (two head chunks)
+    wl("split_gqa3", 1, 6, 2, 700, 900, 64, "f16", True, 200, seed=95),
+    wl("split_gqa8", 1, 16, 2, 500, 500, 128, "bf16", True, 0, seed=96),
+]
+
+
+@pytest.mark.parametrize("w", SPLIT_SMALL, ids=[w.name for w in SPLIT_SMALL])
+def test_prefill_split_matches_oracle(w):
+    say(f"prefill_split {w}")
+    # these shapes do split: the tail workgroups and the merge run
+    assert fa.fa_prefill_workspace_bytes(w.B, w.Hq, w.Hkv, w.Sq, w.Sk, w.D, int(w.causal),
+                                         w.causal_offset, w.kv_code) > 4096
+    x = W.generate(w)
+    compare(w, gpu_prefill_split(w, x).reshape(-1, w.D), oracle_out(w, x).reshape(-1, w.D),
+            w.name)
+
+
+def test_prefill_split_nothing_to_split():
+    """Where no unit holds more than the cap (a single small query block) the call is
+    fa_prefill, bit for bit, and needs no workspace."""
+    w = W.WORKLOADS["tiny"]
+    assert fa.fa_prefill_workspace_bytes(w.B, w.Hq, w.Hkv, w.Sq, w.Sk, w.D, 1, w.causal_offset,
+                                         w.kv_code) == 0
+    x = W.generate(w)
+    q, k, v = device_inputs(w, x)
+    o = torch.empty_like(q)
+    rc = fa.fa_prefill_split(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), w.B, w.Hq,
+                             w.Hkv, w.Sq, w.Sk, w.D, 1, w.causal_offset, w.scale, w.kv_code,
+                             None, 0, torch.cuda.current_stream().cuda_stream)
+    assert rc == fa.FA_OK
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host(o), gpu_prefill(w, x))
+
+
+@pytest.mark.parametrize("name", ["prefill_2k_f16", "prefill_16k_f16", "prefill_8k_bf16",
+                                  "prefill_16k_bf16_ramp"])
+def test_prefill_split_full_size_sampled(name):
+    """The benchmark's chunked-prefill shapes: sampled rows against the oracle, and the rows of
+    units that were not split bit-identical to fa_prefill."""
+    w = W.WORKLOADS[name]
+    say(f"prefill_split {w}")
+    x = W.generate(w)
+    got = gpu_prefill_split(w, x).reshape(w.B, w.Sq, w.Hq, w.D)
+    rows = sample_rows(w, 512, seed=3)
+    compare(w, got.reshape(-1, w.D)[rows], oracle_out(w, x, rows=rows), name)
+    plain = gpu_prefill(w, x).reshape(w.B, w.Sq, w.Hq, w.D)
+    n_first = 64 * 17   # query blocks 0-16 are below the split threshold at all four shapes
+    assert np.array_equal(got[:, :n_first], plain[:, :n_first])
+    assert float(np.max(np.abs(got - plain))) <= TOL[w.kv]
+
+
+def test_prefill_split_workspace_reused():
+    """One zero-filled workspace for calls of different sizes in turn: each matches the
+    oracle and leaves the 4096 counter bytes at zero; a call with nothing to split (non-causal)
+    takes no workspace."""
+    cases = [W.WORKLOADS["prefill_16k_f16"], W.WORKLOADS["p2check"],
+             wl("split_reuse", 2, 16, 4, 300, 1000, 128, "f16", True, 700, seed=97),
+             W.WORKLOADS["prefill_2k_bf16"]]
+    nbytes = max(fa.fa_prefill_workspace_bytes(w.B, w.Hq, w.Hkv, w.Sq, w.Sk, w.D, 1,
+                                               w.causal_offset, w.kv_code) for w in cases)
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    for w in cases:
+        say(f"prefill_split, shared workspace: {w}")
+        x = W.generate(w)
+        got = gpu_prefill_split(w, x, workspace=ws).reshape(-1, w.D)
+        rows = sample_rows(w, 256, seed=4)
+        compare(w, got[rows], oracle_out(w, x, rows=rows), w.name)
+        assert int(torch.count_nonzero(ws[:4096]).item()) == 0, f"{w.name}: counters not zero"
+    w = wl("split_noncausal", 1, 8, 2, 200, 300, 128, "f16", False, 0, seed=98)
+    assert fa.fa_prefill_workspace_bytes(w.B, w.Hq, w.Hkv, w.Sq, w.Sk, w.D, 0, 0, w.kv_code) == 0
+    x = W.generate(w)
+    q, k, v = device_inputs(w, x)
+    o = torch.empty_like(q)
+    rc = fa.fa_prefill_split(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), w.B, w.Hq,
+                             w.Hkv, w.Sq, w.Sk, w.D, 0, 0, w.scale, w.kv_code, None, 0,
+                             torch.cuda.current_stream().cuda_stream)
+    assert rc == fa.FA_OK
+    torch.cuda.synchronize()
+    compare(w, to_host(o).reshape(-1, w.D), oracle_out(w, x).reshape(-1, w.D), w.name)
