@@ -37,11 +37,12 @@ hipError_t launch_prefill16(const AttnArgs &a, const PrefillGrid &g, hipStream_t
 // the paged prefill keeps a sequence's page numbers in LDS: at most this many per sequence
 constexpr int kPrefillMaxPages = 4096;
 // Balanced causal prefill (fa_prefill_split, contiguous f16/bf16 caches): units holding more
-// than `cap` tiles run their tiles past the cap in a tail workgroup, and the two parts are
-// merged through a caller workspace: kSplitCounterBytes of arrival counters (zero between
-// calls), then the parts' partial rows. n_tail = 0: nothing to split (plain prefill).
+// than `cap` tiles leave their tiles past the cap to the workgroup of their mirror query block
+// (n - 1 - q), which runs them after its own unit; the two parts are merged through a caller
+// workspace: kSplitCounterBytes of arrival counters (zero between calls), then the parts'
+// partial rows. n_main: workgroups (one per unit); n_tail: split units, 0 when nothing splits
+// (plain prefill).
 constexpr size_t kSplitCounterBytes = 4096;
-constexpr int kSplitCUs = 256;      // workgroups resident at once (one per CU)
 struct PrefillSplit {
     int q_split, cap;
     int64_t n_main, n_tail;

@@ -55,9 +55,10 @@ struct Prefill16Params {
     const int32_t *block_table, *seq_lens, *q_lens;
     int max_pages, n_pages;
     // balanced causal prefill (SPLIT instances): the units (b, kv head, head chunk, query block)
-    // of query block >= q_split hold more than `cap` tiles; the first n_main workgroups run every
-    // unit's tiles [0, cap), the n_tail after them the split units' tiles [cap, end), and the
-    // two parts of a unit are merged through the workspace
+    // of query block >= q_split hold more than `cap` tiles and run only their tiles [0, cap);
+    // the workgroup of the mirror unit (query block n_qblk - 1 - q) runs the rest after its
+    // own unit, and the two parts of a unit are merged through the workspace. n_main: the
+    // workgroups (one per unit); n_tail: the split units
     int q_split, cap, n_main, n_tail;
     uint32_t *cnt;     // arrival counters, one per split unit, zero between calls
     float *part;       // partial rows [split unit][part][wave][64 rows][kPartRow floats]
@@ -396,27 +397,19 @@ __global__ __launch_bounds__(kNT, 1) void prefill16_kernel(Prefill16Params p)
     const int half = lane >> 5, col = lane & 31;
 
     // ---- which (b, kv head, head chunk, query block) this workgroup owns -------------------
-    // (SPLIT: part 0 of every unit, then part 1 of the split units, heaviest first in each)
-    int rest, part = 0;
-    if constexpr (SPLIT) {
-        if ((int)blockIdx.x < p.n_main) {
-            rest = xcd_remap(blockIdx.x, p.n_main);
-        } else {
-            part = 1;
-            rest = xcd_remap(blockIdx.x - p.n_main, p.n_tail);
-        }
-    } else {
-        rest = xcd_remap(blockIdx.x, gridDim.x);
-    }
-    const int nqb = part ? p.n_qblk - p.q_split : p.n_qblk;   // query blocks of this set
-    const int qbl = rest % nqb;
-    rest /= nqb;
+    int rest = xcd_remap(blockIdx.x, gridDim.x);
+    const int qbl = rest % p.n_qblk;
+    rest /= p.n_qblk;
     const int hc = rest % p.n_hchunk;
     rest /= p.n_hchunk;
     const int kvh = rest % a.Hkv;
     const int b = rest / a.Hkv;
-    const int qblk = a.causal ? p.n_qblk - 1 - qbl : qbl;    // heaviest blocks first
+    const int qblk0 = a.causal ? p.n_qblk - 1 - qbl : qbl;    // heaviest blocks first
+    __shared__ uint32_t arrived;                                // SPLIT: arrival flag
 
+    // One unit's tiles: all of them, or (SPLIT, a split unit) its first cap tiles (part 0) or
+    // the rest (part 1)
+    auto run = [&](const int qblk, const int part) INL {
     // this sequence's keys and queries, and the position of its first query
     int sk = a.Sk, sq = a.Sq;
     int64_t off = a.offset;
@@ -1005,7 +998,6 @@ __global__ __launch_bounds__(kNT, 1) void prefill16_kernel(Prefill16Params p)
                 for (int e = 2 * lane; e < RUN; e += 128)
                     store_through2(mine + j * RUN + e, stg[e], stg[e + 1]);
             }
-            __shared__ uint32_t arrived;
             if (!arrive_last(p.cnt + su, 2u, &arrived))
                 return;
 #pragma unroll
@@ -1063,6 +1055,18 @@ __global__ __launch_bounds__(kNT, 1) void prefill16_kernel(Prefill16Params p)
                 *(u32x2 *)(op + 32 * dt + 8 * ii + 4 * half) = w;
             }
     }
+    };
+
+    run(qblk0, 0);
+    if constexpr (SPLIT) {
+        // a light unit then runs the tiles past the cap of its mirror unit n - 1 - q, whose
+        // tile count rises as this one's falls
+        const int partner = p.n_qblk - 1 - qblk0;
+        if (qblk0 < p.q_split && partner >= p.q_split) {
+            __syncthreads();   // every wave is done with the LDS of the first unit
+            run(partner, 1);
+        }
+    }
 }
 
 template <int D, int KT, int VT>
@@ -1071,7 +1075,7 @@ hipError_t launch16(const Prefill16Params &p, int64_t n_wg, hipStream_t stream)
     if constexpr (KT == VT && KT != KV_Q4_0) {
         if (p.cnt) {
             hipLaunchKernelGGL((prefill16_kernel<D, KT, VT, false, true>),
-                               dim3((unsigned)(p.n_main + p.n_tail)), dim3(kNT), 0, stream, p);
+                               dim3((unsigned)p.n_main), dim3(kNT), 0, stream, p);
             return hipGetLastError();
         }
     }
@@ -1103,13 +1107,15 @@ hipError_t launch16_kv(const Prefill16Params &p, int64_t n_wg, hipStream_t strea
 
 }  // namespace
 
-// Balanced causal split: the units' tile counts grow with the query block; the cap is the
-// average per unit (or per CU when there are fewer units than CUs) plus kSplitBias tiles,
-// and every unit above it gives its tiles past the cap to a tail workgroup. A tail pays a
-// workgroup's start (Q and its first tiles from memory) and the merge before and after its
-// own tiles, about 6-8 tiles' time measured on the box, and tails reach the CUs that free
-// first only in the dispatcher's order; a bias of 6 tiles timed best among 0, 3, 6 and 9.
-constexpr int kSplitBias = 6;
+// Balanced causal split: the units' tile counts grow with the query block, linearly where
+// every row sees the keys up to its own position. Query blocks q and n - 1 - q together hold
+// about twice the average, so the heavier of the two (q >= q_split, q_split >= n / 2) runs
+// its first `cap` tiles and the lighter one runs the rest after its own, in the same
+// workgroup: cap = the average tiles per unit plus kSplitBias, which leaves the light
+// workgroup the time to restart (load the second unit's Q and first tiles) and merge. Timed
+// on the box at 2K, 8K and 16K keys, biases 0-6: 3 was best (4 close, 0 and 6 worst).
+constexpr int kSplitBias = 3;
+
 PrefillSplit prefill_split_plan(const AttnArgs &a)
 {
     PrefillSplit sp{};
@@ -1128,18 +1134,17 @@ PrefillSplit prefill_split_plan(const AttnArgs &a)
     for (int q = 0; q < g.n_qblk; ++q)
         total += tiles(q);
     const int64_t per = (int64_t)g.n_hchunk * a.Hkv * a.B;       // units per query block
-    const int64_t units = (int64_t)g.n_qblk * per;
-    const int64_t slots = units > kSplitCUs ? units : kSplitCUs;
-    const int64_t cap = (total * per + slots - 1) / slots + kSplitBias;
+    const int64_t cap = (total + g.n_qblk - 1) / g.n_qblk + kSplitBias;
     int q_split = g.n_qblk;
     while (q_split > 0 && tiles(q_split - 1) > cap)              // tiles grow with the block
         --q_split;
+    q_split = std::max(q_split, (g.n_qblk + 1) / 2);             // every split unit's mirror is light
     const int64_t n_split = (int64_t)(g.n_qblk - q_split) * per;
     if (n_split == 0 || n_split * sizeof(uint32_t) > kSplitCounterBytes || cap < 1)
         return sp;
     sp.q_split = q_split;
     sp.cap = (int)cap;
-    sp.n_main = units;
+    sp.n_main = (int64_t)g.n_qblk * per;
     sp.n_tail = n_split;
     sp.workspace_bytes = kSplitCounterBytes + (size_t)n_split * 2 * kNW * kQW * kPartRow * 4;
     return sp;

@@ -108,11 +108,11 @@ def prefill_split(**kw):
 
 def test_prefill_workspace_bytes():
     # 2048 queries at the end of 16384 keys, GQA 32/8: query block q of 64 rows holds 225 + q
-    # tiles, 240.5 on average over the 256 units; with the cap at 241 + 6 the 9 blocks above
-    # 247 (q = 23..31) of each of the 8 KV heads split: 72 units, 2 parts x 4 waves x 64 rows
-    # x 132 floats each, after 4096 bytes of counters
+    # tiles, 240.5 on average; with the cap at 241 + 3 the 12 blocks above 244 (q = 20..31) of
+    # each of the 8 KV heads split (their mirrors q = 0..11 run the rest): 96 units, 2 parts x
+    # 4 waves x 64 rows x 132 floats each, after 4096 bytes of counters
     n = fa.fa_prefill_workspace_bytes(1, 32, 8, 2048, 16384, 128, 1, 14336, 0)
-    assert n == 4096 + 72 * 2 * 4 * 64 * 132 * 4
+    assert n == 4096 + 96 * 2 * 4 * 64 * 132 * 4
     assert fa.fa_prefill_workspace_bytes(1, 32, 8, 2048, 16384, 128, 1, 14336, 1) == n   # bf16
     # nothing splits: q4_0 or mixed caches, non-causal, one small query block, empty calls
     assert fa.fa_prefill_workspace_bytes(1, 32, 8, 2048, 16384, 128, 1, 14336, 2) == 0

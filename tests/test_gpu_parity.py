@@ -615,9 +615,10 @@ def gpu_prefill_split(w, x, workspace=None):
 
 
 SPLIT_SMALL = [
-    W.WORKLOADS["p2check"],
+    # MHA at D = 64 (head chunks of 1 head x 4 query sub-blocks), two sequences
+    wl("split_mha_d64", 2, 8, 8, 1024, 1024, 64, "f16", True, 0, seed=90),
     # GQA 4 with a ragged query tail, a chunk at the end of longer keys, two sequences
-    wl("split_gqa_ragged", 2, 16, 4, 300, 1000, 128, "f16", True, 700, seed=91),
+    wl("split_gqa_ragged", 2, 16, 4, 900, 1600, 128, "f16", True, 700, seed=91),
     wl("split_bf16_d64", 1, 8, 2, 640, 640, 64, "bf16", True, 0, seed=92),
     # one KV head: 24 query blocks on 256 CUs, the cap is the per-CU average (tiles / 256)
     wl("split_one_head", 1, 4, 1, 1500, 1500, 128, "f16", True, 0, seed=93),
@@ -625,7 +626,7 @@ SPLIT_SMALL = [
     wl("split_negative_offset", 1, 8, 2, 1200, 1000, 128, "f16", True, -100, seed=94),
     # GQA 3 (head chunks of 3 of 4 waves) and G = 8 (two head chunks)
     wl("split_gqa3", 1, 6, 2, 700, 900, 64, "f16", True, 200, seed=95),
-    wl("split_gqa8", 1, 16, 2, 500, 500, 128, "bf16", True, 0, seed=96),
+    wl("split_gqa8", 1, 16, 2, 1000, 1000, 128, "bf16", True, 0, seed=96),
 ]
 
 
@@ -678,8 +679,9 @@ def test_prefill_split_workspace_reused():
     """One zero-filled workspace for calls of different sizes in turn: each matches the
     oracle and leaves the 4096 counter bytes at zero; a call with nothing to split (non-causal)
     takes no workspace."""
-    cases = [W.WORKLOADS["prefill_16k_f16"], W.WORKLOADS["p2check"],
-             wl("split_reuse", 2, 16, 4, 300, 1000, 128, "f16", True, 700, seed=97),
+    cases = [W.WORKLOADS["prefill_16k_f16"], wl("split_reuse_mha", 2, 8, 8, 1024, 1024, 64,
+                                                     "f16", True, 0, seed=99),
+             wl("split_reuse", 2, 16, 4, 900, 1600, 128, "f16", True, 700, seed=97),
              W.WORKLOADS["prefill_2k_bf16"]]
     nbytes = max(fa.fa_prefill_workspace_bytes(w.B, w.Hq, w.Hkv, w.Sq, w.Sk, w.D, 1,
                                                w.causal_offset, w.kv_code) for w in cases)
