@@ -120,6 +120,11 @@ def test_prefill_workspace_bytes():
     assert fa.fa_prefill_workspace_bytes(1, 32, 8, 2048, 16384, 128, 0, 0, 0) == 0
     assert fa.fa_prefill_workspace_bytes(1, 2, 2, 128, 128, 64, 1, 0, 0) == 0
     assert fa.fa_prefill_workspace_bytes(0, 32, 8, 2048, 16384, 128, 1, 14336, 0) == 0
+    # more split units than the 4096 counter bytes hold (64 sequences x 8 KV heads x 12
+    # blocks = 6144): no split, the call is fa_prefill
+    assert fa.fa_prefill_workspace_bytes(64, 32, 8, 2048, 16384, 128, 1, 14336, 0) == 0
+    assert fa.fa_prefill_workspace_bytes(10, 32, 8, 2048, 16384, 128, 1, 14336, 0) == \
+        4096 + 960 * 2 * 4 * 64 * 132 * 4
     # invalid sizes give 0 too
     assert fa.fa_prefill_workspace_bytes(1, 30, 8, 2048, 16384, 128, 1, 14336, 0) == 0
     assert fa.fa_prefill_workspace_bytes(1, 32, 8, 2048, 16384, 96, 1, 14336, 0) == 0
