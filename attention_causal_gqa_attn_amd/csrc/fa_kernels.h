@@ -36,8 +36,8 @@ hipError_t launch_prefill16(const AttnArgs &a, const PrefillGrid &g, hipStream_t
                             const PagedKV *paged = nullptr, const int32_t *q_lens = nullptr);
 // the paged prefill keeps a sequence's page numbers in LDS: at most this many per sequence
 constexpr int kPrefillMaxPages = 4096;
-// Balanced causal prefill (fa_prefill_split, contiguous f16/bf16 caches): units holding more
-// than `cap` tiles leave their tiles past the cap to the workgroup of their mirror query block
+// Balanced causal prefill (fa_prefill_split, contiguous caches; a q4_0 tensor at D = 128
+// only): units holding more than `cap` tiles leave their tiles past the cap to the workgroup of their mirror query block
 // (n - 1 - q), which runs them after its own unit; the two parts are merged through a caller
 // workspace: kSplitCounterBytes of arrival counters (zero between calls), then the parts'
 // partial rows. n_main: workgroups (one per unit); n_tail: split units, 0 when nothing splits

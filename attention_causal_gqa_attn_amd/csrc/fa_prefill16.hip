@@ -361,7 +361,7 @@ struct Plans {
 template <int D, int KT, int VT, bool PAGED, bool SPLIT = false>
 __global__ __launch_bounds__(kNT, 1) void prefill16_kernel(Prefill16Params p)
 {
-    static_assert(!SPLIT || (!PAGED && KT == VT && KT != KV_Q4_0), "split: contiguous 16-bit");
+    static_assert(!SPLIT || !PAGED, "split: contiguous caches");
     static_assert(KT == VT || (KT != KV_BF16 && VT != KV_BF16), "bf16 caches are not mixed");
     constexpr bool BF = KT == KV_BF16;
     constexpr bool QK = KT == KV_Q4_0, QV = VT == KV_Q4_0;     // which tensors arrive raw
@@ -1072,7 +1072,9 @@ __global__ __launch_bounds__(kNT, 1) void prefill16_kernel(Prefill16Params p)
 template <int D, int KT, int VT>
 hipError_t launch16(const Prefill16Params &p, int64_t n_wg, hipStream_t stream)
 {
-    if constexpr (KT == VT && KT != KV_Q4_0) {
+    // the split instances: 16-bit caches at both head dims; a q4_0 tensor at D = 128 only (at
+    // D = 64 its kernel's LDS is smaller than the split's staging)
+    if constexpr (D == 128 || (KT != KV_Q4_0 && VT != KV_Q4_0)) {
         if (p.cnt) {
             hipLaunchKernelGGL((prefill16_kernel<D, KT, VT, false, true>),
                                dim3((unsigned)p.n_main), dim3(kNT), 0, stream, p);
@@ -1120,7 +1122,8 @@ PrefillSplit prefill_split_plan(const AttnArgs &a)
 {
     PrefillSplit sp{};
     const int kv = a.kv;
-    if (!a.causal || (kv != KV_F16 && kv != KV_BF16) || (int64_t)a.B * a.Sq == 0)
+    const bool q4 = kv == KV_Q4_0 || kv == KV_F16_Q4_0 || kv == KV_Q4_0_F16;
+    if (!a.causal || (q4 && a.D != 128) || (int64_t)a.B * a.Sq == 0)
         return sp;
     const PrefillGrid g = prefill16_grid(a);
     const int bmq = kQW * g.qsub;

@@ -105,9 +105,10 @@ int fa_prefill(const void *q, const void *k, const void *v, void *o,
  *               call without clearing. The rest holds the split units' partial rows. Non-zero
  *               counter bytes give wrong output rows, never an access outside the workspace.
  *               Calls that share a workspace must be ordered on one stream.
- * Only contiguous f16 and bf16 caches split; for other cache types, non-causal calls, or
- * shapes with nothing to split (fa_prefill_workspace_bytes returns 0) the call is fa_prefill
- * and the workspace may be NULL. Errors as fa_prefill, plus FA_ERR_WORKSPACE.
+ * Contiguous caches split (a cache type with a q4_0 tensor at D = 128 only); for paged
+ * caches, non-causal calls, or shapes with nothing to split (fa_prefill_workspace_bytes
+ * returns 0) the call is fa_prefill and the workspace may be NULL. Errors as fa_prefill, plus
+ * FA_ERR_WORKSPACE.
  */
 size_t fa_prefill_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Sk, int D, int causal,
                                   int64_t causal_offset, int kv_dtype);

@@ -114,9 +114,12 @@ def test_prefill_workspace_bytes():
     n = fa.fa_prefill_workspace_bytes(1, 32, 8, 2048, 16384, 128, 1, 14336, 0)
     assert n == 4096 + 96 * 2 * 4 * 64 * 132 * 4
     assert fa.fa_prefill_workspace_bytes(1, 32, 8, 2048, 16384, 128, 1, 14336, 1) == n   # bf16
-    # nothing splits: q4_0 or mixed caches, non-causal, one small query block, empty calls
-    assert fa.fa_prefill_workspace_bytes(1, 32, 8, 2048, 16384, 128, 1, 14336, 2) == 0
-    assert fa.fa_prefill_workspace_bytes(1, 32, 8, 2048, 16384, 128, 1, 14336, 3) == 0
+    # q4_0 and mixed caches split at D = 128 (the same plan), not at D = 64
+    assert fa.fa_prefill_workspace_bytes(1, 32, 8, 2048, 16384, 128, 1, 14336, 2) == n
+    assert fa.fa_prefill_workspace_bytes(1, 32, 8, 2048, 16384, 128, 1, 14336, 3) == n
+    assert fa.fa_prefill_workspace_bytes(1, 32, 8, 2048, 16384, 64, 1, 14336, 2) == 0
+    assert fa.fa_prefill_workspace_bytes(1, 32, 8, 2048, 16384, 64, 1, 14336, 0) > 0
+    # nothing splits: non-causal, one small query block, empty calls
     assert fa.fa_prefill_workspace_bytes(1, 32, 8, 2048, 16384, 128, 0, 0, 0) == 0
     assert fa.fa_prefill_workspace_bytes(1, 2, 2, 128, 128, 64, 1, 0, 0) == 0
     assert fa.fa_prefill_workspace_bytes(0, 32, 8, 2048, 16384, 128, 1, 14336, 0) == 0

@@ -627,6 +627,8 @@ SPLIT_SMALL = [
     # GQA 3 (head chunks of 3 of 4 waves) and G = 8 (two head chunks)
     wl("split_gqa3", 1, 6, 2, 700, 900, 64, "f16", True, 200, seed=95),
     wl("split_gqa8", 1, 16, 2, 1000, 1000, 128, "bf16", True, 0, seed=96),
+    # q4_0 cache (D = 128): the raw rings and in-kernel dequantization over offset tiles
+    wl("split_q4_0", 1, 16, 4, 1100, 1700, 128, "q4_0", True, 600, seed=100),
 ]
 
 
@@ -658,8 +660,31 @@ def test_prefill_split_nothing_to_split():
     assert np.array_equal(to_host(o), gpu_prefill(w, x))
 
 
+SPLIT_MIXED = [
+    # (name, B, Hq, Hkv, Sq, Sk, D, K type, V type, offset, seed)
+    ("split_f16k_q4v", 1, 8, 2, 1000, 1000, 128, "f16", "q4_0", 0, 101),
+    ("split_q4k_f16v", 2, 8, 2, 900, 1200, 128, "q4_0", "f16", 300, 102),
+]
+
+
+@pytest.mark.parametrize("case", SPLIT_MIXED, ids=[c[0] for c in SPLIT_MIXED])
+def test_prefill_split_mixed_matches_oracle(case):
+    name, B, Hq, Hkv, Sq, Sk, D, kt, vt, offset, seed = case
+    say(f"prefill_split, mixed caches {case}")
+    w = wl(name, B, Hq, Hkv, Sq, Sk, D, "f16", True, offset, seed)
+    code = fa.FA_KV_F16_Q4_0 if kt == "f16" else fa.FA_KV_Q4_0_F16
+    assert fa.fa_prefill_workspace_bytes(B, Hq, Hkv, Sq, Sk, D, 1, offset, code) > 4096
+    q, k, v = _mixed(w, kt, vt)
+    got = fa.prefill_split(to_dev(q, "f16"), to_dev(k, kt), to_dev(v, vt), causal=True,
+                           offset=w.causal_offset, scale=w.scale)
+    torch.cuda.synchronize()
+    err = float(np.max(np.abs(got.float().cpu().numpy() - _mixed_oracle(w, q, k, v, kt, vt))))
+    say(f"  max|err| = {err:.3e}")
+    assert err <= TOL["q4_0"], (name, err)
+
+
 @pytest.mark.parametrize("name", ["prefill_2k_f16", "prefill_16k_f16", "prefill_8k_bf16",
-                                  "prefill_16k_bf16_ramp"])
+                                  "prefill_16k_bf16_ramp", "prefill_16k_q4_0"])
 def test_prefill_split_full_size_sampled(name):
     """The benchmark's chunked-prefill shapes: sampled rows against the oracle, and the rows of
     units that were not split bit-identical to fa_prefill."""
