@@ -21,8 +21,8 @@ One step = one pass of the whole path over resident inputs:
   * the decode workload's shape with an f16 cache (537 MB; the 16-bit split kernel);
   * the rest of the chunked-prefill configuration: 2048 queries at the end of 2048 and 8192
     keys (f16 and bf16), bf16 at 16384 keys, and the score-ramp variant at 16384 keys (f16 and
-    bf16), and the balanced causal prefill (fa_prefill_split) at 2048, 8192 and 16384 keys,
-    under `prefill_sweep` (reported).
+    bf16), and the balanced causal prefill (fa_prefill_split) at 2048, 8192 and 16384 keys
+    (f16) and at 16384 keys over the q4_0 cache, under `prefill_sweep` (reported).
 Before each call a 1 GiB buffer is read so that neither call finds its inputs in the 256 MB
 last-level cache (the decode working set, 151 MB, would otherwise stay resident). The flush
 reads rather than writes: a written flush leaves up to 256 MB of dirty lines in that cache,
@@ -65,7 +65,7 @@ CLOCK_WARMUP_S = 0.25
 SWEEP = ["prefill_2k_f16", "prefill_8k_f16", "prefill_2k_bf16", "prefill_8k_bf16",
          "prefill_16k_bf16", "prefill_16k_f16_ramp", "prefill_16k_bf16_ramp"]
 # the balanced causal prefill (fa_prefill_split) beside fa_prefill at these shapes
-SWEEP_SPLIT = ["prefill_16k_f16", "prefill_2k_f16", "prefill_8k_f16"]
+SWEEP_SPLIT = ["prefill_16k_f16", "prefill_2k_f16", "prefill_8k_f16", "prefill_16k_q4_0"]
 
 
 def source_hash() -> str:
@@ -324,6 +324,7 @@ def main():
     if not args.no_sweep:
         have = {w.name: (w, q_, k_, v_) for w, q_, k_, v_, _o in sweep}
         have[wp.name] = (wp, pq, pk, pv)
+        have[wq.name] = (wq, qq, qk, qv)
         for name in SWEEP_SPLIT:
             w, q_, k_, v_ = have[name]
             nb_ = fa.prefill_workspace_bytes(q_, k_, v_, offset=w.causal_offset)
