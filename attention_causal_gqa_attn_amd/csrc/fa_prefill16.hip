@@ -408,7 +408,8 @@ __global__ __launch_bounds__(kNT, 1) void prefill16_kernel(Prefill16Params p)
     __shared__ uint32_t arrived;                                // SPLIT: arrival flag
 
     // One unit's tiles: all of them, or (SPLIT, a split unit) its first cap tiles (part 0) or
-    // the rest (part 1)
+    // the rest (part 1). The body below, down to the end of the epilogue, keeps the kernel's
+    // indentation.
     auto run = [&](const int qblk, const int part) INL {
     // this sequence's keys and queries, and the position of its first query
     int sk = a.Sk, sq = a.Sq;
@@ -1055,7 +1056,7 @@ __global__ __launch_bounds__(kNT, 1) void prefill16_kernel(Prefill16Params p)
                 *(u32x2 *)(op + 32 * dt + 8 * ii + 4 * half) = w;
             }
     }
-    };
+    };  // run
 
     run(qblk0, 0);
     if constexpr (SPLIT) {
