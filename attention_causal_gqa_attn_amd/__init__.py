@@ -8,9 +8,11 @@ missing every call raises.
 
 Raw entry points with the C names (pointers and ints): fa_prefill, fa_prefill_split,
 fa_prefill_workspace_bytes, fa_decode, fa_decode_paged, fa_prefill_paged,
-fa_decode_workspace_bytes, fa_dequant_q4_0, fa_quantize_q4_0, fa_strerror, fa_version.
+fa_decode_workspace_bytes, fa_prefill_stats, fa_decode_stats, fa_dequant_q4_0,
+fa_quantize_q4_0, fa_strerror, fa_version.
 Tensor helpers: prefill, prefill_split, prefill_workspace_bytes, prefill_paged, decode,
-decode_paged, decode_workspace_bytes, dequant_q4_0, quantize_q4_0.
+decode_paged, decode_workspace_bytes, prefill_stats, decode_stats, dequant_q4_0,
+quantize_q4_0.
 """
 from __future__ import annotations
 
@@ -36,8 +38,8 @@ FA_ERR_HIP = -7
 FA_ERR_VALUE = -8
 
 EXPORTS = ("fa_prefill", "fa_prefill_split", "fa_prefill_workspace_bytes", "fa_decode",
-           "fa_decode_paged", "fa_prefill_paged", "fa_decode_workspace_bytes", "fa_dequant_q4_0",
-           "fa_quantize_q4_0", "fa_strerror", "fa_version")
+           "fa_decode_paged", "fa_prefill_paged", "fa_decode_workspace_bytes", "fa_prefill_stats",
+           "fa_decode_stats", "fa_dequant_q4_0", "fa_quantize_q4_0", "fa_strerror", "fa_version")
 PAGE_KEYS = 64
 
 
@@ -77,6 +79,10 @@ def load() -> ctypes.CDLL:
         lib.fa_prefill_paged.restype = i32
         lib.fa_decode_workspace_bytes.argtypes = [i32] * 6
         lib.fa_decode_workspace_bytes.restype = sz
+        lib.fa_prefill_stats.argtypes = attn + [vp, vp]
+        lib.fa_prefill_stats.restype = i32
+        lib.fa_decode_stats.argtypes = attn + [vp, sz, vp, vp]
+        lib.fa_decode_stats.restype = i32
         lib.fa_dequant_q4_0.argtypes = [vp, i64, vp, vp, vp]
         lib.fa_dequant_q4_0.restype = i32
         lib.fa_quantize_q4_0.argtypes = [vp, i32, vp, i64, i64, i32, i64, i64, vp]
@@ -116,6 +122,18 @@ def fa_decode(q, k, v, o, B, Hq, Hkv, Sq, Sk, D, causal, causal_offset, scale, k
 
 def fa_decode_workspace_bytes(B, Hq, Hkv, Sq, Sk, D) -> int:
     return load().fa_decode_workspace_bytes(B, Hq, Hkv, Sq, Sk, D)
+
+
+def fa_prefill_stats(q, k, v, o, B, Hq, Hkv, Sq, Sk, D, causal, causal_offset, scale, kv_dtype,
+                     counts, stream) -> int:
+    return load().fa_prefill_stats(q, k, v, o, B, Hq, Hkv, Sq, Sk, D, causal, causal_offset,
+                                   scale, kv_dtype, counts, stream)
+
+
+def fa_decode_stats(q, k, v, o, B, Hq, Hkv, Sq, Sk, D, causal, causal_offset, scale, kv_dtype,
+                    workspace, workspace_bytes, counts, stream) -> int:
+    return load().fa_decode_stats(q, k, v, o, B, Hq, Hkv, Sq, Sk, D, causal, causal_offset,
+                                  scale, kv_dtype, workspace, workspace_bytes, counts, stream)
 
 
 def fa_dequant_q4_0(blocks, n_blocks, out_f32, out_f16, stream) -> int:
@@ -198,6 +216,41 @@ def _stream(t, stream) -> int:
     return int(_torch().cuda.current_stream(t.device).cuda_stream)
 
 
+def _q_dtype(kv):
+    """Q and O element type of a cache code: bfloat16 for bf16 caches, float16 otherwise."""
+    torch = _torch()
+    return torch.bfloat16 if kv == FA_KV_BF16 else torch.float16
+
+
+def _check_q(q, kv):
+    if q.dtype != _q_dtype(kv):
+        raise ValueError(f"q is {q.dtype}; this cache type takes {_q_dtype(kv)} queries")
+
+
+def _check_device(q, **others):
+    """Every tensor must live on q's GPU: a host tensor's address or another device's would
+    reach the kernels as a wild pointer. Runs after the dtype and shape checks, so those are
+    testable with host tensors."""
+    if q.device.type != "cuda":
+        raise ValueError(f"q is on {q.device}; the kernels need GPU tensors")
+    for name, t in others.items():
+        if t is not None and t.device != q.device:
+            raise ValueError(f"{name} is on {t.device}, q on {q.device}")
+
+
+def _check_out(out, q):
+    if out is None:
+        return
+    if out.dtype != q.dtype or tuple(out.shape) != tuple(q.shape) or not out.is_contiguous():
+        raise ValueError(f"out must be a contiguous {q.dtype} tensor of q's shape "
+                         f"{tuple(q.shape)} (got {out.dtype} {tuple(out.shape)})")
+
+
+def _check_workspace(ws):
+    if ws is not None and not ws.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+
+
 def _sizes(q, k, v, kv):
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
         raise ValueError("q, k, v must be 4-d: [B, S, H, D] (q4_0: [B, S, H, D/32*18] bytes)")
@@ -205,6 +258,7 @@ def _sizes(q, k, v, kv):
         raise ValueError("q, k, v must be contiguous")
     if k.shape[:3] != v.shape[:3]:
         raise ValueError("k and v shapes differ")
+    _check_q(q, kv)
     B, Sq, Hq, D = q.shape
     Bk, Sk, Hkv, _ = k.shape
     if Bk != B:
@@ -225,6 +279,8 @@ def prefill(q, k, v, *, causal: bool = True, offset: Optional[int] = None,
     type (float16, bfloat16, or uint8 q4_0 blocks). offset defaults to Sk - Sq."""
     kv = _kv_code(k, v)
     B, Hq, Hkv, Sq, Sk, D = _sizes(q, k, v, kv)
+    _check_out(out, q)
+    _check_device(q, k=k, v=v, out=out)
     offset = Sk - Sq if offset is None else int(offset)
     scale = D ** -0.5 if scale is None else float(scale)
     if out is None:
@@ -253,6 +309,9 @@ def prefill_split(q, k, v, *, causal: bool = True, offset: Optional[int] = None,
     torch = _torch()
     kv = _kv_code(k, v)
     B, Hq, Hkv, Sq, Sk, D = _sizes(q, k, v, kv)
+    _check_out(out, q)
+    _check_workspace(workspace)
+    _check_device(q, k=k, v=v, out=out, workspace=workspace)
     offset = Sk - Sq if offset is None else int(offset)
     scale = D ** -0.5 if scale is None else float(scale)
     if out is None:
@@ -279,6 +338,9 @@ def decode(q, k, v, *, causal: bool = True, offset: Optional[int] = None,
     torch = _torch()
     kv = _kv_code(k, v)
     B, Hq, Hkv, Sq, Sk, D = _sizes(q, k, v, kv)
+    _check_out(out, q)
+    _check_workspace(workspace)
+    _check_device(q, k=k, v=v, out=out, workspace=workspace)
     offset = Sk - Sq if offset is None else int(offset)
     scale = D ** -0.5 if scale is None else float(scale)
     if out is None:
@@ -292,6 +354,48 @@ def decode(q, k, v, *, causal: bool = True, offset: Optional[int] = None,
     if rc != FA_OK:
         raise FAError(rc, "fa_decode")
     return out
+
+
+def prefill_stats(q, k, v, *, causal: bool = True, offset: Optional[int] = None,
+                  scale: Optional[float] = None, stream=None):
+    """fa_prefill_stats: (out, counts) with counts int32 [B, Sq, Hq, 2] (frame moves per row,
+    tiles in which the row's wave ran the O rescale)."""
+    torch = _torch()
+    kv = _kv_code(k, v)
+    B, Hq, Hkv, Sq, Sk, D = _sizes(q, k, v, kv)
+    _check_device(q, k=k, v=v)
+    offset = Sk - Sq if offset is None else int(offset)
+    scale = D ** -0.5 if scale is None else float(scale)
+    out = torch.empty_like(q)
+    counts = torch.zeros((B, Sq, Hq, 2), dtype=torch.int32, device=q.device)
+    rc = fa_prefill_stats(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, Hq, Hkv,
+                          Sq, Sk, D, int(bool(causal)), offset, scale, kv, counts.data_ptr(),
+                          _stream(q, stream))
+    if rc != FA_OK:
+        raise FAError(rc, "fa_prefill_stats")
+    return out, counts
+
+
+def decode_stats(q, k, v, *, causal: bool = True, offset: Optional[int] = None,
+                 scale: Optional[float] = None, stream=None):
+    """fa_decode_stats: (out, counts) with counts int32 [B, Sq, Hq, 2] (frame moves summed over
+    the splits, splits that held keys)."""
+    torch = _torch()
+    kv = _kv_code(k, v)
+    B, Hq, Hkv, Sq, Sk, D = _sizes(q, k, v, kv)
+    _check_device(q, k=k, v=v)
+    offset = Sk - Sq if offset is None else int(offset)
+    scale = D ** -0.5 if scale is None else float(scale)
+    out = torch.empty_like(q)
+    counts = torch.zeros((B, Sq, Hq, 2), dtype=torch.int32, device=q.device)
+    nbytes = decode_workspace_bytes(B, Hq, Hkv, Sq, Sk, D)
+    ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    rc = fa_decode_stats(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, Hq, Hkv,
+                         Sq, Sk, D, int(bool(causal)), offset, scale, kv, ws.data_ptr(),
+                         ws.numel(), counts.data_ptr(), _stream(q, stream))
+    if rc != FA_OK:
+        raise FAError(rc, "fa_decode_stats")
+    return out, counts
 
 
 def _paged_sizes(q, k_pages, v_pages, block_table, seq_lens, q_lens=None):
@@ -311,7 +415,9 @@ def _paged_sizes(q, k_pages, v_pages, block_table, seq_lens, q_lens=None):
             or v_pages.shape[:3] != k_pages.shape[:3]
             or (q_lens is not None and q_lens.numel() != B)):
         raise ValueError("block_table, seq_lens, q_lens and pages disagree with q")
-    _check_widths(k_pages, v_pages, _kv_code(k_pages, v_pages), D)
+    kv = _kv_code(k_pages, v_pages)
+    _check_q(q, kv)
+    _check_widths(k_pages, v_pages, kv, D)
     return B, Hq, Hkv, Sq, D, block_table.shape[1], n_pages
 
 
@@ -325,6 +431,9 @@ def prefill_paged(q, k_pages, v_pages, block_table, seq_lens, q_lens=None, *,
     kv = _kv_code(k_pages, v_pages)
     B, Hq, Hkv, Sq, D, max_pages, n_pages = _paged_sizes(q, k_pages, v_pages, block_table,
                                                          seq_lens, q_lens)
+    _check_out(out, q)
+    _check_device(q, k_pages=k_pages, v_pages=v_pages, block_table=block_table,
+                  seq_lens=seq_lens, q_lens=q_lens, out=out)
     scale = D ** -0.5 if scale is None else float(scale)
     if out is None:
         out = torch.zeros_like(q)
@@ -346,6 +455,10 @@ def decode_paged(q, k_pages, v_pages, block_table, seq_lens, *, causal: bool = T
     kv = _kv_code(k_pages, v_pages)
     B, Hq, Hkv, Sq, D, max_pages, n_pages = _paged_sizes(q, k_pages, v_pages, block_table,
                                                          seq_lens)
+    _check_out(out, q)
+    _check_workspace(workspace)
+    _check_device(q, k_pages=k_pages, v_pages=v_pages, block_table=block_table,
+                  seq_lens=seq_lens, out=out, workspace=workspace)
     scale = D ** -0.5 if scale is None else float(scale)
     if out is None:
         out = torch.empty_like(q)
@@ -366,6 +479,7 @@ def dequant_q4_0(blocks, stream=None):
     torch = _torch()
     if blocks.dtype != torch.uint8 or not blocks.is_contiguous() or blocks.numel() % 18:
         raise ValueError("blocks must be a contiguous uint8 tensor of whole 18-byte blocks")
+    _check_device(blocks)
     n = blocks.numel() // 18
     f32 = torch.empty(n * 32, dtype=torch.float32, device=blocks.device)
     f16 = torch.empty(n * 32, dtype=torch.float16, device=blocks.device)
@@ -394,6 +508,7 @@ def quantize_q4_0(x, out=None, stream=None):
         raise ValueError("out must be uint8 of x's shape with D/32*18 bytes last")
     if not (out[0] if out.dim() > 1 else out).is_contiguous():
         raise ValueError("out's rows must be contiguous within its first dimension")
+    _check_device(x, out=out)
     n_seq = x.shape[0] if x.dim() > 1 else 1
     rows = x.numel() // D // max(n_seq, 1) if x.numel() else 0
     x_stride = x.stride(0) if x.dim() > 1 else x.numel()

@@ -192,6 +192,62 @@ int fa_decode(const void *q, const void *k, const void *v, void *o, int B, int H
     return hip_status(fa::launch_decode(a, g, workspace, (hipStream_t)stream));
 }
 
+int fa_prefill_stats(const void *q, const void *k, const void *v, void *o, int B, int Hq,
+                     int Hkv, int Sq, int Sk, int D, int causal, int64_t causal_offset,
+                     float scale, int kv_dtype, int32_t *counts, fa_stream_t stream)
+{
+    fa::AttnArgs a;
+    const int rc = check_attention(q, k, v, o, B, Hq, Hkv, Sq, Sk, D, causal, causal_offset,
+                                   scale, kv_dtype, a);
+    if (rc != FA_OK)
+        return rc;
+    if (D != 128 || (kv_dtype != FA_KV_F16 && kv_dtype != FA_KV_BF16 && kv_dtype != FA_KV_Q4_0))
+        return FA_ERR_UNSUPPORTED;
+    if ((int64_t)B * Sq == 0)
+        return FA_OK;
+    if (!counts)
+        return FA_ERR_NULL;
+    if (!aligned(counts, 8))
+        return FA_ERR_ALIGN;
+    if (fa::prefill_grid(a).n_wg > kMaxWorkgroups)
+        return FA_ERR_UNSUPPORTED;
+    return hip_status(fa::launch_prefill(a, (hipStream_t)stream, nullptr, nullptr, counts));
+}
+
+int fa_decode_stats(const void *q, const void *k, const void *v, void *o, int B, int Hq,
+                    int Hkv, int Sq, int Sk, int D, int causal, int64_t causal_offset,
+                    float scale, int kv_dtype, void *workspace, size_t workspace_bytes,
+                    int32_t *counts, fa_stream_t stream)
+{
+    fa::AttnArgs a;
+    const int rc = check_attention(q, k, v, o, B, Hq, Hkv, Sq, Sk, D, causal, causal_offset,
+                                   scale, kv_dtype, a);
+    if (rc != FA_OK)
+        return rc;
+    if ((int64_t)(Hq / Hkv) * Sq > 16)
+        return FA_ERR_UNSUPPORTED;
+    if (!fa::q4_grouped(kv_dtype, (Hq / Hkv) * Sq, Hkv))
+        return FA_ERR_UNSUPPORTED;
+    if ((int64_t)B * Sq == 0)
+        return FA_OK;
+    if (!counts)
+        return FA_ERR_NULL;
+    if (!aligned(counts, 8))
+        return FA_ERR_ALIGN;
+    const fa::DecodeGrid g = fa::decode_grid(B, Hq, Hkv, Sq, Sk, D,
+                                             visible_end(Sq, Sk, a.causal, a.offset), false,
+                                             a.kv);
+    if (g.n_wg > kMaxWorkgroups)
+        return FA_ERR_UNSUPPORTED;
+    if (g.workspace_bytes > 0) {
+        if (!workspace || workspace_bytes < g.workspace_bytes)
+            return FA_ERR_WORKSPACE;
+        if (!aligned(workspace, 16))
+            return FA_ERR_ALIGN;
+    }
+    return hip_status(fa::launch_decode(a, g, workspace, (hipStream_t)stream, nullptr, counts));
+}
+
 int fa_dequant_q4_0(const void *blocks, int64_t n_blocks, float *out_f32, void *out_f16,
                     fa_stream_t stream)
 {

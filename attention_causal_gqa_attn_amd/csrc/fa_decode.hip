@@ -36,6 +36,11 @@ struct DecodeParams {
     // j / kBN]; sequence b has seq_lens[b] keys and its Sq queries are its last Sq positions
     const int32_t *block_table, *seq_lens;
     int max_pages, n_pages;
+    // counter instance of the head-group q4_0 kernel: per query row (b, i, h) two int32 that
+    // every split adds to (they must start at zero): the times the row's softmax frame moved
+    // in the split (the deferred-rescale test fired, counting the split's first frame), and 1
+    // for each split that held keys
+    int32_t *stats;
 };
 
 // One sequence's keys: how many it has, how many its rows can see ([0, kend)), and the
@@ -578,6 +583,7 @@ struct Q4Head {
     f32x4 sinit[NB];
     f32x4 oacc[8];                                  // P.V, MFMA q + 4 hh: byte q, nibble hh
     float frame, lsum, csum;
+    int nmove;                                      // frame moves (the counter instance)
 
     // Query rows j = lane % 4 (qi * G + hl; rows >= p.rows are padding, computed and never
     // written) of KV head kvh of batch b, over keys below ke.
@@ -658,11 +664,13 @@ struct Q4Head {
         frame = -INFINITY;
         lsum = 0.0f;
         csum = 0.0f;
+        nmove = 0;
     }
 
     // Scores of the tile's 64 keys (from key k0; kt = the head's key row 0 in LDS) and the
     // softmax state update; returns P as two packed f16 pairs (keys 4 blk + 0..3 of row j).
     // Lane l supplies key l's K row as A; D lane j + 4 blk, register r is key 4 blk + r.
+    template <bool STATS = false>
     __device__ __forceinline__ u32x2 scores(const uint8_t *kt, int64_t k0, float c)
     {
         uint32_t w[ROWDW];
@@ -744,6 +752,8 @@ struct Q4Head {
         mx = pair_max(mx);
         const float m2 = mx * c;
         const bool need = m2 > frame + kRescaleMarginLog2;
+        if constexpr (STATS)
+            nmove += need ? 1 : 0;
         if (__any(need)) {
             const float alpha = need ? exp2_fast(frame - m2) : 1.0f;
 #pragma unroll
@@ -878,7 +888,7 @@ struct Q4G {
 };
 constexpr int kQ4gWorkgroups = 256 * Q4G<128>::OCC;
 
-template <int D>
+template <int D, bool STATS = false>
 __global__ __launch_bounds__(kThreads, Q4G<D>::OCC) void decode_q4g_kernel(DecodeParams p)
 {
     using G = Q4G<D>;
@@ -967,10 +977,19 @@ __global__ __launch_bounds__(kThreads, Q4G<D>::OCC) void decode_q4g_kernel(Decod
             dma_tile(kb + NSTG - 1);
         const uint8_t *kt = lds + (kb % NSTG) * G::STAGE + wave * G::ROWB;
         hd.load_v(kt + G::TB);
-        const u32x2 pk = hd.scores(kt, ks + (int64_t)kb * kBN, a.c);
+        const u32x2 pk = hd.template scores<STATS>(kt, ks + (int64_t)kb * kBN, a.c);
         hd.pv(pk);
     }
 
+    if constexpr (STATS) {
+        // one lane per row adds this split's counts
+        if (lane < p.rows && nb > 0) {
+            const int qi = lane / a.G, h = kvh * a.G + lane % a.G;
+            int32_t *st = p.stats + 2 * (((int64_t)b * a.Sq + qi) * a.Hq + h);
+            atomicAdd(st, hd.nmove);
+            atomicAdd(st + 1, 1);
+        }
+    }
     // this wave's head: write the split's partial rows directly
     hd.reduce();
     if (hd.kg == 0 && hd.j < p.rows) {
@@ -1248,8 +1267,13 @@ __global__ __launch_bounds__(256) void decode_merge4_kernel(DecodeParams p)
 template <int D, int KV>
 hipError_t launch(const DecodeParams &p, int64_t n_wg, hipStream_t stream)
 {
+    if (p.stats && !(KV == KV_Q4_0 && q4_grouped(p.a.kv, p.rows, p.a.Hkv)))
+        return hipErrorInvalidValue;
     if constexpr (KV == KV_Q4_0) {
-        if (q4_grouped(p.a.kv, p.rows, p.a.Hkv))
+        if (p.stats)
+            hipLaunchKernelGGL((decode_q4g_kernel<D, true>), dim3((unsigned)n_wg),
+                               dim3(kThreads), 0, stream, p);
+        else if (q4_grouped(p.a.kv, p.rows, p.a.Hkv))
             hipLaunchKernelGGL((decode_q4g_kernel<D>), dim3((unsigned)n_wg), dim3(kThreads), 0,
                                stream, p);
         else if (p.rows <= kQ4Rows)
@@ -1308,7 +1332,7 @@ DecodeGrid decode_grid(int B, int Hq, int Hkv, int Sq, int Sk, int D, int64_t ke
 }
 
 hipError_t launch_decode(const AttnArgs &a, const DecodeGrid &g, void *workspace,
-                         hipStream_t stream, const PagedKV *paged)
+                         hipStream_t stream, const PagedKV *paged, int32_t *stats)
 {
     if (g.n_wg == 0)
         return hipSuccess;
@@ -1325,6 +1349,7 @@ hipError_t launch_decode(const AttnArgs &a, const DecodeGrid &g, void *workspace
     p.max_pages = paged ? paged->max_pages : 0;
     p.n_pages = paged ? paged->n_pages : 0;
     p.part = (float *)workspace;
+    p.stats = stats;
     if (a.D == 128) {
         if (a.kv == KV_F16)
             return launch<128, KV_F16>(p, g.n_wg, stream);

@@ -28,12 +28,15 @@ struct PrefillGrid {
 PrefillGrid prefill_grid(const AttnArgs &a);
 struct PagedKV;
 // paged: a paged cache (a.Sk = max_pages * 64, a.offset unused); q_lens (paged only, may be
-// null): sequence b's query count, rows [0, q_lens[b]) of its Sq
+// null): sequence b's query count, rows [0, q_lens[b]) of its Sq; stats (contiguous caches,
+// D = 128, one cache type for K and V; else hipErrorInvalidValue): the counter instance, two
+// int32 per query row [B, Sq, Hq, 2]
 hipError_t launch_prefill(const AttnArgs &a, hipStream_t stream, const PagedKV *paged = nullptr,
-                          const int32_t *q_lens = nullptr);
+                          const int32_t *q_lens = nullptr, int32_t *stats = nullptr);
 PrefillGrid prefill16_grid(const AttnArgs &a);
 hipError_t launch_prefill16(const AttnArgs &a, const PrefillGrid &g, hipStream_t stream,
-                            const PagedKV *paged = nullptr, const int32_t *q_lens = nullptr);
+                            const PagedKV *paged = nullptr, const int32_t *q_lens = nullptr,
+                            int32_t *stats = nullptr);
 // the paged prefill keeps a sequence's page numbers in LDS: at most this many per sequence
 constexpr int kPrefillMaxPages = 4096;
 // Balanced causal prefill (fa_prefill_split, contiguous caches; a q4_0 tensor at D = 128
@@ -70,8 +73,11 @@ struct PagedKV {
     const int32_t *block_table, *seq_lens;
     int max_pages, n_pages;
 };
+// stats (q4_0 caches taking the head-group kernel only, else hipErrorInvalidValue): the
+// counter instance, two int32 per query row [B, Sq, Hq, 2] that every split adds to
 hipError_t launch_decode(const AttnArgs &a, const DecodeGrid &g, void *workspace,
-                         hipStream_t stream, const PagedKV *paged = nullptr);
+                         hipStream_t stream, const PagedKV *paged = nullptr,
+                         int32_t *stats = nullptr);
 
 hipError_t launch_dequant_q4_0(const void *blocks, int64_t n_blocks, float *out_f32,
                                void *out_f16, hipStream_t stream);

@@ -62,6 +62,10 @@ struct Prefill16Params {
     int q_split, cap, n_main, n_tail;
     uint32_t *cnt;     // arrival counters, one per split unit, zero between calls
     float *part;       // partial rows [split unit][part][wave][64 rows][kPartRow floats]
+    // STATS instances: per query row (b, i, h), two int32 counters written in the epilogue:
+    // how many times the row's softmax frame moved (the deferred-rescale test fired for the
+    // row, counting the first frame), and in how many tiles its wave block ran the O rescale
+    int32_t *stats;
 };
 // a partial row: D unnormalised outputs, frame, sum, padding to 16 bytes
 constexpr int kPartRow = 132;
@@ -358,10 +362,11 @@ struct Plans {
     static_assert(schedule_ok<NDT, NST, NM>(sc), "softmax units placed in time");
 };
 
-template <int D, int KT, int VT, bool PAGED, bool SPLIT = false>
+template <int D, int KT, int VT, bool PAGED, bool SPLIT = false, bool STATS = false>
 __global__ __launch_bounds__(kNT, 1) void prefill16_kernel(Prefill16Params p)
 {
     static_assert(!SPLIT || !PAGED, "split: contiguous caches");
+    static_assert(!STATS || (!SPLIT && !PAGED), "counters: the plain contiguous kernel");
     static_assert(KT == VT || (KT != KV_BF16 && VT != KV_BF16), "bf16 caches are not mixed");
     constexpr bool BF = KT == KV_BF16;
     constexpr bool QK = KT == KV_Q4_0, QV = VT == KV_Q4_0;     // which tensors arrive raw
@@ -487,6 +492,7 @@ __global__ __launch_bounds__(kNT, 1) void prefill16_kernel(Prefill16Params p)
     float frame[2] = {-INFINITY, -INFINITY}, lsum[2] = {0.0f, 0.0f};
     float fr[2] = {0.0f, 0.0f}, alpha[2] = {1.0f, 1.0f};
     bool rescale[2] = {false, false};
+    int nmove[2] = {0, 0}, nresc[2] = {0, 0};        // STATS counters
 
     // ---- tile DMA: transfer i of thread t moves 16-byte chunk n = (i*kNW + wave)*64 + lane ---
     // (b, kv head)'s key 0; a paged cache: kv head's row in a page, pages added per tile
@@ -732,6 +738,10 @@ __global__ __launch_bounds__(kNT, 1) void prefill16_kernel(Prefill16Params p)
             fr[j] = (frame[j] == -INFINITY) ? 0.0f : frame[j];
             lsum[j] *= alpha[j];
             rescale[j] = __any(need[j]);
+            if constexpr (STATS) {
+                nmove[j] += need[j] ? 1 : 0;
+                nresc[j] += rescale[j] ? 1 : 0;
+            }
             pin(fr[j]);
         } else if constexpr (x.kind == UE) {
             constexpr int t4 = x.idx >> 2, e = x.idx & 3, i = 8 * (t4 & 1) + 2 * e;
@@ -1046,6 +1056,11 @@ __global__ __launch_bounds__(kNT, 1) void prefill16_kernel(Prefill16Params p)
             continue;
         const float inv = ltot > 0.0f ? 1.0f / ltot : 0.0f;
         uint16_t *op = (uint16_t *)a.o + (((int64_t)b * a.Sq + qi[j]) * a.Hq + h) * D;
+        if constexpr (STATS) {
+            if (half == 0)
+                *(int2 *)(p.stats + 2 * (((int64_t)b * a.Sq + qi[j]) * a.Hq + h)) =
+                    make_int2(nmove[j], nresc[j]);
+        }
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
@@ -1082,6 +1097,16 @@ hipError_t launch16(const Prefill16Params &p, int64_t n_wg, hipStream_t stream)
             return hipGetLastError();
         }
     }
+    // the counter instances: D = 128, one cache type for K and V
+    if constexpr (D == 128 && KT == VT) {
+        if (p.stats) {
+            hipLaunchKernelGGL((prefill16_kernel<D, KT, VT, false, false, true>),
+                               dim3((unsigned)n_wg), dim3(kNT), 0, stream, p);
+            return hipGetLastError();
+        }
+    }
+    if (p.stats)
+        return hipErrorInvalidValue;
     if (p.block_table)
         hipLaunchKernelGGL((prefill16_kernel<D, KT, VT, true>), dim3((unsigned)n_wg), dim3(kNT),
                            0, stream, p);
@@ -1170,10 +1195,10 @@ PrefillGrid prefill16_grid(const AttnArgs &a)
 PrefillGrid prefill_grid(const AttnArgs &a) { return prefill16_grid(a); }
 
 hipError_t launch_prefill(const AttnArgs &a, hipStream_t stream, const PagedKV *paged,
-                          const int32_t *q_lens)
+                          const int32_t *q_lens, int32_t *stats)
 {
     const PrefillGrid g = prefill16_grid(a);
-    return g.n_wg == 0 ? hipSuccess : launch_prefill16(a, g, stream, paged, q_lens);
+    return g.n_wg == 0 ? hipSuccess : launch_prefill16(a, g, stream, paged, q_lens, stats);
 }
 
 hipError_t launch_prefill_split(const AttnArgs &a, const PrefillSplit &sp, void *workspace,
@@ -1195,9 +1220,10 @@ hipError_t launch_prefill_split(const AttnArgs &a, const PrefillSplit &sp, void 
 }
 
 hipError_t launch_prefill16(const AttnArgs &a, const PrefillGrid &g, hipStream_t stream,
-                            const PagedKV *paged, const int32_t *q_lens)
+                            const PagedKV *paged, const int32_t *q_lens, int32_t *stats)
 {
     Prefill16Params p{a, g.hpw, g.qsub, g.n_qblk, g.n_hchunk, nullptr, nullptr, nullptr, 0, 0};
+    p.stats = stats;
     if (paged) {
         if (paged->max_pages > kPrefillMaxPages || !paged->block_table || !paged->seq_lens)
             return hipErrorInvalidValue;

@@ -92,11 +92,14 @@ int fa_prefill(const void *q, const void *k, const void *v, void *o,
  * Causal prefill with the work balanced across workgroups. In a causal chunk the later query
  * blocks see more keys, so the workgroups that own them hold more 64-key tiles and the call
  * waits for them (at 2048 queries against 2048 keys the tiles per workgroup run from 1 to
- * 32). fa_prefill_split gives every (b, KV head, 64-row query block) unit that holds more
- * tiles than the average (over units, or over the 256 CUs when units are fewer) a second
- * workgroup for its tiles past the average; the second workgroups run after the first ones,
- * and the later of a unit's two parts to finish merges them (log-sum-exp of the two partial
- * softmax states) and writes the unit's rows. No workgroup waits for another.
+ * 32). Where the tile count grows with the query block, blocks q and n-1-q together hold about
+ * twice the average, so fa_prefill_split pairs them: a unit (b, KV head, head chunk, 64-row
+ * query block) of block q >= q_split holds more than `cap` tiles (cap = the average tiles per
+ * unit plus a small bias, q_split >= n/2) and runs only its first cap tiles; the workgroup of
+ * its mirror block n-1-q, a light unit, runs the remaining tiles after its own unit. The grid
+ * stays one workgroup per unit. The later of a split unit's two parts to finish merges them
+ * (log-sum-exp of the two partial softmax states) and writes the unit's rows. No workgroup
+ * waits for another.
  * Arguments as fa_prefill, plus the caller-owned workspace:
  *   workspace   >= fa_prefill_workspace_bytes(...) bytes, 16-byte aligned. Its first 4096
  *               bytes are arrival counters that must be zero before the first call that uses
@@ -118,7 +121,13 @@ int fa_prefill_split(const void *q, const void *k, const void *v, void *o,
                      void *workspace, size_t workspace_bytes, fa_stream_t stream);
 
 /*
- * Bytes of workspace fa_decode needs for these sizes (0 when nothing is needed).
+ * Split-K decode. The pages give decode only as model-level token rates (mi210-llm-stack,
+ * "FlashAttention on gfx90a", "The Problem": FA on against FA off); the split-K organisation
+ * with a log-sum-exp merge is this library's design for the memory-bound one-token step, not
+ * a passage of the pages. What each row computes is the same attention as fa_prefill.
+ *
+ * Bytes of workspace fa_decode needs for these sizes (0 when nothing is needed). Hkv is an
+ * argument because the kernel choice, and with it the split count, depends on it.
  * The workspace holds one partial (running max, sum, unnormalised output row) per query
  * row and key split; it is scratch between the split kernel and the merge kernel of one
  * call and need not be initialised.
@@ -176,6 +185,35 @@ int fa_prefill_paged(const void *q, const void *k_pages, const void *v_pages, vo
                      const int32_t *block_table, const int32_t *seq_lens, const int32_t *q_lens,
                      int B, int Hq, int Hkv, int Sq, int D, int max_pages, int n_pages,
                      int causal, float scale, int kv_dtype, fa_stream_t stream);
+
+/*
+ * Counter instances, for tests of the deferred rescale (mlxcel PR #2306, "What changed" and
+ * "Test plan": the O/l rescale runs only when a row's block maximum outgrows its frame by
+ * more than the margin, rarely in the steady state of a chunked prefill, and a score ramp
+ * drives rows past the margin so the branch is exercised). They run the same kernel source as
+ * fa_prefill / fa_decode with two counters per query row added, and give the same output.
+ *   counts   device int32 [B, Sq, Hq, 2], 8-byte aligned. Per query row (b, i, h):
+ *            counts[..., 0] = how many times the row's softmax frame moved (the rescale test
+ *            fired for the row; the first frame, taken from -inf, counts as one);
+ *            counts[..., 1] = fa_prefill_stats: in how many 64-key tiles the row's wave ran
+ *            the O rescale (it runs when any row of its 32-row block moved);
+ *                             fa_decode_stats: how many key splits held keys for the row.
+ *            fa_prefill_stats writes every row of the call; fa_decode_stats adds to the
+ *            counters (every split of the row adds its own), so they must be zero first.
+ * fa_prefill_stats: D = 128 and kv_dtype FA_KV_F16, FA_KV_BF16 or FA_KV_Q4_0, else
+ * FA_ERR_UNSUPPORTED. fa_decode_stats: a q4_0 cache with at most 4 query rows per KV head
+ * (Sq * Hq / Hkv <= 4) and Hkv a multiple of 4 (the head-group decode kernel), else
+ * FA_ERR_UNSUPPORTED. Other arguments and errors as fa_prefill / fa_decode.
+ */
+int fa_prefill_stats(const void *q, const void *k, const void *v, void *o,
+                     int B, int Hq, int Hkv, int Sq, int Sk, int D,
+                     int causal, int64_t causal_offset, float scale, int kv_dtype,
+                     int32_t *counts, fa_stream_t stream);
+int fa_decode_stats(const void *q, const void *k, const void *v, void *o,
+                    int B, int Hq, int Hkv, int Sq, int Sk, int D,
+                    int causal, int64_t causal_offset, float scale, int kv_dtype,
+                    void *workspace, size_t workspace_bytes, int32_t *counts,
+                    fa_stream_t stream);
 
 /*
  * Dequantize n_blocks q4_0 blocks (18 bytes each, 2-byte aligned) with the same device

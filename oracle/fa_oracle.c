@@ -18,8 +18,9 @@
  *   - layouts are [B, S, H, D] contiguous; query head h reads K/V head h / (Hq / Hkv)
  *     (consecutive grouping of "GQA 32/8", mlxcel PR commit message 1);
  *   - query i sits at absolute position i + offset and, when causal, sees key j iff
- *     j <= i + offset ("2,048-token query chunks against 2K to 16K keys": the chunk is the
- *     last Sq positions, so offset = Sk - Sq there);
+ *     j <= i + offset (the mlxcel PR #2306 measures query chunks of 2048 tokens against key
+ *     ranges of 2K to 16K, which this reads as the chunk being the last Sq positions, so
+ *     offset = Sk - Sq there);
  *   - a row that sees no key outputs zeros;
  *   - q4_0 ("-ctk q4_0 -ctv q4_0", mi210-llm-stack page 1): 18-byte blocks of 32 head-dim
  *     elements, a little-endian f16 scale d then 16 bytes where byte t holds the 4-bit code of

@@ -288,3 +288,107 @@ def test_binding_refuses_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(fa, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="not built"):
         fa.load()
+
+
+# ---- tensor helpers: type, shape and device checks that run before any pointer is taken ----
+# Host tensors are enough here: every rejection below is raised before the C ABI is called,
+# and a host tensor with the right types is itself rejected (its address would reach the
+# kernels as a wild pointer).
+
+def _t(shape, dtype):
+    import torch
+    return torch.zeros(shape, dtype=dtype)
+
+
+def _qkv(q_dtype, kv_dtype, D=128, Sq=4, Sk=8):
+    import torch
+    width = D // 32 * 18 if kv_dtype == torch.uint8 else D
+    return (_t((1, Sq, 8, D), q_dtype), _t((1, Sk, 2, width), kv_dtype),
+            _t((1, Sk, 2, width), kv_dtype))
+
+
+@pytest.mark.parametrize("call", ["prefill", "prefill_split", "decode"])
+def test_helpers_reject_wrong_q_type(call):
+    import torch
+    fn = getattr(fa, call)
+    for qd, kvd in [(torch.float32, torch.float16), (torch.bfloat16, torch.float16),
+                    (torch.float16, torch.bfloat16), (torch.float32, torch.uint8),
+                    (torch.bfloat16, torch.uint8)]:
+        q, k, v = _qkv(qd, kvd)
+        with pytest.raises(ValueError, match="queries"):
+            fn(q, k, v)
+
+
+@pytest.mark.parametrize("call", ["prefill", "prefill_split", "decode"])
+def test_helpers_reject_bad_out(call):
+    import torch
+    fn = getattr(fa, call)
+    q, k, v = _qkv(torch.float16, torch.float16)
+    for out in (_t((1, 4, 8, 64), torch.float16),            # too small
+                _t((1, 4, 8, 128), torch.float32),           # wrong type
+                _t((1, 8, 4, 128), torch.float16).transpose(1, 2)):   # not contiguous
+        with pytest.raises(ValueError, match="out must be"):
+            fn(q, k, v, out=out)
+
+
+@pytest.mark.parametrize("call", ["prefill", "prefill_split", "decode"])
+def test_helpers_reject_host_tensors(call):
+    import torch
+    fn = getattr(fa, call)
+    for kvd in (torch.float16, torch.uint8):
+        q, k, v = _qkv(torch.float16, kvd)
+        with pytest.raises(ValueError, match="GPU tensors"):
+            fn(q, k, v)
+    q, k, v = _qkv(torch.bfloat16, torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU tensors"):
+        fn(q, k, v, out=torch.empty_like(q))
+
+
+def test_paged_helpers_reject_wrong_types_and_host_tensors():
+    import torch
+    q = _t((2, 4, 8, 128), torch.float32)
+    pages = _t((3, 64, 2, 128), torch.float16)
+    table = torch.zeros((2, 2), dtype=torch.int32)
+    lens = torch.zeros(2, dtype=torch.int32)
+    with pytest.raises(ValueError, match="queries"):
+        fa.decode_paged(q, pages, pages, table, lens)
+    with pytest.raises(ValueError, match="queries"):
+        fa.prefill_paged(q, pages, pages, table, lens)
+    q = q.half()
+    with pytest.raises(ValueError, match="out must be"):
+        fa.decode_paged(q, pages, pages, table, lens, out=_t((2, 4, 8, 64), torch.float16))
+    with pytest.raises(ValueError, match="GPU tensors"):
+        fa.decode_paged(q, pages, pages, table, lens)
+    with pytest.raises(ValueError, match="GPU tensors"):
+        fa.prefill_paged(q, pages, pages, table, lens)
+
+
+def test_dequant_and_writer_reject_host_tensors():
+    import torch
+    with pytest.raises(ValueError, match="GPU tensors"):
+        fa.dequant_q4_0(_t((36,), torch.uint8))
+    with pytest.raises(ValueError, match="GPU tensors"):
+        fa.quantize_q4_0(_t((4, 32), torch.float16))
+
+
+def test_stats_entry_points_reject():
+    """The counter instances take the documented subset and check their counts buffer."""
+    st = fa.fa_prefill_stats
+    args = [P, P, P, P, 1, 32, 8, 16, 64, 128, 1, 48, 0.088]
+    assert st(*args, 0, None, None) == fa.FA_ERR_NULL                   # counts missing
+    assert st(*args, 0, ODD, None) == fa.FA_ERR_ALIGN                   # counts misaligned
+    assert st(*args, 3, P, None) == fa.FA_ERR_UNSUPPORTED               # mixed cache
+    assert st(*args[:9], 64, 1, 48, 0.125, 0, P, None) == fa.FA_ERR_UNSUPPORTED   # D = 64
+    assert st(*args, 7, P, None) == fa.FA_ERR_DTYPE
+    assert st(P, P, P, P, 1, 32, 8, 0, 64, 128, 1, 48, 0.088, 0, None, None) == fa.FA_OK
+    dt = fa.fa_decode_stats
+    dargs = [P, P, P, P, 4, 32, 8, 1, 4096, 128, 1, 4095, 0.088]
+    nbytes = fa.fa_decode_workspace_bytes(4, 32, 8, 1, 4096, 128)
+    assert dt(*dargs, 2, P, nbytes, None, None) == fa.FA_ERR_NULL
+    assert dt(*dargs, 2, P, nbytes, ODD, None) == fa.FA_ERR_ALIGN
+    assert dt(*dargs, 2, P, 16, P, None) == fa.FA_ERR_WORKSPACE
+    assert dt(*dargs, 0, P, nbytes, P, None) == fa.FA_ERR_UNSUPPORTED    # f16: other kernel
+    assert dt(P, P, P, P, 4, 32, 8, 2, 4096, 128, 1, 4094, 0.088, 2, P, nbytes, P,
+              None) == fa.FA_ERR_UNSUPPORTED                             # 8 rows per KV head
+    assert dt(P, P, P, P, 4, 8, 2, 1, 4096, 128, 1, 4095, 0.088, 2, P, nbytes, P,
+              None) == fa.FA_ERR_UNSUPPORTED                             # Hkv not 4k
