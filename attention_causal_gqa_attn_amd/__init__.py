@@ -36,9 +36,12 @@ FA_ERR_WORKSPACE = -5
 FA_ERR_ALIGN = -6
 FA_ERR_HIP = -7
 FA_ERR_VALUE = -8
+FA_ERR_TOO_LARGE = -9
+FA_NOALLOC_SCRATCH_BYTES = 16 << 20
 
 EXPORTS = ("fa_prefill", "fa_prefill_split", "fa_prefill_workspace_bytes", "fa_decode",
-           "fa_decode_paged", "fa_prefill_paged", "fa_decode_workspace_bytes", "fa_prefill_stats",
+           "fa_decode_paged", "fa_prefill_paged", "fa_decode_workspace_bytes", "fa_decode_noalloc",
+           "fa_prefill_stats",
            "fa_decode_stats", "fa_dequant_q4_0", "fa_quantize_q4_0", "fa_strerror", "fa_version")
 PAGE_KEYS = 64
 
@@ -71,6 +74,8 @@ def load() -> ctypes.CDLL:
         lib.fa_prefill_workspace_bytes.restype = sz
         lib.fa_decode.argtypes = attn + [vp, sz, vp]
         lib.fa_decode.restype = i32
+        lib.fa_decode_noalloc.argtypes = attn + [vp]
+        lib.fa_decode_noalloc.restype = i32
         lib.fa_decode_paged.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
                                         i32, i32, f32, i32, vp, sz, vp]
         lib.fa_decode_paged.restype = i32
@@ -118,6 +123,12 @@ def fa_decode(q, k, v, o, B, Hq, Hkv, Sq, Sk, D, causal, causal_offset, scale, k
               workspace, workspace_bytes, stream) -> int:
     return load().fa_decode(q, k, v, o, B, Hq, Hkv, Sq, Sk, D, causal, causal_offset, scale,
                             kv_dtype, workspace, workspace_bytes, stream)
+
+
+def fa_decode_noalloc(q, k, v, o, B, Hq, Hkv, Sq, Sk, D, causal, causal_offset, scale, kv_dtype,
+                      stream) -> int:
+    return load().fa_decode_noalloc(q, k, v, o, B, Hq, Hkv, Sq, Sk, D, causal, causal_offset,
+                                    scale, kv_dtype, stream)
 
 
 def fa_decode_workspace_bytes(B, Hq, Hkv, Sq, Sk, D) -> int:

@@ -3,6 +3,7 @@
 // the first HIP call, so a rejected call has launched nothing; the library allocates nothing.
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "../../include/fa.h"
 #include "fa_device.h"
@@ -92,6 +93,35 @@ int64_t visible_end(int Sq, int Sk, int causal, int64_t offset)
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
+
+// ---- fixed scratch of fa_decode_noalloc -------------------------------------------------------
+// The decode workspace of fa_decode_noalloc lives in this file-scope device array, one copy per
+// GPU, held until the process ends. Host code never uses the array's name as an address (on
+// the host it is only a stand-in for the symbol): each device's copy is looked up once with
+// hipGetSymbolAddress, with that device current, and the pointer is kept per device.
+constexpr size_t kNoAllocScratchBytes = FA_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's copy of `scratch`; FA_ERR_HIP if it cannot be found.
+int scratch_of_current_device(void **out)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return FA_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr)
+            return FA_ERR_HIP;
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return FA_OK;
+}
 
 }  // namespace
 
@@ -190,6 +220,35 @@ int fa_decode(const void *q, const void *k, const void *v, void *o, int B, int H
             return FA_ERR_ALIGN;
     }
     return hip_status(fa::launch_decode(a, g, workspace, (hipStream_t)stream));
+}
+
+int fa_decode_noalloc(const void *q, const void *k, const void *v, void *o, int B, int Hq,
+                      int Hkv, int Sq, int Sk, int D, int causal, int64_t causal_offset,
+                      float scale, int kv_dtype, fa_stream_t stream)
+{
+    fa::AttnArgs a;
+    const int rc = check_attention(q, k, v, o, B, Hq, Hkv, Sq, Sk, D, causal, causal_offset,
+                                   scale, kv_dtype, a);
+    if (rc != FA_OK)
+        return rc;
+    if ((int64_t)(Hq / Hkv) * Sq > 16)
+        return FA_ERR_UNSUPPORTED;
+    if ((int64_t)B * Sq == 0)
+        return FA_OK;
+    const fa::DecodeGrid g = fa::decode_grid(B, Hq, Hkv, Sq, Sk, D,
+                                             visible_end(Sq, Sk, a.causal, a.offset), false,
+                                             a.kv);
+    if (g.n_wg > kMaxWorkgroups)
+        return FA_ERR_UNSUPPORTED;
+    if (g.workspace_bytes > kNoAllocScratchBytes)
+        return FA_ERR_TOO_LARGE;
+    // every partial row the merge reads is written by the split kernel of the same call, so
+    // nothing in the scratch has to start at zero
+    void *ws = nullptr;
+    const int sc = scratch_of_current_device(&ws);
+    if (sc != FA_OK)
+        return sc;
+    return hip_status(fa::launch_decode(a, g, ws, (hipStream_t)stream));
 }
 
 int fa_prefill_stats(const void *q, const void *k, const void *v, void *o, int B, int Hq,
@@ -389,6 +448,9 @@ const char *fa_strerror(int code)
         return "HIP runtime error at launch";
     case FA_ERR_VALUE:
         return "scale must be finite and positive";
+    case FA_ERR_TOO_LARGE:
+        return "fa_decode_noalloc: the call needs more than the fixed scratch "
+               "(FA_NOALLOC_SCRATCH_BYTES); use fa_decode with a workspace";
     default:
         return "unknown status code";
     }

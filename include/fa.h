@@ -69,6 +69,7 @@ enum fa_status {
     FA_ERR_ALIGN = -6,        /* Q/O/K/V not 16-byte aligned (a q4_0 K or V: 4-byte aligned) */
     FA_ERR_HIP = -7,          /* the HIP runtime reported an error at launch */
     FA_ERR_VALUE = -8,        /* scale not finite and > 0 */
+    FA_ERR_TOO_LARGE = -9,    /* fa_decode_noalloc: more scratch than FA_NOALLOC_SCRATCH_BYTES */
 };
 
 /*
@@ -145,6 +146,26 @@ int fa_decode(const void *q, const void *k, const void *v, void *o,
               int B, int Hq, int Hkv, int Sq, int Sk, int D,
               int causal, int64_t causal_offset, float scale, int kv_dtype,
               void *workspace, size_t workspace_bytes, fa_stream_t stream);
+
+/*
+ * fa_decode for callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc. Same arguments, kernels, results and
+ * errors as fa_decode, without the workspace: the split partials go to a fixed scratch array
+ * of FA_NOALLOC_SCRATCH_BYTES inside the library, one per GPU, held until the process ends.
+ * The call itself allocates nothing (no hipMalloc, no allocating library routine); its first
+ * call on a device looks up that device's copy of the array (the device that is current must
+ * be the stream's). Calls that need more scratch than the maximum (fa_decode_workspace_bytes
+ * of the call above it; 4.3 MB at 4 sequences x 32768 q4_0 keys, GQA 32/8, D = 128) return
+ * FA_ERR_TOO_LARGE before any HIP call. Every call on one GPU shares that GPU's array (it keeps
+ * the last call's partials; nothing in it needs to start at zero), so calls that may overlap
+ * on one GPU (different streams, or different threads without ordering) race and give wrong
+ * output: order them on one stream.
+ */
+#define FA_NOALLOC_SCRATCH_BYTES (16u << 20)
+int fa_decode_noalloc(const void *q, const void *k, const void *v, void *o,
+                      int B, int Hq, int Hkv, int Sq, int Sk, int D,
+                      int causal, int64_t causal_offset, float scale, int kv_dtype,
+                      fa_stream_t stream);
 
 /*
  * Split-K decode over paged K/V caches (a batch of sequences of different lengths, as a
