@@ -8,11 +8,12 @@ missing every call raises.
 
 Raw entry points with the C names (pointers and ints): fa_prefill, fa_prefill_split,
 fa_prefill_workspace_bytes, fa_decode, fa_decode_paged, fa_prefill_paged,
-fa_decode_workspace_bytes, fa_prefill_stats, fa_decode_stats, fa_dequant_q4_0,
+fa_decode_workspace_bytes, fa_decode_noalloc, fa_standard_attention,
+fa_standard_workspace_bytes, fa_prefill_stats, fa_decode_stats, fa_dequant_q4_0,
 fa_quantize_q4_0, fa_strerror, fa_version.
 Tensor helpers: prefill, prefill_split, prefill_workspace_bytes, prefill_paged, decode,
-decode_paged, decode_workspace_bytes, prefill_stats, decode_stats, dequant_q4_0,
-quantize_q4_0.
+decode_paged, decode_workspace_bytes, standard_attention, standard_workspace_bytes,
+prefill_stats, decode_stats, dequant_q4_0, quantize_q4_0.
 """
 from __future__ import annotations
 
@@ -41,8 +42,9 @@ FA_NOALLOC_SCRATCH_BYTES = 16 << 20
 
 EXPORTS = ("fa_prefill", "fa_prefill_split", "fa_prefill_workspace_bytes", "fa_decode",
            "fa_decode_paged", "fa_prefill_paged", "fa_decode_workspace_bytes", "fa_decode_noalloc",
-           "fa_prefill_stats",
-           "fa_decode_stats", "fa_dequant_q4_0", "fa_quantize_q4_0", "fa_strerror", "fa_version")
+           "fa_standard_attention", "fa_standard_workspace_bytes", "fa_prefill_stats",
+           "fa_decode_stats", "fa_dequant_q4_0", "fa_quantize_q4_0", "fa_measure_read",
+           "fa_strerror", "fa_version")
 PAGE_KEYS = 64
 
 
@@ -84,6 +86,10 @@ def load() -> ctypes.CDLL:
         lib.fa_prefill_paged.restype = i32
         lib.fa_decode_workspace_bytes.argtypes = [i32] * 6
         lib.fa_decode_workspace_bytes.restype = sz
+        lib.fa_standard_attention.argtypes = attn + [vp, sz, vp]
+        lib.fa_standard_attention.restype = i32
+        lib.fa_standard_workspace_bytes.argtypes = [i32] * 8
+        lib.fa_standard_workspace_bytes.restype = sz
         lib.fa_prefill_stats.argtypes = attn + [vp, vp]
         lib.fa_prefill_stats.restype = i32
         lib.fa_decode_stats.argtypes = attn + [vp, sz, vp, vp]
@@ -92,6 +98,8 @@ def load() -> ctypes.CDLL:
         lib.fa_dequant_q4_0.restype = i32
         lib.fa_quantize_q4_0.argtypes = [vp, i32, vp, i64, i64, i32, i64, i64, vp]
         lib.fa_quantize_q4_0.restype = i32
+        lib.fa_measure_read.argtypes = [vp, i64, vp, ctypes.c_uint32, i32, vp]
+        lib.fa_measure_read.restype = i32
         lib.fa_strerror.argtypes = [i32]
         lib.fa_strerror.restype = ctypes.c_char_p
         lib.fa_version.argtypes = []
@@ -135,6 +143,16 @@ def fa_decode_workspace_bytes(B, Hq, Hkv, Sq, Sk, D) -> int:
     return load().fa_decode_workspace_bytes(B, Hq, Hkv, Sq, Sk, D)
 
 
+def fa_standard_attention(q, k, v, o, B, Hq, Hkv, Sq, Sk, D, causal, causal_offset, scale,
+                          kv_dtype, workspace, workspace_bytes, stream) -> int:
+    return load().fa_standard_attention(q, k, v, o, B, Hq, Hkv, Sq, Sk, D, causal, causal_offset,
+                                        scale, kv_dtype, workspace, workspace_bytes, stream)
+
+
+def fa_standard_workspace_bytes(B, Hq, Hkv, Sq, Sk, D, kv_dtype, units_per_pass) -> int:
+    return load().fa_standard_workspace_bytes(B, Hq, Hkv, Sq, Sk, D, kv_dtype, units_per_pass)
+
+
 def fa_prefill_stats(q, k, v, o, B, Hq, Hkv, Sq, Sk, D, causal, causal_offset, scale, kv_dtype,
                      counts, stream) -> int:
     return load().fa_prefill_stats(q, k, v, o, B, Hq, Hkv, Sq, Sk, D, causal, causal_offset,
@@ -170,6 +188,10 @@ def fa_quantize_q4_0(x, x_dtype, blocks, n_seq, rows_per_seq, D, x_seq_stride,
                      blocks_seq_stride, stream) -> int:
     return load().fa_quantize_q4_0(x, x_dtype, blocks, n_seq, rows_per_seq, D, x_seq_stride,
                                    blocks_seq_stride, stream)
+
+
+def fa_measure_read(buf, nbytes, sink, magic, workgroups, stream) -> int:
+    return load().fa_measure_read(buf, nbytes, sink, magic, workgroups, stream)
 
 
 def fa_strerror(code: int) -> str:
@@ -364,6 +386,41 @@ def decode(q, k, v, *, causal: bool = True, offset: Optional[int] = None,
                    workspace.numel() * workspace.element_size(), _stream(q, stream))
     if rc != FA_OK:
         raise FAError(rc, "fa_decode")
+    return out
+
+
+def standard_workspace_bytes(q, k, v, units_per_pass: int = 0) -> int:
+    """Workspace bytes of fa_standard_attention for these tensors, units_per_pass (b, KV head)
+    units at a time (0: all of them, 1: the minimum)."""
+    kv = _kv_code(k, v)
+    B, Hq, Hkv, Sq, Sk, D = _sizes(q, k, v, kv)
+    return fa_standard_workspace_bytes(B, Hq, Hkv, Sq, Sk, D, kv, int(units_per_pass))
+
+
+def standard_attention(q, k, v, *, causal: bool = True, offset: Optional[int] = None,
+                       scale: Optional[float] = None, out=None, workspace=None, stream=None):
+    """Standard (non-flash) attention via fa_standard_attention: a q4_0 K / V dequantized to
+    f16, S = scale Q K^T materialised, row softmax, P V. A workspace for every unit at once is
+    allocated when none is given (256-byte aligned)."""
+    torch = _torch()
+    kv = _kv_code(k, v)
+    B, Hq, Hkv, Sq, Sk, D = _sizes(q, k, v, kv)
+    _check_out(out, q)
+    _check_workspace(workspace)
+    _check_device(q, k=k, v=v, out=out, workspace=workspace)
+    offset = Sk - Sq if offset is None else int(offset)
+    scale = D ** -0.5 if scale is None else float(scale)
+    if out is None:
+        out = torch.empty_like(q)
+    if workspace is None:
+        nbytes = fa_standard_workspace_bytes(B, Hq, Hkv, Sq, Sk, D, kv, 0)
+        workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=q.device)
+    rc = fa_standard_attention(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, Hq,
+                               Hkv, Sq, Sk, D, int(bool(causal)), offset, scale, kv,
+                               workspace.data_ptr(),
+                               workspace.numel() * workspace.element_size(), _stream(q, stream))
+    if rc != FA_OK:
+        raise FAError(rc, "fa_standard_attention")
     return out
 
 

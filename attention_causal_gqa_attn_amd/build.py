@@ -18,7 +18,8 @@ import tempfile
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libfa.so")
-SOURCES = ["fa_api.cpp", "fa_prefill16.hip", "fa_decode.hip", "fa_dequant.hip", "fa_quant.hip"]
+SOURCES = ["fa_api.cpp", "fa_prefill16.hip", "fa_decode.hip", "fa_dequant.hip", "fa_quant.hip",
+           "fa_standard.hip", "fa_measure.hip"]
 ARCH = "gfx950"
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
@@ -38,8 +39,39 @@ def _quiet(out: str) -> str:
     return "\n".join(l for l in out.splitlines() if "packed-fp32-ops" not in l)
 
 
+# The prefill kernels issue some MFMAs and lane exchanges from inline asm and wait out their
+# hazards with hand-counted s_nop drains; those counts were checked against the code this
+# compiler emits. Another compiler may schedule around them differently: the build says so.
+TESTED_HIPCC = "AMD clang version 22.0.0git (https://github.com/RadeonOpenCompute/llvm-project roc-7.2.0"
+BUILD_INFO = os.path.join(HERE, "libfa.build.json")
+
+
+def hipcc_version(hipcc=None) -> str:
+    r = subprocess.run([hipcc or _hipcc(), "--version"], capture_output=True, text=True)
+    return " | ".join(l.strip() for l in r.stdout.splitlines()[:2])
+
+
+def build_info() -> dict:
+    """What build() recorded about the library in this tree (empty if nothing was recorded)."""
+    import json
+    try:
+        with open(BUILD_INFO) as f:
+            return json.load(f)
+    except (OSError, ValueError):
+        return {}
+
+
 def build(verbose: bool = False, extra_flags=()) -> str:
+    import json
     hipcc = _hipcc()
+    version = hipcc_version(hipcc)
+    tested = TESTED_HIPCC in version
+    if verbose:
+        print(f"hipcc: {version}", flush=True)
+    if not tested:
+        print(f"warning: {hipcc} is not the compiler the asm hazard drains were checked "
+              f"against ({TESTED_HIPCC}...); run the GPU parity tests before trusting it",
+              file=sys.stderr, flush=True)
     with tempfile.TemporaryDirectory(prefix="fa_build_") as tmp:
         def compile_one(src):
             obj = os.path.join(tmp, os.path.splitext(src)[0] + ".o")
@@ -63,6 +95,9 @@ def build(verbose: bool = False, extra_flags=()) -> str:
             raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{_quiet(r.stdout + r.stderr)}")
         shutil.copyfile(out, LIB + ".tmp")
         os.replace(LIB + ".tmp", LIB)
+    with open(BUILD_INFO, "w") as f:
+        json.dump({"hipcc_version": version, "tested_compiler": tested, "arch": ARCH,
+                   "flags": COMMON + list(extra_flags)}, f)
     if verbose:
         print(f"built {LIB}", flush=True)
     return LIB

@@ -307,6 +307,40 @@ int fa_decode_stats(const void *q, const void *k, const void *v, void *o, int B,
     return hip_status(fa::launch_decode(a, g, workspace, (hipStream_t)stream, nullptr, counts));
 }
 
+size_t fa_standard_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Sk, int D, int kv_dtype,
+                                   int units_per_pass)
+{
+    fa::AttnArgs a;
+    const void *nz = (const void *)(uintptr_t)4096;
+    if (check_attention(nz, nz, nz, (void *)nz, B, Hq, Hkv, Sq, Sk, D, 0, 0, 1.0f, kv_dtype,
+                        a) != FA_OK || (int64_t)B * Sq == 0)
+        return 0;
+    return fa::standard_workspace_bytes(B, Hq, Hkv, Sq, Sk, D, kv_dtype, units_per_pass);
+}
+
+int fa_standard_attention(const void *q, const void *k, const void *v, void *o, int B, int Hq,
+                          int Hkv, int Sq, int Sk, int D, int causal, int64_t causal_offset,
+                          float scale, int kv_dtype, void *workspace, size_t workspace_bytes,
+                          fa_stream_t stream)
+{
+    fa::AttnArgs a;
+    const int rc = check_attention(q, k, v, o, B, Hq, Hkv, Sq, Sk, D, causal, causal_offset,
+                                   scale, kv_dtype, a);
+    if (rc != FA_OK)
+        return rc;
+    if ((int64_t)B * Sq == 0)
+        return FA_OK;
+    if (fa::standard_max_workgroups(B, Hq, Hkv, Sq, Sk, D, kv_dtype) > kMaxWorkgroups)
+        return FA_ERR_UNSUPPORTED;
+    const size_t need = fa::standard_workspace_bytes(B, Hq, Hkv, Sq, Sk, D, kv_dtype, 1);
+    if (!workspace || workspace_bytes < need)
+        return FA_ERR_WORKSPACE;
+    if (!aligned(workspace, 256))
+        return FA_ERR_ALIGN;
+    return hip_status(fa::launch_standard(a, scale, workspace, workspace_bytes,
+                                          (hipStream_t)stream));
+}
+
 int fa_dequant_q4_0(const void *blocks, int64_t n_blocks, float *out_f32, void *out_f16,
                     fa_stream_t stream)
 {
@@ -425,6 +459,21 @@ int fa_quantize_q4_0(const void *x, int x_dtype, void *blocks, int64_t n_seq,
         return FA_ERR_UNSUPPORTED;
     return hip_status(fa::launch_quantize_q4_0(x, x_dtype, blocks, n_seq, per, x_seq_stride,
                                                blocks_seq_stride, (hipStream_t)stream));
+}
+
+int fa_measure_read(const void *buf, int64_t bytes, uint32_t *sink, uint32_t magic,
+                    int workgroups, fa_stream_t stream)
+{
+    if (bytes < 0 || bytes % 16 || workgroups < 0 || workgroups > (1 << 20))
+        return FA_ERR_SHAPE;
+    if (bytes == 0)
+        return FA_OK;
+    if (!buf || !sink)
+        return FA_ERR_NULL;
+    if (!aligned(buf, 16) || !aligned(sink, 4))
+        return FA_ERR_ALIGN;
+    return hip_status(fa::launch_read(buf, bytes / 16, sink, magic,
+                                      workgroups > 0 ? workgroups : 2048, (hipStream_t)stream));
 }
 
 const char *fa_strerror(int code)

@@ -79,6 +79,19 @@ hipError_t launch_decode(const AttnArgs &a, const DecodeGrid &g, void *workspace
                          hipStream_t stream, const PagedKV *paged = nullptr,
                          int32_t *stats = nullptr);
 
+// Standard (non-flash) attention, the comparison arm (fa_standard.hip): workspace bytes for
+// units_per_pass (b, KV head) units at a time (<= 0: all of them), the largest grid it
+// launches, and the launch (a.k / a.v as fa_prefill; the workspace holds at least one unit).
+size_t standard_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Sk, int D, int kv,
+                                int units_per_pass);
+int64_t standard_max_workgroups(int B, int Hq, int Hkv, int Sq, int Sk, int D, int kv);
+hipError_t launch_standard(const AttnArgs &a, float scale, void *workspace,
+                           size_t workspace_bytes, hipStream_t stream);
+
+// Streaming read of n16 16-byte chunks with `grid` workgroups (fa_measure.hip).
+hipError_t launch_read(const void *buf, int64_t n16, uint32_t *sink, uint32_t magic, int grid,
+                       hipStream_t stream);
+
 hipError_t launch_dequant_q4_0(const void *blocks, int64_t n_blocks, float *out_f32,
                                void *out_f16, hipStream_t stream);
 // src: 0 f32, 1 f16, 2 bf16 (fa_src_dtype)

@@ -208,6 +208,32 @@ int fa_prefill_paged(const void *q, const void *k_pages, const void *v_pages, vo
                      int causal, float scale, int kv_dtype, fa_stream_t stream);
 
 /*
+ * Standard (non-flash) attention, the comparison arm of the mi210-llm-stack page
+ * "FlashAttention on gfx90a" ("Three Patching Approaches", Approach C; "The V Dequantization
+ * Gap"): that page's fast path is the non-FA one, with K dequantized before use and V to be
+ * dequantized the same way. Here, per (b, KV head): a q4_0 K or V is dequantized to f16 (the
+ * routine of fa_dequant_q4_0); S = scale * Q K^T is written to the workspace in f32 for every
+ * tile holding a visible pair; a row softmax over the visible keys writes P = exp(S - max) /
+ * sum in the Q type; O = P V. Every intermediate goes through memory: this is the path the
+ * flash kernels are timed against, not a fast path.
+ * Arguments, layouts, cache types and errors as fa_prefill (any Sq, including decode shapes),
+ * plus the caller-owned workspace:
+ *   workspace   >= fa_standard_workspace_bytes(..., 1) bytes (one (b, KV head) unit at a time),
+ *               256-byte aligned, need not be initialised. With more (up to
+ *               fa_standard_workspace_bytes(..., 0), every unit at once) more units run per
+ *               pass. Per unit it holds Sq * Hq/Hkv rows of S (f32) and P (16-bit) over the
+ *               keys rounded up to 128, plus f16 copies of a q4_0 K or V (B * Sk * Hkv * D * 2
+ *               bytes each). Calls sharing a workspace must be ordered on one stream.
+ * fa_standard_workspace_bytes returns 0 for invalid sizes or an empty call.
+ */
+size_t fa_standard_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Sk, int D, int kv_dtype,
+                                   int units_per_pass);
+int fa_standard_attention(const void *q, const void *k, const void *v, void *o,
+                          int B, int Hq, int Hkv, int Sq, int Sk, int D,
+                          int causal, int64_t causal_offset, float scale, int kv_dtype,
+                          void *workspace, size_t workspace_bytes, fa_stream_t stream);
+
+/*
  * Counter instances, for tests of the deferred rescale (mlxcel PR #2306, "What changed" and
  * "Test plan": the O/l rescale runs only when a row's block maximum outgrows its frame by
  * more than the margin, rarely in the steady state of a chunked prefill, and a score ramp
@@ -278,6 +304,15 @@ enum fa_src_dtype {
 int fa_quantize_q4_0(const void *x, int x_dtype, void *blocks, int64_t n_seq,
                      int64_t rows_per_seq, int D, int64_t x_seq_stride,
                      int64_t blocks_seq_stride, fa_stream_t stream);
+
+/*
+ * Measurement export: a plain streaming read of `bytes` bytes (a multiple of 16) at buf
+ * (16-byte aligned), the HBM read rate the memory-bound decode is compared with. Every thread
+ * folds what it reads into one word; that word is written to *sink only if it equals magic,
+ * so a sink is needed but normally never written. workgroups: grid size (0: 2048).
+ */
+int fa_measure_read(const void *buf, int64_t bytes, uint32_t *sink, uint32_t magic,
+                    int workgroups, fa_stream_t stream);
 
 /* Static text for a status code. */
 const char *fa_strerror(int code);

@@ -392,3 +392,22 @@ def test_stats_entry_points_reject():
               None) == fa.FA_ERR_UNSUPPORTED                             # 8 rows per KV head
     assert dt(P, P, P, P, 4, 8, 2, 1, 4096, 128, 1, 4095, 0.088, 2, P, nbytes, P,
               None) == fa.FA_ERR_UNSUPPORTED                             # Hkv not 4k
+
+
+def test_standard_attention_rejects():
+    sa = fa.fa_standard_attention
+    args = [P, P, P, P, 1, 32, 8, 16, 64, 128, 1, 48, 0.088, 2]
+    need = fa.fa_standard_workspace_bytes(1, 32, 8, 16, 64, 128, 2, 1)
+    allu = fa.fa_standard_workspace_bytes(1, 32, 8, 16, 64, 128, 2, 0)
+    assert 0 < need < allu
+    assert sa(*args, None, need, None) == fa.FA_ERR_WORKSPACE
+    assert sa(*args, P, need - 1, None) == fa.FA_ERR_WORKSPACE
+    assert sa(*args, P + 16, need, None) == fa.FA_ERR_ALIGN             # 256-byte alignment
+    assert sa(P, P, P, P, 1, 30, 8, 16, 64, 128, 1, 48, 0.088, 2, P, need,
+              None) == fa.FA_ERR_SHAPE
+    assert sa(P, P, P, P, 1, 32, 8, 16, 64, 96, 1, 48, 0.088, 2, P, need,
+              None) == fa.FA_ERR_UNSUPPORTED
+    assert sa(P, P, P, P, 1, 32, 8, 0, 64, 128, 1, 48, 0.088, 2, None, 0, None) == fa.FA_OK
+    assert fa.fa_standard_workspace_bytes(1, 32, 8, 0, 64, 128, 2, 0) == 0
+    # f16 caches need no dequantized copies: less workspace than q4_0 at the same shape
+    assert fa.fa_standard_workspace_bytes(1, 32, 8, 16, 64, 128, 0, 1) < need
