@@ -6,8 +6,12 @@
 // +max|x| gives 16, clamped to 15); every code is 8 when d = 0. Byte t of the 16 code bytes holds
 // element t's code (low nibble) and element t + 16's (high nibble).
 //
-// One thread per block: 128 (f32) or 64 bytes in as 16-byte loads, 18 bytes out as 2-byte
-// stores (block starts are only 2-byte aligned). The path is HBM-bound.
+// One thread per block: 128 (f32) or 64 bytes in as 16-byte loads. A wave's 64 consecutive
+// blocks are 1152 contiguous output bytes when they belong to one sequence: they are staged in
+// LDS and written as one run of 16-byte, 4-byte or 2-byte stores (whichever the run's start
+// address allows; block starts are only 2-byte aligned), every store instruction covering
+// consecutive bytes. A wave whose blocks straddle two sequences writes each block's 18 bytes
+// itself. The path is HBM-bound.
 #include "fa_kernels.h"
 #include "fa_device.h"
 
@@ -31,12 +35,32 @@ __device__ __forceinline__ uint32_t q4_code(float x, float d)
     return (uint32_t)min(max(c, 0), 15);
 }
 
+// The same code without a full division per element: with r = RN(1 / d) (one correctly rounded
+// division per block), q0 = RN(x r), the residual e = x - q0 d (exact, one fma) and
+// q1 = RN(q0 + e r) (one fma) is the correctly rounded quotient RN(x / d) (Markstein's
+// theorem on division by a correctly rounded reciprocal, round to nearest). Here x / d stays in
+// [-8.004, 8.004] and d is a positive f16 value, so no step over- or underflows; the argument
+// needs x and q0 d away from the subnormal range, which the exact fallback below covers
+// (|x| < 2^-100: the code is 8 either way unless d is as small, checked by the caller).
+__device__ __forceinline__ uint32_t q4_code_r(float x, float d, float r)
+{
+    const float q0 = x * r;
+    const float e = __builtin_fmaf(-q0, d, x);
+    const float q1 = __builtin_fmaf(e, r, q0);
+    const int c = (int)__builtin_roundf(q1) + 8;
+    return (uint32_t)min(max(c, 0), 15);
+}
+
 template <int SRC>      // 0: f32, 1: f16, 2: bf16
 __global__ __launch_bounds__(256) void quantize_q4_0_kernel(QuantParams p)
 {
-    const int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (id >= p.n_seq * p.blocks_per_seq)
-        return;
+    __shared__ __attribute__((aligned(16))) uint16_t stage[4][64 * 9];   // a wave's 64 blocks
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t total = p.n_seq * p.blocks_per_seq;
+    const int64_t id0 = ((int64_t)blockIdx.x * blockDim.x) + 64 * wave;  // the wave's first block
+    if (id0 >= total)
+        return;                                    // whole wave
+    const int64_t id = min(id0 + lane, total - 1); // lanes past the end redo the last block
     const int64_t s = id / p.blocks_per_seq, j = id % p.blocks_per_seq;
     float v[32];
     if constexpr (SRC == 0) {
@@ -73,16 +97,63 @@ __global__ __launch_bounds__(256) void quantize_q4_0_kernel(QuantParams p)
     const _Float16 dh = (_Float16)(amax * 0.125f);      // exact quotient, then RNE to f16
     const float d = (float)dh;
     uint32_t code4[4] = {0u, 0u, 0u, 0u};
+    if (d >= 0x1p-14f) {                                // a normal f16 scale: no subnormal steps
+        const float r = 1.0f / d;                       // correctly rounded
 #pragma unroll
-    for (int t = 0; t < 16; ++t) {
-        const uint32_t byte = q4_code(v[t], d) | (q4_code(v[t + 16], d) << 4);
-        code4[t / 4] |= byte << (8 * (t % 4));
+        for (int t = 0; t < 16; ++t) {
+            const uint32_t byte = q4_code_r(v[t], d, r) | (q4_code_r(v[t + 16], d, r) << 4);
+            code4[t / 4] |= byte << (8 * (t % 4));
+        }
+    } else {
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+            const uint32_t byte = q4_code(v[t], d) | (q4_code(v[t + 16], d) << 4);
+            code4[t / 4] |= byte << (8 * (t % 4));
+        }
     }
-    uint16_t *dst = (uint16_t *)(p.blocks + s * p.blk_seq_stride + 18 * j);
-    dst[0] = __builtin_bit_cast(uint16_t, dh);
+    uint16_t out[9];
+    out[0] = __builtin_bit_cast(uint16_t, dh);
 #pragma unroll
     for (int m = 0; m < 8; ++m)
-        dst[1 + m] = (uint16_t)(code4[m / 2] >> (16 * (m % 2)));
+        out[1 + m] = (uint16_t)(code4[m / 2] >> (16 * (m % 2)));
+
+    // the wave's blocks [id0, id0 + n): one output run if they lie in one sequence
+    const int n = (int)min((int64_t)64, total - id0);
+    const int64_t s0 = id0 / p.blocks_per_seq, j0 = id0 % p.blocks_per_seq;
+    if (j0 + n > p.blocks_per_seq) {
+        if (id0 + lane < total) {
+            uint16_t *dst = (uint16_t *)(p.blocks + s * p.blk_seq_stride + 18 * j);
+#pragma unroll
+            for (int m = 0; m < 9; ++m)
+                dst[m] = out[m];
+        }
+        return;
+    }
+    uint16_t *st = stage[wave];
+#pragma unroll
+    for (int m = 0; m < 9; ++m)
+        st[9 * lane + m] = out[m];
+    // other lanes' staged bytes are read next: the wave's LDS writes complete first, and the
+    // clobber keeps the compiler from moving the reads above them
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    uint8_t *run = p.blocks + s0 * p.blk_seq_stride + 18 * j0;
+    const int bytes = 18 * n;
+    if (((uintptr_t)run & 15) == 0) {
+        for (int o = 16 * lane; o + 16 <= bytes; o += 16 * 64)
+            *(u32x4 *)(run + o) = *(const u32x4 *)((const uint8_t *)st + o);
+        const int tail = bytes & ~15;               // n odd: the last 2-byte pieces
+        for (int o = tail + 2 * lane; o < bytes; o += 2 * 64)
+            *(uint16_t *)(run + o) = *(const uint16_t *)((const uint8_t *)st + o);
+    } else if (((uintptr_t)run & 3) == 0) {
+        for (int o = 4 * lane; o + 4 <= bytes; o += 4 * 64)
+            *(uint32_t *)(run + o) = *(const uint32_t *)((const uint8_t *)st + o);
+        const int tail = bytes & ~3;
+        for (int o = tail + 2 * lane; o < bytes; o += 2 * 64)
+            *(uint16_t *)(run + o) = *(const uint16_t *)((const uint8_t *)st + o);
+    } else {
+        for (int o = 2 * lane; o < bytes; o += 2 * 64)
+            *(uint16_t *)(run + o) = *(const uint16_t *)((const uint8_t *)st + o);
+    }
 }
 
 }  // namespace

@@ -208,6 +208,48 @@ def test_quantize_q4_0_appends_into_cache():
     assert np.all(host[:, rest] == 0xAB)
 
 
+def test_quantize_q4_0_quotient_rounding():
+    """Elements at and within a few ulps of the half-integer code boundaries x = (k + 1/2) d,
+    for many scales d (every block's first element is 8 d, so its scale is d exactly), from
+    float32 sources: the codes must follow the correctly rounded quotient x / d exactly."""
+    rng = np.random.default_rng(74)
+    n = 40000
+    d16 = rng.integers(0x0400, 0x7800, size=n).astype(np.uint16)       # normal f16 scales
+    d16[:8] = [0x3BFF, 0x37FF, 0x07FF, 0x0400, 0x77FF, 0x3C00, 0x4BFF, 0x13FF]
+    d = d16.view(np.float16).astype(np.float32)
+    k = rng.integers(-8, 8, size=(n, 31)).astype(np.float32)
+    x = ((k + np.float32(0.5)) * d[:, None]).astype(np.float32)
+    ulps = rng.integers(-3, 4, size=(n, 31)).astype(np.int32)
+    x = (x.view(np.int32) + ulps).view(np.float32)                     # nudge by up to 3 ulps
+    x = np.where(np.abs(x) > 7.9 * d[:, None], np.float32(0.25) * d[:, None], x)
+    blocks = np.concatenate([(8 * d)[:, None], x], axis=1).astype(np.float32)
+    say(f"q4_0 writer quotient rounding: {n} blocks")
+    expect = oracle.quantize_q4_0(blocks, "f32")
+    got = fa.quantize_q4_0(torch.from_numpy(blocks).cuda())
+    torch.cuda.synchronize()
+    assert np.array_equal(got.cpu().numpy(), expect)
+
+
+@pytest.mark.parametrize("pos", [1, 2, 8])
+def test_quantize_q4_0_append_alignments(pos):
+    """Appends whose output runs start 2-, 4- and 16-byte aligned (18-byte rows at position pos
+    of a [2, 400, 1, 18-byte] cache; 150 new rows per sequence, so waves both inside one
+    sequence and across two): every written byte as the oracle's, the rest untouched."""
+    B, Smax, S_new, D = 2, 400, 150, 32
+    say(f"q4_0 writer append at position {pos} (run start {18 * pos % 16} mod 16)")
+    x = _writer_blocks(B * S_new, seed=73 + pos).reshape(B, S_new, 1, D)
+    bits = _src_bits(x, "f32")
+    cache = torch.full((B, Smax, 1, 18), 0xCD, dtype=torch.uint8, device="cuda")
+    fa.quantize_q4_0(_src_dev(bits, "f32"), out=cache[:, pos:pos + S_new])
+    torch.cuda.synchronize()
+    host = cache.cpu().numpy()
+    expect = oracle.quantize_q4_0(bits, "f32").reshape(B, S_new, 1, 18)
+    assert np.array_equal(host[:, pos:pos + S_new], expect)
+    rest = np.ones(Smax, bool)
+    rest[pos:pos + S_new] = False
+    assert np.all(host[:, rest] == 0xCD)
+
+
 # ---------------------------------------------------------------------------------------------
 # decode (split-K + log-sum-exp merge)
 # ---------------------------------------------------------------------------------------------
