@@ -21,7 +21,10 @@ import ctypes
 import os
 from typing import Optional
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
+# the library built in this directory; FA_LIBRARY names another build of the same sources (the
+# sanitizer test loads a host-instrumented one this way)
+LIB_PATH = os.environ.get("FA_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                        "libfa.so")
 
 FA_KV_F16, FA_KV_BF16, FA_KV_Q4_0 = 0, 1, 2
 FA_KV_F16_Q4_0, FA_KV_Q4_0_F16 = 3, 4          # mixed caches: (K type, V type)

@@ -61,9 +61,22 @@ def build_info() -> dict:
         return {}
 
 
-def build(verbose: bool = False, extra_flags=()) -> str:
+# host-side AddressSanitizer + UndefinedBehaviorSanitizer (the device code is built as usual):
+# every flag goes after -Xarch_host so that it reaches the host compilation only
+HOST_SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                 "-Xarch_host", "-fno-sanitize-recover=undefined",
+                 "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def build(verbose: bool = False, extra_flags=(), out_path: str = LIB,
+          host_sanitize: bool = False) -> str:
+    """Compile every source and link libfa.so at out_path (default: in-tree). host_sanitize:
+    instrument the host code (the C ABI's checks, the launch planning) with ASan and UBSan; such a
+    build needs the sanitizer runtime preloaded and is for tests only."""
     import json
     hipcc = _hipcc()
+    if host_sanitize:
+        extra_flags = tuple(extra_flags) + tuple(HOST_SANITIZE)
     version = hipcc_version(hipcc)
     tested = TESTED_HIPCC in version
     if verbose:
@@ -89,18 +102,20 @@ def build(verbose: bool = False, extra_flags=()) -> str:
         with concurrent.futures.ThreadPoolExecutor(max_workers=min(4, len(SOURCES))) as ex:
             objs = list(ex.map(compile_one, SOURCES))
         out = os.path.join(tmp, "libfa.so")
+        # (a host-sanitized build leaves the sanitizer runtime's symbols to the preloaded runtime)
         cmd = [hipcc, "-shared", f"--offload-arch={ARCH}", *objs, "-o", out]
         r = subprocess.run(cmd, capture_output=True, text=True)
         if r.returncode != 0:
             raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{_quiet(r.stdout + r.stderr)}")
-        shutil.copyfile(out, LIB + ".tmp")
-        os.replace(LIB + ".tmp", LIB)
-    with open(BUILD_INFO, "w") as f:
-        json.dump({"hipcc_version": version, "tested_compiler": tested, "arch": ARCH,
-                   "flags": COMMON + list(extra_flags)}, f)
+        shutil.copyfile(out, out_path + ".tmp")
+        os.replace(out_path + ".tmp", out_path)
+    if out_path == LIB:
+        with open(BUILD_INFO, "w") as f:
+            json.dump({"hipcc_version": version, "tested_compiler": tested, "arch": ARCH,
+                       "flags": COMMON + list(extra_flags)}, f)
     if verbose:
-        print(f"built {LIB}", flush=True)
-    return LIB
+        print(f"built {out_path}", flush=True)
+    return out_path
 
 
 if __name__ == "__main__":

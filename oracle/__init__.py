@@ -172,12 +172,16 @@ _default: Optional[Oracle] = None
 
 
 def default() -> Oracle:
-    """The oracle built from fa_oracle.c (built on first use if no build exists)."""
+    """The oracle built from fa_oracle.c (built on first use if no build exists); FA_ORACLE_LIB
+    names another build of it (the sanitizer test loads an instrumented one this way)."""
     global _default
     if _default is None:
-        if not os.path.exists(_build.LIB):
-            _build.build()
-        _default = Oracle(_build.LIB)
+        path = os.environ.get("FA_ORACLE_LIB")
+        if not path:
+            if not os.path.exists(_build.LIB):
+                _build.build()
+            path = _build.LIB
+        _default = Oracle(path)
     return _default
 
 
