@@ -46,10 +46,13 @@ constexpr int kPrefillMaxPages = 4096;
 // partial rows. n_main: workgroups (one per unit); n_tail: split units, 0 when nothing splits
 // (plain prefill).
 constexpr size_t kSplitCounterBytes = 4096;
+// parts > 0: the key split for shapes with few units (each unit's tiles cut into `parts` runs,
+// one workgroup each, n_main = units x parts; a merge kernel follows); 0: the pairing above.
 struct PrefillSplit {
     int q_split, cap;
     int64_t n_main, n_tail;
     size_t workspace_bytes;
+    int parts;
 };
 PrefillSplit prefill_split_plan(const AttnArgs &a);
 hipError_t launch_prefill_split(const AttnArgs &a, const PrefillSplit &sp, void *workspace,

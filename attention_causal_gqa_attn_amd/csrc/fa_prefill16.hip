@@ -62,6 +62,10 @@ struct Prefill16Params {
     int q_split, cap, n_main, n_tail;
     uint32_t *cnt;     // arrival counters, one per split unit, zero between calls
     float *part;       // partial rows [split unit][part][wave][64 rows][kPartRow floats]
+    // key split (SPLIT instances with parts > 0, for shapes with few units): every unit's tiles
+    // are cut into `parts` runs, one workgroup each; each writes its partial rows to
+    // part[unit][run][wave][64 rows][kPartRow] and prefill_parts_merge_kernel combines them
+    int parts;
     // STATS instances: per query row (b, i, h), two int32 counters written in the epilogue:
     // how many times the row's softmax frame moved (the deferred-rescale test fired for the
     // row, counting the first frame), and in how many tiles its wave block ran the O rescale
@@ -403,6 +407,14 @@ __global__ __launch_bounds__(kNT, 1) void prefill16_kernel(Prefill16Params p)
 
     // ---- which (b, kv head, head chunk, query block) this workgroup owns -------------------
     int rest = xcd_remap(blockIdx.x, gridDim.x);
+    int run_id = 0;                       // key split: this workgroup's run of its unit's tiles
+    if constexpr (SPLIT) {
+        if (p.parts > 0) {
+            run_id = rest % p.parts;
+            rest /= p.parts;
+        }
+    }
+    const int unit_id = rest;             // ((b * Hkv + kvh) * n_hchunk + hc) * n_qblk + qbl
     const int qbl = rest % p.n_qblk;
     rest /= p.n_qblk;
     const int hc = rest % p.n_hchunk;
@@ -444,6 +456,13 @@ __global__ __launch_bounds__(kNT, 1) void prefill16_kernel(Prefill16Params p)
     const int nb_unit = (int)((kend + kBN - 1) / kBN);
     int t0 = 0, nb = nb_unit;
     const bool split_unit = SPLIT && qblk >= p.q_split;
+    if constexpr (SPLIT) {
+        if (p.parts > 0) {
+            const int per = (nb_unit + p.parts - 1) / p.parts;
+            t0 = run_id * per;
+            nb = max(min(per, nb_unit - t0), 0);
+        }
+    }
     if (split_unit) {
         if (part == 0) {
             nb = min(nb_unit, p.cap);
@@ -976,6 +995,36 @@ __global__ __launch_bounds__(kNT, 1) void prefill16_kernel(Prefill16Params p)
 
     // ---- epilogue ----------------------------------------------------------------------------
     if constexpr (SPLIT) {
+        if (p.parts > 0) {
+            // key split: this run's rows (unnormalised O, frame, sum) go to the workspace as
+            // contiguous runs through LDS (the tile rings, free after the last tile), for the
+            // merge kernel that follows
+            static_assert(LDSB >= kNW * 32 * kPartRow * 4, "staging fits the tile rings");
+            constexpr int RUN = 32 * kPartRow;
+            float *mine = p.part + (((int64_t)unit_id * p.parts + run_id) * kNW + wave) *
+                                       (int64_t)(2 * RUN);
+            float *stg = (float *)lds + wave * RUN;
+            float *row = stg + col * kPartRow;
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const float ltot = pair_sum(lsum[j]);
+                __syncthreads();
+#pragma unroll
+                for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+                    for (int ii = 0; ii < 4; ++ii)
+                        *(f32x4 *)(row + 32 * dt + 8 * ii + 4 * half) =
+                            f32x4{acc[j][dt][4 * ii + 0], acc[j][dt][4 * ii + 1],
+                                  acc[j][dt][4 * ii + 2], acc[j][dt][4 * ii + 3]};
+                if (half == 0)
+                    *(f32x2 *)(row + D) = f32x2{frame[j], ltot};
+                __syncthreads();
+#pragma unroll
+                for (int e = 4 * lane; e < RUN; e += 256)
+                    *(f32x4 *)(mine + j * RUN + e) = *(const f32x4 *)(stg + e);
+            }
+            return;
+        }
         if (split_unit) {
             // This part's rows (unnormalised O, frame, sum) go to the workspace; the later of
             // the unit's two parts merges them: F = max f, O = sum 2^(f - F) O_f / sum 2^(f - F)
@@ -1085,6 +1134,63 @@ __global__ __launch_bounds__(kNT, 1) void prefill16_kernel(Prefill16Params p)
     }
 }
 
+// Key split: combine the runs of each unit's rows. One workgroup per (unit, wave): thread t
+// takes row t / 4 of the wave's 64 and a quarter of its D outputs; with the runs' frames f_r and
+// sums l_r, F = max f_r and O = sum 2^(f_r - F) O_r / sum 2^(f_r - F) l_r (a run that saw no key
+// has f_r = -inf and weight 0; a row no run saw gets O = 0).
+template <int D, bool BF>
+__global__ __launch_bounds__(256) void prefill_parts_merge_kernel(Prefill16Params p)
+{
+    constexpr int RUN = 32 * kPartRow, QD = D / 4;
+    const AttnArgs &a = p.a;
+    const int wave = blockIdx.x % kNW, unit_id = blockIdx.x / kNW;
+    int rest = unit_id;
+    const int qbl = rest % p.n_qblk;
+    rest /= p.n_qblk;
+    const int hc = rest % p.n_hchunk;
+    rest /= p.n_hchunk;
+    const int kvh = rest % a.Hkv;
+    const int b = rest / a.Hkv;
+    const int qblk = a.causal ? p.n_qblk - 1 - qbl : qbl;
+    const int hs = wave % p.hpw, qs = wave / p.hpw;
+    const int hl = hc * p.hpw + hs;
+    const int q0 = qblk * kQW * p.qsub + qs * kQW;
+    if (wave >= p.hpw * p.qsub || hl >= a.G || q0 >= a.Sq)
+        return;                                      // a wave slot with no rows
+    const int h = kvh * a.G + hl;
+    const int r = threadIdx.x >> 2, qd = threadIdx.x & 3;
+    const int qi = q0 + r;                           // row r: block r / 32, column r % 32
+    if (qi >= a.Sq)
+        return;
+    const float *base = p.part + (int64_t)unit_id * p.parts * kNW * 2 * RUN +
+                        (int64_t)wave * 2 * RUN + (r >> 5) * RUN + (r & 31) * kPartRow;
+    const int64_t rstride = (int64_t)kNW * 2 * RUN;  // between runs of the unit
+    float F = -INFINITY;
+    for (int k = 0; k < p.parts; ++k)
+        F = fmaxf(F, base[k * rstride + D]);
+    float L = 0.0f;
+    f32x4 o[QD / 4];
+#pragma unroll
+    for (int e = 0; e < QD / 4; ++e)
+        o[e] = (f32x4){};
+    if (F != -INFINITY) {
+        for (int k = 0; k < p.parts; ++k) {
+            const float *src = base + k * rstride;
+            const float w = exp2_fast(src[D] - F);
+            L += w * src[D + 1];
+#pragma unroll
+            for (int e = 0; e < QD / 4; ++e)
+                o[e] += w * *(const f32x4 *)(src + qd * QD + 4 * e);
+        }
+    }
+    const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+    uint16_t *op = (uint16_t *)a.o + (((int64_t)b * a.Sq + qi) * a.Hq + h) * D + qd * QD;
+#pragma unroll
+    for (int e = 0; e < QD / 4; ++e)
+        *(u32x2 *)(op + 4 * e) = (u32x2){pack2<BF>(o[e][0] * inv, o[e][1] * inv),
+                                         pack2<BF>(o[e][2] * inv, o[e][3] * inv)};
+}
+
 template <int D, int KT, int VT>
 hipError_t launch16(const Prefill16Params &p, int64_t n_wg, hipStream_t stream)
 {
@@ -1094,6 +1200,14 @@ hipError_t launch16(const Prefill16Params &p, int64_t n_wg, hipStream_t stream)
         if (p.cnt) {
             hipLaunchKernelGGL((prefill16_kernel<D, KT, VT, false, true>),
                                dim3((unsigned)p.n_main), dim3(kNT), 0, stream, p);
+            if (p.parts > 0) {
+                const hipError_t e = hipGetLastError();
+                if (e != hipSuccess)
+                    return e;
+                hipLaunchKernelGGL((prefill_parts_merge_kernel<D, KT == KV_BF16>),
+                                   dim3((unsigned)(p.n_main / p.parts * kNW)), dim3(256), 0,
+                                   stream, p);
+            }
             return hipGetLastError();
         }
     }
@@ -1144,25 +1258,51 @@ hipError_t launch16_kv(const Prefill16Params &p, int64_t n_wg, hipStream_t strea
 // on the box at 2K, 8K and 16K keys, biases 0-6: 3 was best (4 close, 0 and 6 worst).
 constexpr int kSplitBias = 3;
 
+// Key split: when the units are few (a short chunk of queries against many keys, where each
+// workgroup would run its unit's tiles alone while most CUs idle), every unit's tiles are cut
+// into `parts` runs of at least kMinRunTiles tiles, enough for about kPartsTarget workgroups,
+// merged by a second kernel.
+constexpr int64_t kFewUnits = 128;
+constexpr int64_t kPartsTarget = 512;
+constexpr int64_t kMinRunTiles = 4;
+constexpr int64_t kMaxParts = 64;
+
 PrefillSplit prefill_split_plan(const AttnArgs &a)
 {
     PrefillSplit sp{};
     const int kv = a.kv;
     const bool q4 = kv == KV_Q4_0 || kv == KV_F16_Q4_0 || kv == KV_Q4_0_F16;
-    if (!a.causal || (q4 && a.D != 128) || (int64_t)a.B * a.Sq == 0)
+    if ((q4 && a.D != 128) || (int64_t)a.B * a.Sq == 0)
         return sp;
     const PrefillGrid g = prefill16_grid(a);
     const int bmq = kQW * g.qsub;
     auto tiles = [&](int qblk) -> int64_t {
         const int64_t qlast = std::min((int64_t)qblk * bmq + bmq, (int64_t)a.Sq) - 1;
-        int64_t kend = std::min((int64_t)a.Sk, qlast + a.offset + 1);
+        int64_t kend = a.causal ? std::min((int64_t)a.Sk, qlast + a.offset + 1) : (int64_t)a.Sk;
         kend = kend < 0 ? 0 : kend;
         return (kend + kBN - 1) / kBN;
     };
+    const int64_t per = (int64_t)g.n_hchunk * a.Hkv * a.B;       // units per query block
+    const int64_t n_units = (int64_t)g.n_qblk * per;
+    const int64_t t_max = tiles(a.causal ? g.n_qblk - 1 : 0);
+    const size_t unit_part_bytes = (size_t)kNW * kQW * kPartRow * 4;   // one run of one unit
+    if (n_units < kFewUnits) {
+        int64_t parts = (kPartsTarget + n_units - 1) / n_units;
+        parts = std::min(parts, std::min(kMaxParts, t_max / kMinRunTiles));
+        if (parts >= 2) {
+            sp.parts = (int)parts;
+            sp.q_split = g.n_qblk;                               // no unit is paired
+            sp.n_main = n_units * parts;
+            sp.n_tail = n_units;
+            sp.workspace_bytes = kSplitCounterBytes + (size_t)(n_units * parts) * unit_part_bytes;
+            return sp;
+        }
+    }
+    if (!a.causal)
+        return sp;
     int64_t total = 0;
     for (int q = 0; q < g.n_qblk; ++q)
         total += tiles(q);
-    const int64_t per = (int64_t)g.n_hchunk * a.Hkv * a.B;       // units per query block
     const int64_t cap = (total + g.n_qblk - 1) / g.n_qblk + kSplitBias;
     int q_split = g.n_qblk;
     while (q_split > 0 && tiles(q_split - 1) > cap)              // tiles grow with the block
@@ -1175,7 +1315,7 @@ PrefillSplit prefill_split_plan(const AttnArgs &a)
     sp.cap = (int)cap;
     sp.n_main = (int64_t)g.n_qblk * per;
     sp.n_tail = n_split;
-    sp.workspace_bytes = kSplitCounterBytes + (size_t)n_split * 2 * kNW * kQW * kPartRow * 4;
+    sp.workspace_bytes = kSplitCounterBytes + (size_t)n_split * 2 * unit_part_bytes;
     return sp;
 }
 
@@ -1214,6 +1354,7 @@ hipError_t launch_prefill_split(const AttnArgs &a, const PrefillSplit &sp, void 
     p.cap = sp.cap;
     p.n_main = (int)sp.n_main;
     p.n_tail = (int)sp.n_tail;
+    p.parts = sp.parts;
     p.cnt = (uint32_t *)workspace;
     p.part = (float *)((uint8_t *)workspace + kSplitCounterBytes);
     return a.D == 128 ? launch16_kv<128>(p, g.n_wg, stream) : launch16_kv<64>(p, g.n_wg, stream);

@@ -60,11 +60,15 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_16k_f16_traffic.txt")
 DECODE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_q4_0_traffic.txt")
 MFMA_UTIL_FILE = os.path.join(ROOT, "profiles", "prefill_16k_mfma_util.txt")
 CLOCK_WARMUP_S = 0.25
-# the chunked-prefill configuration's other key counts, dtypes and the score ramp
+# the chunked-prefill configuration's other key counts, dtypes and the score ramp, and a short
+# chunk of 256 queries against 16384 keys
 SWEEP = ["prefill_2k_f16", "prefill_8k_f16", "prefill_2k_bf16", "prefill_8k_bf16",
-         "prefill_16k_bf16", "prefill_16k_f16_ramp", "prefill_16k_bf16_ramp"]
-# the balanced causal prefill (fa_prefill_split) beside fa_prefill at these shapes
-SWEEP_SPLIT = ["prefill_16k_f16", "prefill_2k_f16", "prefill_8k_f16", "prefill_16k_q4_0"]
+         "prefill_16k_bf16", "prefill_16k_f16_ramp", "prefill_16k_bf16_ramp",
+         "chunk256_16k_f16", "chunk256_16k_q4_0"]
+# the balanced causal prefill (fa_prefill_split) beside fa_prefill at these shapes (the 256-query
+# chunks take its key split)
+SWEEP_SPLIT = ["prefill_16k_f16", "prefill_2k_f16", "prefill_8k_f16", "prefill_16k_q4_0",
+               "chunk256_16k_f16", "chunk256_16k_q4_0"]
 
 
 def source_hash() -> str:

@@ -101,6 +101,11 @@ int fa_prefill(const void *q, const void *k, const void *v, void *o,
  * stays one workgroup per unit. The later of a split unit's two parts to finish merges them
  * (log-sum-exp of the two partial softmax states) and writes the unit's rows. No workgroup
  * waits for another.
+ * With fewer than 128 units (a short chunk of queries against many keys, or a small batch),
+ * most CUs would idle while each unit's workgroup runs all of its tiles, so instead every
+ * unit's tiles are cut into up to 64 runs of at least 4 tiles (about 512 workgroups in all),
+ * each run writes its partial softmax state to the workspace, and a second kernel merges the
+ * runs of every row (the same log-sum-exp combine). The arrival counters are not used then.
  * Arguments as fa_prefill, plus the caller-owned workspace:
  *   workspace   >= fa_prefill_workspace_bytes(...) bytes, 16-byte aligned. Its first 4096
  *               bytes are arrival counters that must be zero before the first call that uses
@@ -109,10 +114,10 @@ int fa_prefill(const void *q, const void *k, const void *v, void *o,
  *               call without clearing. The rest holds the split units' partial rows. Non-zero
  *               counter bytes give wrong output rows, never an access outside the workspace.
  *               Calls that share a workspace must be ordered on one stream.
- * Contiguous caches split (a cache type with a q4_0 tensor at D = 128 only); for paged
- * caches, non-causal calls, or shapes with nothing to split (fa_prefill_workspace_bytes
- * returns 0) the call is fa_prefill and the workspace may be NULL. Errors as fa_prefill, plus
- * FA_ERR_WORKSPACE.
+ * Contiguous caches split (a cache type with a q4_0 tensor at D = 128 only); non-causal calls
+ * only by the key split. For paged caches, or shapes with nothing to split
+ * (fa_prefill_workspace_bytes returns 0) the call is fa_prefill and the workspace may be NULL.
+ * Errors as fa_prefill, plus FA_ERR_WORKSPACE.
  */
 size_t fa_prefill_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Sk, int D, int causal,
                                   int64_t causal_offset, int kv_dtype);

@@ -658,7 +658,7 @@ SPLIT_SMALL = [
     # GQA 4 with a ragged query tail, a chunk at the end of longer keys, two sequences
     wl("split_gqa_ragged", 2, 16, 4, 900, 1600, 128, "f16", True, 700, seed=91),
     wl("split_bf16_d64", 1, 8, 2, 640, 640, 64, "bf16", True, 0, seed=92),
-    # one KV head: 24 query blocks, the heaviest ones split with their mirrors
+    # one KV head: 24 units, few enough that every unit's keys are cut into runs
     wl("split_one_head", 1, 4, 1, 1500, 1500, 128, "f16", True, 0, seed=93),
     # queries before the keys: early rows see nothing
     wl("split_negative_offset", 1, 8, 2, 1200, 1000, 128, "f16", True, -100, seed=94),
@@ -667,6 +667,9 @@ SPLIT_SMALL = [
     wl("split_gqa8", 1, 16, 2, 1000, 1000, 128, "bf16", True, 0, seed=96),
     # q4_0 cache (D = 128): the raw rings and in-kernel dequantization over offset tiles
     wl("split_q4_0", 1, 16, 4, 1100, 1700, 128, "q4_0", True, 600, seed=100),
+    # 128 units (GQA 2, two sequences): heavy units paired with their mirrors
+    wl("split_pair_gqa2", 2, 16, 8, 1024, 1024, 128, "f16", True, 0, seed=103),
+    wl("split_pair_q4_0", 2, 16, 8, 1024, 1500, 128, "q4_0", True, 476, seed=104),
 ]
 
 
@@ -679,6 +682,43 @@ def test_prefill_split_matches_oracle(w):
     x = W.generate(w)
     compare(w, gpu_prefill_split(w, x).reshape(-1, w.D), oracle_out(w, x).reshape(-1, w.D),
             w.name)
+
+
+# key split (fewer than 128 units): a short chunk of queries against many keys; every unit's
+# tiles are cut into runs of their own workgroups and a merge kernel combines them
+SPLIT_PARTS = [
+    wl("parts_chunk64_16k", 1, 32, 8, 64, 16384, 128, "f16", True, None, seed=105),
+    wl("parts_chunk300_bf16", 1, 32, 8, 300, 5000, 128, "bf16", True, None, seed=106),
+    wl("parts_chunk128_q4_0", 1, 32, 8, 128, 8000, 128, "q4_0", True, None, seed=107),
+    wl("parts_noncausal_d64", 2, 8, 2, 40, 3000, 64, "f16", False, 0, seed=108),
+    wl("parts_before_keys", 1, 8, 2, 512, 3000, 128, "f16", True, -50, seed=109),
+    wl("parts_mha", 1, 4, 4, 96, 6000, 128, "bf16", True, None, seed=110),
+    wl("parts_d64_bf16_ragged", 1, 16, 4, 77, 2333, 64, "bf16", True, None, seed=111),
+]
+
+
+@pytest.mark.parametrize("w", SPLIT_PARTS, ids=[w.name for w in SPLIT_PARTS])
+def test_prefill_split_parts_matches_oracle(w):
+    say(f"prefill_split, key split {w}")
+    assert fa.fa_prefill_workspace_bytes(w.B, w.Hq, w.Hkv, w.Sq, w.Sk, w.D, int(w.causal),
+                                         w.causal_offset, w.kv_code) > 4096
+    x = inputs(w)
+    got = gpu_prefill_split(w, x).reshape(-1, w.D)
+    compare(w, got, oracle_full(w), w.name)
+    compare(w, got, gpu_prefill(w, x).reshape(-1, w.D), w.name + " vs fa_prefill")
+
+
+def test_prefill_split_parts_mixed_matches_oracle():
+    for kt, vt in (("f16", "q4_0"), ("q4_0", "f16")):
+        w = wl(f"parts_mixed_{kt}_{vt}", 1, 32, 8, 100, 4000, 128, "f16", True, None, seed=112)
+        say(f"prefill_split, key split, mixed caches {kt}/{vt}")
+        q, k, v = _mixed(w, kt, vt)
+        got = fa.prefill_split(to_dev(q, "f16"), to_dev(k, kt), to_dev(v, vt), causal=True,
+                               offset=w.causal_offset, scale=w.scale)
+        torch.cuda.synchronize()
+        err = float(np.max(np.abs(got.float().cpu().numpy() - _mixed_oracle(w, q, k, v, kt, vt))))
+        say(f"  max|err| = {err:.3e}")
+        assert err <= TOL["q4_0"], (kt, vt, err)
 
 
 def test_prefill_split_nothing_to_split():

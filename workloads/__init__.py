@@ -106,6 +106,9 @@ WORKLOADS = {w.name: w for w in [
     Workload("decode_q4_0", B=4, Hq=32, Hkv=8, Sq=1, Sk=32768, D=128, kv="q4_0", seed=4),
     # chunked prefill against a q4_0 cache
     _prefill("prefill_16k_q4_0", 16384, "q4_0", 5),
+    # a short chunk (256 queries) at the end of 16384 keys: few (b, KV head, query block) units
+    Workload("chunk256_16k_f16", B=1, Hq=32, Hkv=8, Sq=256, Sk=16384, D=128, seed=6),
+    Workload("chunk256_16k_q4_0", B=1, Hq=32, Hkv=8, Sq=256, Sk=16384, D=128, kv="q4_0", seed=7),
 ]}
 
 
