@@ -53,6 +53,10 @@ struct PrefillSplit {
     int64_t n_main, n_tail;
     size_t workspace_bytes;
     int parts;
+    // q4_0 tensors widened to f16 in the workspace first (bit 0: K, bit 1: V), each copy
+    // deq_bytes long, the first at deq_off; the split then runs on the 16-bit copies
+    int deq;
+    size_t deq_off, deq_bytes;
 };
 PrefillSplit prefill_split_plan(const AttnArgs &a);
 hipError_t launch_prefill_split(const AttnArgs &a, const PrefillSplit &sp, void *workspace,

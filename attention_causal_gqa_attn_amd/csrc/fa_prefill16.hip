@@ -1258,23 +1258,54 @@ hipError_t launch16_kv(const Prefill16Params &p, int64_t n_wg, hipStream_t strea
 // on the box at 2K, 8K and 16K keys, biases 0-6: 3 was best (4 close, 0 and 6 worst).
 constexpr int kSplitBias = 3;
 
-// Key split: when the units are few (a short chunk of queries against many keys, where each
-// workgroup would run its unit's tiles alone while most CUs idle), every unit's tiles are cut
-// into `parts` runs of at least kMinRunTiles tiles, enough for about kPartsTarget workgroups,
-// merged by a second kernel.
-constexpr int64_t kFewUnits = 128;
-constexpr int64_t kPartsTarget = 512;
+// Key split: when the units are at most half the CUs (a short chunk of queries against many
+// keys, where each workgroup would run its unit's tiles alone while most CUs idle), every
+// unit's tiles are cut into `parts` runs of at least kMinRunTiles tiles, as many as fill the
+// kCUs CUs in one round (parts = kCUs / units), merged by a second kernel. Timed on the box at
+// 8-128 units and 2K-16K keys against runs sized for two or four rounds (512 or 1024
+// workgroups): one round was fastest at every shape (e.g. 1024 queries x 16K keys: 267 us
+// against 278 and 307; 64 queries: 78 against 130). With more units than that, pairing.
+constexpr int64_t kCUs = 256;          // compute units of the gfx950 part (MI355X)
 constexpr int64_t kMinRunTiles = 4;
 constexpr int64_t kMaxParts = 64;
 
-PrefillSplit prefill_split_plan(const AttnArgs &a)
+// Dequantize first: the fused kernel dequantizes a q4_0 tile in every workgroup that reads it,
+// once per query block and head chunk of its KV head; widening the cache to f16 once costs a
+// pass over it. Timed at 16K keys, GQA 32/8 (fa_prefill_split both ways, same box): 64-256
+// queries (1-4 blocks) fused faster (118-135 us against 138-161), 512 (8) even, 1024 (16) and
+// more the dequantized copy faster. Output bits are the same either way (one unpack routine).
+constexpr int64_t kDequantFirstBlocks = 16;
+
+PrefillSplit prefill_split_plan(const AttnArgs &a0)
 {
     PrefillSplit sp{};
-    const int kv = a.kv;
-    const bool q4 = kv == KV_Q4_0 || kv == KV_F16_Q4_0 || kv == KV_Q4_0_F16;
-    if ((q4 && a.D != 128) || (int64_t)a.B * a.Sq == 0)
+    if ((int64_t)a0.B * a0.Sq == 0)
         return sp;
-    const PrefillGrid g = prefill16_grid(a);
+    const PrefillGrid g = prefill16_grid(a0);
+    AttnArgs a = a0;
+    const bool qk = a0.kv == KV_Q4_0 || a0.kv == KV_Q4_0_F16;
+    const bool qv = a0.kv == KV_Q4_0 || a0.kv == KV_F16_Q4_0;
+    const int64_t n_blocks = (int64_t)a0.B * a0.Sk * a0.Hkv * (a0.D / 32);
+    if ((qk || qv) && (int64_t)g.n_qblk * g.n_hchunk >= kDequantFirstBlocks &&
+        n_blocks / 256 < INT32_MAX) {                             // the dequant grid fits
+
+        sp.deq = (qk ? 1 : 0) | (qv ? 2 : 0);
+        sp.deq_bytes = (size_t)a0.B * a0.Sk * a0.Hkv * a0.D * 2;
+        a.kv = KV_F16;
+    }
+    // the workspace: arrival counters and partial rows, then any f16 copies (after the counter
+    // bytes even when nothing is split, so a later call that shares the workspace finds its
+    // counters at zero)
+    auto finish = [&](PrefillSplit s) {
+        if (s.deq) {
+            s.deq_off = (std::max(s.workspace_bytes, kSplitCounterBytes) + 255) & ~(size_t)255;
+            s.workspace_bytes = s.deq_off + (size_t)((s.deq & 1) + (s.deq >> 1)) * s.deq_bytes;
+        }
+        return s;
+    };
+    const bool q4 = a.kv == KV_Q4_0 || a.kv == KV_F16_Q4_0 || a.kv == KV_Q4_0_F16;
+    if (q4 && a.D != 128)
+        return finish(sp);
     const int bmq = kQW * g.qsub;
     auto tiles = [&](int qblk) -> int64_t {
         const int64_t qlast = std::min((int64_t)qblk * bmq + bmq, (int64_t)a.Sq) - 1;
@@ -1286,20 +1317,19 @@ PrefillSplit prefill_split_plan(const AttnArgs &a)
     const int64_t n_units = (int64_t)g.n_qblk * per;
     const int64_t t_max = tiles(a.causal ? g.n_qblk - 1 : 0);
     const size_t unit_part_bytes = (size_t)kNW * kQW * kPartRow * 4;   // one run of one unit
-    if (n_units < kFewUnits) {
-        int64_t parts = (kPartsTarget + n_units - 1) / n_units;
-        parts = std::min(parts, std::min(kMaxParts, t_max / kMinRunTiles));
+    {
+        const int64_t parts = std::min(kCUs / n_units, std::min(kMaxParts, t_max / kMinRunTiles));
         if (parts >= 2) {
             sp.parts = (int)parts;
             sp.q_split = g.n_qblk;                               // no unit is paired
             sp.n_main = n_units * parts;
             sp.n_tail = n_units;
             sp.workspace_bytes = kSplitCounterBytes + (size_t)(n_units * parts) * unit_part_bytes;
-            return sp;
+            return finish(sp);
         }
     }
     if (!a.causal)
-        return sp;
+        return finish(sp);
     int64_t total = 0;
     for (int q = 0; q < g.n_qblk; ++q)
         total += tiles(q);
@@ -1310,13 +1340,13 @@ PrefillSplit prefill_split_plan(const AttnArgs &a)
     q_split = std::max(q_split, (g.n_qblk + 1) / 2);             // every split unit's mirror is light
     const int64_t n_split = (int64_t)(g.n_qblk - q_split) * per;
     if (n_split == 0 || n_split * sizeof(uint32_t) > kSplitCounterBytes || cap < 1)
-        return sp;
+        return finish(sp);
     sp.q_split = q_split;
     sp.cap = (int)cap;
     sp.n_main = (int64_t)g.n_qblk * per;
     sp.n_tail = n_split;
     sp.workspace_bytes = kSplitCounterBytes + (size_t)n_split * 2 * unit_part_bytes;
-    return sp;
+    return finish(sp);
 }
 
 PrefillGrid prefill16_grid(const AttnArgs &a)
@@ -1341,12 +1371,32 @@ hipError_t launch_prefill(const AttnArgs &a, hipStream_t stream, const PagedKV *
     return g.n_wg == 0 ? hipSuccess : launch_prefill16(a, g, stream, paged, q_lens, stats);
 }
 
-hipError_t launch_prefill_split(const AttnArgs &a, const PrefillSplit &sp, void *workspace,
+hipError_t launch_prefill_split(const AttnArgs &a0, const PrefillSplit &sp, void *workspace,
                                 hipStream_t stream)
 {
-    const PrefillGrid g = prefill16_grid(a);
+    const PrefillGrid g = prefill16_grid(a0);
     if (g.n_wg == 0)
         return hipSuccess;
+    AttnArgs a = a0;
+    if (sp.deq) {
+        // widen the q4_0 tensors into the workspace, then run the 16-bit kernel on the copies
+        uint8_t *copy = (uint8_t *)workspace + sp.deq_off;
+        const int64_t n_blocks = (int64_t)a0.B * a0.Sk * a0.Hkv * (a0.D / 32);
+        if (sp.deq & 1) {
+            const hipError_t e = launch_dequant_q4_0(a0.k, n_blocks, nullptr, copy, stream);
+            if (e != hipSuccess)
+                return e;
+            a.k = copy;
+            copy += sp.deq_bytes;
+        }
+        if (sp.deq & 2) {
+            const hipError_t e = launch_dequant_q4_0(a0.v, n_blocks, nullptr, copy, stream);
+            if (e != hipSuccess)
+                return e;
+            a.v = copy;
+        }
+        a.kv = KV_F16;
+    }
     if (sp.n_tail == 0)
         return launch_prefill16(a, g, stream);
     Prefill16Params p{a, g.hpw, g.qsub, g.n_qblk, g.n_hchunk, nullptr, nullptr, nullptr, 0, 0};

@@ -101,21 +101,28 @@ int fa_prefill(const void *q, const void *k, const void *v, void *o,
  * stays one workgroup per unit. The later of a split unit's two parts to finish merges them
  * (log-sum-exp of the two partial softmax states) and writes the unit's rows. No workgroup
  * waits for another.
- * With fewer than 128 units (a short chunk of queries against many keys, or a small batch),
- * most CUs would idle while each unit's workgroup runs all of its tiles, so instead every
- * unit's tiles are cut into up to 64 runs of at least 4 tiles (about 512 workgroups in all),
- * each run writes its partial softmax state to the workspace, and a second kernel merges the
- * runs of every row (the same log-sum-exp combine). The arrival counters are not used then.
+ * With at most 128 units, half the 256 CUs (a short chunk of queries against many keys, or a
+ * small batch), most CUs would idle while each unit's workgroup runs all of its tiles, so
+ * instead every unit's tiles are cut into runs of at least 4 tiles, as many runs per unit as
+ * fill the 256 CUs once (at most 64), each run writes its partial softmax state to the
+ * workspace, and a second kernel merges the runs of every row (the same log-sum-exp combine).
+ * The arrival counters are not used then.
+ * A cache with a q4_0 tensor whose KV heads each have 16 or more 64-row query blocks (for GQA
+ * 4, 1024 or more queries) is first widened to f16 in the workspace (the q4_0 tensor or both,
+ * with the routine fa_dequant_q4_0 runs), and the split runs on the copies: the in-kernel
+ * dequantization is repeated by every query block that reads a tile, one pass over the cache
+ * costs less there. The output bits are those of the fused kernel.
  * Arguments as fa_prefill, plus the caller-owned workspace:
  *   workspace   >= fa_prefill_workspace_bytes(...) bytes, 16-byte aligned. Its first 4096
  *               bytes are arrival counters that must be zero before the first call that uses
  *               the workspace (allocate it zero-filled, or clear it once); every call returns
  *               them to zero when it completes, so the workspace can be reused for any later
- *               call without clearing. The rest holds the split units' partial rows. Non-zero
- *               counter bytes give wrong output rows, never an access outside the workspace.
+ *               call without clearing. The rest holds the split units' partial rows, then any
+ *               f16 copies of the cache (B * Sk * Hkv * D * 2 bytes each). Non-zero counter
+ *               bytes give wrong output rows, never an access outside the workspace.
  *               Calls that share a workspace must be ordered on one stream.
- * Contiguous caches split (a cache type with a q4_0 tensor at D = 128 only); non-causal calls
- * only by the key split. For paged caches, or shapes with nothing to split
+ * Contiguous caches only. A q4_0 tensor at D = 64 splits only through its f16 copy; non-causal
+ * calls only by the key split. For shapes with nothing to split and no copy
  * (fa_prefill_workspace_bytes returns 0) the call is fa_prefill and the workspace may be NULL.
  * Errors as fa_prefill, plus FA_ERR_WORKSPACE.
  */

@@ -114,11 +114,35 @@ def test_prefill_workspace_bytes():
     n = fa.fa_prefill_workspace_bytes(1, 32, 8, 2048, 16384, 128, 1, 14336, 0)
     assert n == 4096 + 96 * 2 * 4 * 64 * 132 * 4
     assert fa.fa_prefill_workspace_bytes(1, 32, 8, 2048, 16384, 128, 1, 14336, 1) == n   # bf16
-    # q4_0 and mixed caches split at D = 128 (the same plan), not at D = 64
-    assert fa.fa_prefill_workspace_bytes(1, 32, 8, 2048, 16384, 128, 1, 14336, 2) == n
-    assert fa.fa_prefill_workspace_bytes(1, 32, 8, 2048, 16384, 128, 1, 14336, 3) == n
-    assert fa.fa_prefill_workspace_bytes(1, 32, 8, 2048, 16384, 64, 1, 14336, 2) == 0
-    assert fa.fa_prefill_workspace_bytes(1, 32, 8, 2048, 16384, 64, 1, 14336, 0) > 0
+    # q4_0 and mixed caches with 16 or more query blocks per KV head (32 here) are widened to
+    # f16 after the split's bytes, one copy [1, 16384, 8, 128] per q4_0 tensor, and split as
+    # f16 (the same plan), at D = 64 too
+    copy = 16384 * 8 * 128 * 2
+    assert n % 256 == 0
+    assert fa.fa_prefill_workspace_bytes(1, 32, 8, 2048, 16384, 128, 1, 14336, 2) == n + 2 * copy
+    assert fa.fa_prefill_workspace_bytes(1, 32, 8, 2048, 16384, 128, 1, 14336, 3) == n + copy
+    assert fa.fa_prefill_workspace_bytes(1, 32, 8, 2048, 16384, 128, 1, 14336, 4) == n + copy
+    n64 = fa.fa_prefill_workspace_bytes(1, 32, 8, 2048, 16384, 64, 1, 14336, 0)
+    assert n64 > 0
+    assert fa.fa_prefill_workspace_bytes(1, 32, 8, 2048, 16384, 64, 1, 14336, 2) == \
+        (n64 + 255) // 256 * 256 + copy
+    # the copy sits after the 4096 counter bytes even when nothing is split (non-causal)
+    assert fa.fa_prefill_workspace_bytes(1, 32, 8, 2048, 16384, 128, 0, 0, 2) == 4096 + 2 * copy
+    # key split: 512 queries (8 blocks x 8 KV heads = 64 units) run 256 / 64 = 4 runs a unit,
+    # 1024 queries (128 units) 2; a run holds 4 waves x 64 rows x 132 floats. The q4_0 cache
+    # at 8 blocks stays fused (the f16 plan), at 16 it is copied first.
+    run = 4 * 64 * 132 * 4
+    assert fa.fa_prefill_workspace_bytes(1, 32, 8, 512, 16384, 128, 1, 15872, 0) == \
+        4096 + 64 * 4 * run
+    assert fa.fa_prefill_workspace_bytes(1, 32, 8, 512, 16384, 128, 1, 15872, 2) == \
+        4096 + 64 * 4 * run
+    assert fa.fa_prefill_workspace_bytes(1, 32, 8, 1024, 16384, 128, 1, 15360, 0) == \
+        4096 + 128 * 2 * run
+    assert fa.fa_prefill_workspace_bytes(1, 32, 8, 1024, 16384, 128, 1, 15360, 2) == \
+        4096 + 128 * 2 * run + 2 * copy
+    # 192 units (1536 queries) are more than half the CUs: pairing, no key split
+    n1536 = fa.fa_prefill_workspace_bytes(1, 32, 8, 1536, 16384, 128, 1, 14848, 0)
+    assert 4096 < n1536 < 4096 + 192 * run
     # nothing splits: non-causal, one small query block, empty calls
     assert fa.fa_prefill_workspace_bytes(1, 32, 8, 2048, 16384, 128, 0, 0, 0) == 0
     assert fa.fa_prefill_workspace_bytes(1, 2, 2, 128, 128, 64, 1, 0, 0) == 0
@@ -126,6 +150,8 @@ def test_prefill_workspace_bytes():
     # more split units than the 4096 counter bytes hold (64 sequences x 8 KV heads x 12
     # blocks = 6144): no split, the call is fa_prefill
     assert fa.fa_prefill_workspace_bytes(64, 32, 8, 2048, 16384, 128, 1, 14336, 0) == 0
+    assert fa.fa_prefill_workspace_bytes(64, 32, 8, 2048, 16384, 128, 1, 14336, 2) == \
+        4096 + 2 * 64 * copy
     assert fa.fa_prefill_workspace_bytes(10, 32, 8, 2048, 16384, 128, 1, 14336, 0) == \
         4096 + 960 * 2 * 4 * 64 * 132 * 4
     # invalid sizes give 0 too

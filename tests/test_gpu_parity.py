@@ -639,9 +639,11 @@ def test_prefill_paged_full_page_table():
         assert err <= TOL["f16"], (b, n, err)
 
 # ---------------------------------------------------------------------------------------------
-# balanced causal prefill (fa_prefill_split): a unit above the cap runs its first cap tiles and
-# the workgroup of its mirror query block (a light unit) runs the rest after its own unit; the
-# later of the two parts to finish merges them
+# balanced causal prefill (fa_prefill_split): with more than 128 units a unit above the cap runs
+# its first cap tiles and the workgroup of its mirror query block (a light unit) runs the rest
+# after its own unit, the later of the two parts to finish merging them; with at most 128 units
+# every unit's keys are cut into runs merged by a second kernel (key split); a q4_0 tensor with
+# 16 or more query blocks per KV head is widened to f16 in the workspace first
 # ---------------------------------------------------------------------------------------------
 
 def gpu_prefill_split(w, x, workspace=None):
@@ -653,23 +655,30 @@ def gpu_prefill_split(w, x, workspace=None):
 
 
 SPLIT_SMALL = [
-    # MHA at D = 64 (head chunks of 1 head x 4 query sub-blocks), two sequences
+    # MHA at D = 64 (head chunks of 1 head x 4 query sub-blocks), two sequences: 64 units
     wl("split_mha_d64", 2, 8, 8, 1024, 1024, 64, "f16", True, 0, seed=90),
     # GQA 4 with a ragged query tail, a chunk at the end of longer keys, two sequences
     wl("split_gqa_ragged", 2, 16, 4, 900, 1600, 128, "f16", True, 700, seed=91),
     wl("split_bf16_d64", 1, 8, 2, 640, 640, 64, "bf16", True, 0, seed=92),
-    # one KV head: 24 units, few enough that every unit's keys are cut into runs
+    # one KV head: 24 units, every unit's keys cut into runs
     wl("split_one_head", 1, 4, 1, 1500, 1500, 128, "f16", True, 0, seed=93),
     # queries before the keys: early rows see nothing
     wl("split_negative_offset", 1, 8, 2, 1200, 1000, 128, "f16", True, -100, seed=94),
     # GQA 3 (head chunks of 3 of 4 waves) and G = 8 (two head chunks)
     wl("split_gqa3", 1, 6, 2, 700, 900, 64, "f16", True, 200, seed=95),
     wl("split_gqa8", 1, 16, 2, 1000, 1000, 128, "bf16", True, 0, seed=96),
-    # q4_0 cache (D = 128): the raw rings and in-kernel dequantization over offset tiles
-    wl("split_q4_0", 1, 16, 4, 1100, 1700, 128, "q4_0", True, 600, seed=100),
-    # 128 units (GQA 2, two sequences): heavy units paired with their mirrors
-    wl("split_pair_gqa2", 2, 16, 8, 1024, 1024, 128, "f16", True, 0, seed=103),
-    wl("split_pair_q4_0", 2, 16, 8, 1024, 1500, 128, "q4_0", True, 476, seed=104),
+    # q4_0 cache, 15 query blocks per KV head: the raw rings and in-kernel dequantization
+    # over the runs' offset tiles
+    wl("split_q4_0", 1, 16, 4, 950, 1700, 128, "q4_0", True, 750, seed=100),
+    # 192 units (GQA 2, three sequences): heavy units paired with their mirrors; the q4_0 one
+    # with 8 query blocks per KV head, so fused
+    wl("split_pair_gqa2", 3, 16, 8, 1024, 1024, 128, "f16", True, 0, seed=103),
+    wl("split_pair_q4_0", 3, 16, 8, 1024, 1500, 128, "q4_0", True, 476, seed=104),
+    # q4_0 copied to f16 first (16+ query blocks per KV head): with the key split, at D = 64,
+    # and with pairing (256 units)
+    wl("split_deq_parts", 1, 8, 2, 1024, 4000, 128, "q4_0", True, None, seed=113),
+    wl("split_deq_d64", 1, 8, 2, 1100, 1700, 64, "q4_0", True, 600, seed=114),
+    wl("split_deq_pair", 2, 32, 8, 1024, 1024, 128, "q4_0", True, 0, seed=115),
 ]
 
 
@@ -684,7 +693,7 @@ def test_prefill_split_matches_oracle(w):
             w.name)
 
 
-# key split (fewer than 128 units): a short chunk of queries against many keys; every unit's
+# key split (at most 128 units): a short chunk of queries against many keys; every unit's
 # tiles are cut into runs of their own workgroups and a merge kernel combines them
 SPLIT_PARTS = [
     wl("parts_chunk64_16k", 1, 32, 8, 64, 16384, 128, "f16", True, None, seed=105),
@@ -739,7 +748,8 @@ def test_prefill_split_nothing_to_split():
 
 
 SPLIT_MIXED = [
-    # (name, B, Hq, Hkv, Sq, Sk, D, K type, V type, offset, seed)
+    # (name, B, Hq, Hkv, Sq, Sk, D, K type, V type, offset, seed): 16 query blocks per KV head
+    # (V copied to f16 first), then 15 (fused)
     ("split_f16k_q4v", 1, 8, 2, 1000, 1000, 128, "f16", "q4_0", 0, 101),
     ("split_q4k_f16v", 2, 8, 2, 900, 1200, 128, "q4_0", "f16", 300, 102),
 ]
@@ -783,8 +793,10 @@ def test_prefill_split_workspace_reused():
     cases = [W.WORKLOADS["prefill_16k_f16"], wl("split_reuse_mha", 2, 8, 8, 1024, 1024, 64,
                                                      "f16", True, 0, seed=99),
              wl("split_reuse", 2, 16, 4, 900, 1600, 128, "f16", True, 700, seed=97),
+             # 160 units, non-causal: nothing to split, only the f16 copy past the counters
+             wl("split_reuse_copy_only", 5, 8, 2, 1024, 700, 128, "q4_0", False, 0, seed=116),
              W.WORKLOADS["prefill_2k_bf16"]]
-    nbytes = max(fa.fa_prefill_workspace_bytes(w.B, w.Hq, w.Hkv, w.Sq, w.Sk, w.D, 1,
+    nbytes = max(fa.fa_prefill_workspace_bytes(w.B, w.Hq, w.Hkv, w.Sq, w.Sk, w.D, int(w.causal),
                                                w.causal_offset, w.kv_code) for w in cases)
     ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
     for w in cases:
