@@ -1076,7 +1076,14 @@ __global__ __launch_bounds__(kNT, 1) void prefill16_kernel(Prefill16Params p)
                 const float F = fmaxf(frame[j], fl[0]);
                 const float wm = F == -INFINITY ? 0.0f : exp2_fast(frame[j] - F);
                 const float wo = F == -INFINITY ? 0.0f : exp2_fast(fl[0] - F);
-                const float L = wm * ltot[j] + wo * fl[1];
+                // part 0's terms first, whichever part merges, so the rows do not depend on
+                // which of the two finished last: w0 y0 + w1 y1 as one fma over one product
+                const bool p0 = part == 0;
+                const float w0 = p0 ? wm : wo, w1 = p0 ? wo : wm;
+                auto mix = [&](float ym, float yo) INL {
+                    return __builtin_fmaf(w0, p0 ? ym : yo, w1 * (p0 ? yo : ym));
+                };
+                const float L = mix(ltot[j], fl[1]);
                 if (!wave_on || qi[j] >= sq)
                     continue;
                 const float inv = L > 0.0f ? 1.0f / L : 0.0f;
@@ -1088,10 +1095,10 @@ __global__ __launch_bounds__(kNT, 1) void prefill16_kernel(Prefill16Params p)
                         const f32x4 x = *(const f32x4 *)(row + 32 * dt + 8 * ii + 4 * half);
                         const f32x16 &c = acc[j][dt];
                         u32x2 w;
-                        w[0] = pack2<BF>((wm * c[4 * ii + 0] + wo * x[0]) * inv,
-                                         (wm * c[4 * ii + 1] + wo * x[1]) * inv);
-                        w[1] = pack2<BF>((wm * c[4 * ii + 2] + wo * x[2]) * inv,
-                                         (wm * c[4 * ii + 3] + wo * x[3]) * inv);
+                        w[0] = pack2<BF>(mix(c[4 * ii + 0], x[0]) * inv,
+                                         mix(c[4 * ii + 1], x[1]) * inv);
+                        w[1] = pack2<BF>(mix(c[4 * ii + 2], x[2]) * inv,
+                                         mix(c[4 * ii + 3], x[3]) * inv);
                         *(u32x2 *)(op + 32 * dt + 8 * ii + 4 * half) = w;
                     }
             }
