@@ -1262,13 +1262,13 @@ hipError_t launch16_kv(const Prefill16Params &p, int64_t n_wg, hipStream_t strea
 // its first `cap` tiles and the lighter one runs the rest after its own, in the same
 // workgroup: cap = the average tiles per unit plus kSplitBias, which leaves the light
 // workgroup the time to restart (load the second unit's Q and first tiles) and merge. Timed
-// on the box at 2K, 8K and 16K keys, biases 0-6: 3 was best (4 close, 0 and 6 worst).
+// on an MI355X at 2K, 8K and 16K keys, biases 0-6: 3 was best (4 close, 0 and 6 worst).
 constexpr int kSplitBias = 3;
 
 // Key split: when the units are at most half the CUs (a short chunk of queries against many
 // keys, where each workgroup would run its unit's tiles alone while most CUs idle), every
 // unit's tiles are cut into `parts` runs of at least kMinRunTiles tiles, as many as fill the
-// kCUs CUs in one round (parts = kCUs / units), merged by a second kernel. Timed on the box at
+// kCUs CUs in one round (parts = kCUs / units), merged by a second kernel. Timed on an MI355X at
 // 8-128 units and 2K-16K keys against runs sized for two or four rounds (512 or 1024
 // workgroups): one round was fastest at every shape (e.g. 1024 queries x 16K keys: 267 us
 // against 278 and 307; 64 queries: 78 against 130). With more units than that, pairing.
@@ -1278,7 +1278,7 @@ constexpr int64_t kMaxParts = 64;
 
 // Dequantize first: the fused kernel dequantizes a q4_0 tile in every workgroup that reads it,
 // once per query block and head chunk of its KV head; widening the cache to f16 once costs a
-// pass over it. Timed at 16K keys, GQA 32/8 (fa_prefill_split both ways, same box): 64-256
+// pass over it. Timed at 16K keys, GQA 32/8 (fa_prefill_split both ways, same GPU): 64-256
 // queries (1-4 blocks) fused faster (118-135 us against 138-161), 512 (8) even, 1024 (16) and
 // more the dequantized copy faster. Output bits are the same either way (one unpack routine).
 constexpr int64_t kDequantFirstBlocks = 16;

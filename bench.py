@@ -11,7 +11,7 @@ One step = one pass of the whole path over resident inputs:
     scale Q K^T materialised, softmax, P V); the decode workload the same three ways; and the
     standard path on the f16 caches beside the f16 flash kernels (the pages' FA-off arm);
   * a plain streaming read of as many bytes as the decode moves (fa_measure_read): the HBM
-    read rate the decode is compared with on this box (`read_ceiling`);
+    read rate the decode is compared with on this GPU (`read_ceiling`);
   * the q4_0 cache writer: fa_quantize_q4_0 of the prefill workload's f16 K and V;
   * the decode over a paged cache (2048 shuffled 64-key pages) and the prefill over one (256);
   * mixed caches (f16 K, q4_0 V); head dim 64 (the prefill at D = 64, and the B=2, S=512,
@@ -221,7 +221,7 @@ def cpu_baseline(w, x, seconds: float):
 
 # Throughput floors of --gate (exit status 1 below either). The mlxcel PR gates its 16K-key
 # call at a floor between the throughputs before and after its change; these sit 5 % under
-# the figures this kernel set measured (bench.py on the box: prefill_16k_f16 TFLOP/s, decode
+# the figures this kernel set measured (bench.py on an MI355X: prefill_16k_f16 TFLOP/s, decode
 # GB/s).
 GATE_PREFILL_TFLOPS = 990.0
 GATE_DECODE_GBS = 3380.0

@@ -2,7 +2,7 @@
 
 Only the tests, the smoke check and the benchmark's CPU-baseline leg may import this package.
 It wraps liboracle.so (plain C, fa_oracle.c), which computes the plain definition
-O = softmax(scale * Q K^T + causal mask) V as an explicit f32 matmul + softmax + matmul
+O = softmax(scale * Q K^T + causal mask) V in f32: a product, a softmax, a second product
 (mlxcel PR #2306, commit message 2; mi210-llm-stack build guide, Verification). It shares no
 code with the HIP path and never calls it.
 

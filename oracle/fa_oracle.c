@@ -7,8 +7,8 @@
  *
  * What it computes is the plain definition that the pages check their kernels against:
  *   O = softmax(scale * Q K^T + causal mask) V
- * evaluated as an explicit f32 matmul + softmax + matmul (mlxcel PR #2306, commit message 2
- * and "Test plan": causal correctness against an explicit f32 reference; mi210-llm-stack
+ * evaluated as an f32 product, a softmax and a second product (mlxcel PR #2306, commit
+ * message 2 and "Test plan", whose causal checks use such an f32 reference; mi210-llm-stack
  * "Build FlashAttention (CK backend) on gfx90a", Verification: the fused kernel compared with
  * torch's scaled_dot_product_attention). Every query row is computed on its own: the row's
  * visible scores, their maximum, exp of the shifted scores, their sum, and the weighted sum of

@@ -2,9 +2,9 @@
 (fa_prefill_stats, fa_decode_stats) report per query row how often its softmax frame moved
 and, for the prefill, in how many tiles its wave ran the O rescale.
 
-mlxcel PR #2306 ("What changed", "Test plan"): the accumulators are rescaled only when a row's
-block maximum outgrows its frame by more than the margin, which in the steady state of a
-chunked prefill does not happen; a score ramp is the input that makes it happen. So on N(0,1)
+mlxcel PR #2306 ("What changed", "Test plan"): O and l are rescaled only for a block whose
+maximum passes the row's frame by more than the margin, which ordinary inputs do not meet once
+a row has its first frame; inputs whose scores climb along the keys are what make it happen. So on N(0,1)
 inputs every row's frame moves exactly once (from -inf to its first block maximum) and its
 wave rescales O once, while under the +0.05-per-key ramp the frame moves about every 3-4
 tiles (the ramp climbs 3.2 per 64-key tile against a margin of 10). The counter instances

@@ -9,8 +9,8 @@ nothing the HIP path computes; it also carries the measurement conventions
 Sources (the pages these workloads stand in for):
   * mlxcel PR #2306 "defer SDPA accumulator rescale, stage Q once per block", commit
     message and Measurements: 2,048-token query chunks placed at the end of 2K / 8K /
-    16K keys, GQA 32/8, head dim 128, f16 and bf16, plus a score ramp that pushes a
-    row's block max past the rescale margin.
+    16K keys, GQA 32/8, head dim 128, f16 and bf16, plus inputs whose scores climb along
+    the keys so that rows outrun the rescale margin.
   * mi210-llm-stack "Build FlashAttention (CK backend) on gfx90a", Verification:
     B=2, S=512, H=8, D=64, causal, max_diff < 0.01.
   * mi210-llm-stack "FlashAttention on gfx90a", "-ctk q4_0 -ctv q4_0": a q4_0 KV cache.
