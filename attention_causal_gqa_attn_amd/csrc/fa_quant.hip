@@ -42,13 +42,31 @@ __device__ __forceinline__ uint32_t q4_code(float x, float d)
 // [-8.004, 8.004] and d is a positive f16 value, so no step over- or underflows; the argument
 // needs x and q0 d away from the subnormal range, which the exact fallback below covers
 // (|x| < 2^-100: the code is 8 either way unless d is as small, checked by the caller).
+// |q1| <= 8.004 also bounds the rounded value by 8, so the code is never below 0 and only
+// +max|x| (16) needs the clamp.
+// Rounding half away from zero: for f16 and bf16 sources v_cvt_rpi_i32_f32 (floor(s + 0.5))
+// of |q1|, the sign put back as (r ^ s) - s with s = 0 or -1. That is exact even if the
+// instruction rounds s + 0.5 to f32 first: such a rounding can move the floor only when
+// s + 0.5 lies within half an ulp below an integer, which for |q1| <= 8.004 needs
+// 0.5 - 2^-25 < |q1| < 0.5, and a quotient of two 16-bit values (x f16 or bf16, d f16 and
+// normal) that is not 0.5 differs from it by at least 2^-11 relative (2x and d lie on the grid
+// of d's ulp). An f32 x can come that close, so f32 sources round with roundf.
+template <int SRC>
 __device__ __forceinline__ uint32_t q4_code_r(float x, float d, float r)
 {
     const float q0 = x * r;
     const float e = __builtin_fmaf(-q0, d, x);
     const float q1 = __builtin_fmaf(e, r, q0);
-    const int c = (int)__builtin_roundf(q1) + 8;
-    return (uint32_t)min(max(c, 0), 15);
+    int c;
+    if constexpr (SRC == 0) {
+        c = (int)__builtin_roundf(q1) + 8;
+    } else {
+        int m;
+        asm("v_cvt_rpi_i32_f32 %0, |%1|" : "=v"(m) : "v"(q1));
+        const int sg = (int)__builtin_bit_cast(uint32_t, q1) >> 31;
+        c = (m ^ sg) - sg + 8;
+    }
+    return (uint32_t)min(c, 15);
 }
 
 template <int SRC>      // 0: f32, 1: f16, 2: bf16
@@ -101,7 +119,8 @@ __global__ __launch_bounds__(256) void quantize_q4_0_kernel(QuantParams p)
         const float r = 1.0f / d;                       // correctly rounded
 #pragma unroll
         for (int t = 0; t < 16; ++t) {
-            const uint32_t byte = q4_code_r(v[t], d, r) | (q4_code_r(v[t + 16], d, r) << 4);
+            const uint32_t byte =
+                q4_code_r<SRC>(v[t], d, r) | (q4_code_r<SRC>(v[t + 16], d, r) << 4);
             code4[t / 4] |= byte << (8 * (t % 4));
         }
     } else {
