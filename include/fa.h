@@ -249,8 +249,9 @@ int fa_standard_attention(const void *q, const void *k, const void *v, void *o,
  * Counter instances, for tests of the deferred rescale (mlxcel PR #2306, "What changed" and
  * "Test plan": O and l are rescaled only for a block whose maximum passes the row's frame by
  * more than the margin, which a chunked prefill on ordinary inputs hardly ever meets after its
- * first block; inputs whose scores climb along the keys are what make the branch run). They run the same kernel source as
- * fa_prefill / fa_decode with two counters per query row added, and give the same output.
+ * first block; inputs whose scores climb along the keys are what make the branch run). They
+ * run the same kernel source as fa_prefill / fa_decode with two counters per query row added,
+ * and give the same output.
  *   counts   device int32 [B, Sq, Hq, 2], 8-byte aligned. Per query row (b, i, h):
  *            counts[..., 0] = how many times the row's softmax frame moved (the rescale test
  *            fired for the row; the first frame, taken from -inf, counts as one);
