@@ -1105,18 +1105,25 @@ __global__ __launch_bounds__(kNT, 1) void prefill16_kernel(Prefill16Params p)
             return;
         }
     }
+    // The wave's 64 normalised rows go out through LDS: written from the accumulators (lane =
+    // row, 8 bytes of 4 d values per write) into the wave's own 64 x 2D-byte region of the
+    // tile rings, 16-byte chunk c of row r at slot c ^ (r % CPR), then read back and stored
+    // as whole rows, 16 bytes a lane. Straight from the accumulators every store instruction
+    // would touch 32 rows. Every transfer has landed (wait_tiles above); the barrier waits
+    // for the other waves' last P.V reads (with a raw q4_0 K the V ring lies in the region).
+    static_assert(LDSB >= kNW * 64 * G::ROW, "the rows fit the tile rings");
+    uint8_t *orow = lds + wave * 64 * G::ROW;
+    __syncthreads();
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
         const float ltot = pair_sum(lsum[j]);
-        if (!wave_on || qi[j] >= sq)
-            continue;
         const float inv = ltot > 0.0f ? 1.0f / ltot : 0.0f;
-        uint16_t *op = (uint16_t *)a.o + (((int64_t)b * a.Sq + qi[j]) * a.Hq + h) * D;
         if constexpr (STATS) {
-            if (half == 0)
+            if (wave_on && qi[j] < sq && half == 0)
                 *(int2 *)(p.stats + 2 * (((int64_t)b * a.Sq + qi[j]) * a.Hq + h)) =
                     make_int2(nmove[j], nresc[j]);
         }
+        const int r = 32 * j + col;
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
@@ -1124,8 +1131,23 @@ __global__ __launch_bounds__(kNT, 1) void prefill16_kernel(Prefill16Params p)
                 u32x2 w;
                 w[0] = pack2<BF>(acc[j][dt][4 * ii + 0] * inv, acc[j][dt][4 * ii + 1] * inv);
                 w[1] = pack2<BF>(acc[j][dt][4 * ii + 2] * inv, acc[j][dt][4 * ii + 3] * inv);
-                *(u32x2 *)(op + 32 * dt + 8 * ii + 4 * half) = w;
+                const int c = 4 * dt + ii;
+                *(u32x2 *)(orow + r * G::ROW + ((c ^ (r % G::CPR)) * 16) + 8 * half) = w;
             }
+    }
+    // the wave reads back its own region: its LDS writes complete first, and the clobber keeps
+    // the compiler from moving the reads above them
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    if (wave_on) {
+        constexpr int RPI = 64 / G::CPR;                 // rows per store instruction
+#pragma unroll
+        for (int s_ = 0; s_ < 64 / RPI; ++s_) {
+            const int r = s_ * RPI + lane / G::CPR, c = lane % G::CPR;
+            const u32x4 x = *(const u32x4 *)(orow + r * G::ROW + ((c ^ (r % G::CPR)) * 16));
+            if (q0 + r < sq)
+                *(u32x4 *)((uint16_t *)a.o + (((int64_t)b * a.Sq + q0 + r) * a.Hq + h) * D +
+                           8 * c) = x;
+        }
     }
     };  // run
 
