@@ -144,20 +144,17 @@ __device__ __forceinline__ void lane_halves(float x, float &lo, float &hi)
     lo = a;
     hi = b;
 }
-// f32 maxima as single instructions. The compiler's fmaxf first quiets every operand it cannot
-// prove canonical (MFMA results issued from asm, DPP results: one extra v_max_f32 each); the
-// values maximised here are scores and their maxima, never NaN (masked keys are -inf).
+// f32 maxima as single instructions (v_maximum3_f32). The compiler's fmaxf first quiets every
+// operand it cannot prove canonical (MFMA results issued from asm, DPP results: one extra
+// v_max_f32 each); the IEEE maximum needs no quieting. The values maximised here are scores and
+// their maxima, never NaN (masked keys are -inf), where the two agree.
 __device__ __forceinline__ float vmax(float a, float b)
 {
-    float r;
-    asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
-    return r;
+    return __builtin_elementwise_maximum(a, b);
 }
 __device__ __forceinline__ float vmax3(float a, float b, float c)
 {
-    float r;
-    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-    return r;
+    return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
 }
 
 __device__ __forceinline__ float pair_max(float x)
