@@ -123,7 +123,9 @@ __device__ __forceinline__ void pin(T &x)
 // instructions, which cannot take AGPR operands). The compiler does not see these as MFMAs:
 // the kernel waits out the MFMA-to-VALU dependency itself (s_nop before the first VALU read
 // of a tile's scores), and the chains accumulate in place (srcC == vdst). The Q operand is
-// taken from AGPRs, where Q stays for the whole kernel.
+// taken from AGPRs, where Q stays for the whole kernel. The asm is volatile: a plain asm
+// statement may be moved past the scheduling fences (its order is free in the compiler's
+// view), which drew half 2's softmax units and transfers in front of its first MFMA.
 template <bool BF>
 __device__ __forceinline__ void smfma_first(f32x16 &d, const u32x4 &a, const u32x4 &b)
 {
@@ -573,22 +575,14 @@ __global__ __launch_bounds__(kNT, 1) void prefill16_kernel(Prefill16Params p)
         dma16(gt, min(rowg[i], lastg) + (is_v ? vc[i] : kc[i]),
               lwave[i] + (uint32_t)(stage * G::TILE));
     };
-    // transfer i of the tiles issued in iteration n: i < NDMA: K(n+LK) at slot sk4, else
-    // V(n+LV) at slot sv2 (into the stages of K(n+LK-FSK) and V(n+LV-FSV), whose last reader
-    // ran before the latest barrier)
-    auto dma_part = [&](int n, int i, int sk4, int sv2) INL {
-        if (i < G::NDMA)
-            dma_one(false, (n + LK) & (FSK - 1), n + LK, sk4, i);
-        else
-            dma_one(true, FSK + ((n + LV) & (FSV - 1)), n + LV, sv2, i - G::NDMA);
-    };
-    // 16-bit contiguous caches (no raw tensor, no pages): the same transfers with less
-    // per-tile arithmetic. A lane's offsets within a tile are fixed (koff, voff); the first rows
-    // of the tiles this iteration reads (kcur, vcur) advance by one tile per iteration up to the
-    // last tile; on the last tile, offsets past the sequence's last row (tail_lim) are clamped
-    // to that row's last chunk, so every byte read lies in the cache and is finite (those rows
-    // are keys every query masks, so what lands there is never used).
-    constexpr bool FAST16 = !ANYQ && !PAGED;
+    // 16-bit caches (no raw tensor): the same transfers with less per-tile arithmetic. A lane's
+    // offsets within a tile are fixed (koff, voff); the first rows of the tiles this iteration
+    // reads (kcur, vcur) advance by one tile per iteration up to the last tile (a paged cache:
+    // the tile's page, looked up per iteration); on the last tile, offsets past the sequence's
+    // last row (tail_lim) are clamped to that row's last chunk, so every byte read lies in the
+    // cache and is finite (those rows are keys every query masks, so what lands there is never
+    // used).
+    constexpr bool FAST16 = !ANYQ;
     // where the transfers go: at D = 128 K's in half 1 and V's in half 2 (the K fragment reads
     // of half 2 then share the LDS with half the transfers); at D = 64 all in half 2 (timed on
     // an MI355X: 0.7 % faster at D = 128, 0.5 % slower at D = 64)
@@ -608,19 +602,25 @@ __global__ __launch_bounds__(kNT, 1) void prefill16_kernel(Prefill16Params p)
         return base + (int64_t)(t0 + min(tl, nb - 1)) * tstep;
     };
     const uint8_t *kcur = tile_row0(kg, LK), *vcur = tile_row0(vg, LV);
-    // transfer i (< NDMA: K(n+LK), else V(n+LV)) of iteration n
-    auto dma_fast = [&](int n, int i) INL {
+    // transfer i (< NDMA: K(n+LK), else V(n+LV)) of iteration n, into the stage of K(n+LK-FSK)
+    // or V(n+LV-FSV), whose last reader ran before the latest barrier; a paged cache's tiles
+    // sit in pages sk4 (K) and sv2 (V)
+    auto dma_fast = [&](int n, int i, int sk4, int sv2) INL {
         const bool is_v = i >= G::NDMA;
         const int ii = is_v ? i - G::NDMA : i;
         const int tl = n + (is_v ? LV : LK);
         const uint32_t lim = tl >= nb - 1 ? tail_lim : ~0u;
         const uint32_t st = (uint32_t)((is_v ? FSK + (tl & (FSV - 1)) : (tl & (FSK - 1))) * G::TILE);
-        dma16c(is_v ? vcur : kcur, is_v ? voff[ii] : koff[ii], lim, lwave[ii], st);
+        const uint8_t *src = PAGED ? (is_v ? vg : kg) + (int64_t)(is_v ? sv2 : sk4) * tstep
+                                   : (is_v ? vcur : kcur);
+        dma16c(src, is_v ? voff[ii] : koff[ii], lim, lwave[ii], st);
     };
     // after iteration n's transfers: the tiles of iteration n + 1
     auto dma_advance = [&](int n) INL {
-        kcur += n + LK + 1 <= nb - 1 ? tstep : 0;
-        vcur += n + LV + 1 <= nb - 1 ? tstep : 0;
+        if constexpr (!PAGED) {
+            kcur += n + LK + 1 <= nb - 1 ? tstep : 0;
+            vcur += n + LV + 1 <= nb - 1 ? tstep : 0;
+        }
     };
 
     // ---- q4_0: raw transfers and the dequantization into the f16 rings ----------------------
@@ -918,7 +918,7 @@ __global__ __launch_bounds__(kNT, 1) void prefill16_kernel(Prefill16Params p)
             }
             units(ic);
             if constexpr (FAST16 && kDmaMode == 2 && (i & 3) == 1 && (i >> 2) < G::NDMA)
-                dma_fast(n, i >> 2);                  // K(n+LK)
+                dma_fast(n, i >> 2, sk4, sv2);        // K(n+LK)
             __builtin_amdgcn_sched_barrier(0);
         });
         // half 2: scores of tile n+1 for both blocks
@@ -937,12 +937,10 @@ __global__ __launch_bounds__(kNT, 1) void prefill16_kernel(Prefill16Params p)
                     dma_mixed(n, i >> 2, sk4, sv2);
             } else if constexpr ((i & 3) == 1 && (i >> 2) < 2 * G::NDMA) {
                 constexpr int m = i >> 2;
-                if constexpr (!FAST16)
-                    dma_part(n, m, sk4, sv2);
-                else if constexpr (kDmaMode == 0)
-                    dma_fast(n, m);
+                if constexpr (kDmaMode == 0)
+                    dma_fast(n, m, sk4, sv2);
                 else if constexpr (kDmaMode == 2 && m < G::NDMA)
-                    dma_fast(n, G::NDMA + m);         // V(n+LV)
+                    dma_fast(n, G::NDMA + m, sk4, sv2);   // V(n+LV)
             }
             __builtin_amdgcn_sched_barrier(0);
         });
