@@ -102,6 +102,18 @@ __device__ __forceinline__ void dma16c(const uint8_t *gbase, uint32_t voff, uint
                  : "memory", "scc");
 }
 
+// The 12-byte transfer with the lane's offset formed on the way, min(rowoff, lim) + col (the
+// row clamped, the column kept), and its LDS base lds_a + lds_b written straight into M0.
+__device__ __forceinline__ void dma12c(const uint8_t *gbase, uint32_t rowoff, uint32_t lim,
+                                       uint32_t col, uint32_t lds_a, uint32_t lds_b)
+{
+    uint32_t t;
+    asm volatile("s_add_u32 m0, %4, %5\n\tv_min_u32 %0, %2, %1\n\tv_add_u32 %0, %0, %3\n\t"
+                 "global_load_lds_dwordx3 %0, %6"
+                 : "=&v"(t) : "v"(rowoff), "s"(lim), "v"(col), "s"(lds_a), "s"(lds_b), "s"(gbase)
+                 : "memory", "scc");
+}
+
 // One 12-byte LDS-DMA transfer per lane: gbase + voff -> LDS lds_base + 16 * lane (a 16-byte
 // slot per lane), for the q4_0 rows, whose 18-byte blocks split into 12-byte chunks.
 __device__ __forceinline__ void dma12(const uint8_t *gbase, uint32_t voff, uint32_t lds_base)
@@ -644,13 +656,48 @@ __global__ __launch_bounds__(kNT, 1) void prefill16_kernel(Prefill16Params p)
               row * growq + 12u * (uint32_t)(sl % QR::CPR),
               __builtin_amdgcn_readfirstlane(lds_addr(stg) + (uint32_t)(1024 * x)));
     };
-    // this wave's m-th transfer of iteration n: raw K(n+4) at slot sk4, then raw V(n+2) at sv2
-    auto dma_q4 = [&](int n, int m, int sk4, int sv2) INL {
+    // Both tensors raw: this wave's m-th transfer of every iteration is transfer
+    // i = min(wave + 4 m, 2 NX - 1) of the pair (i < NX: column i of raw K(n+4), else column
+    // i - NX of raw V(n+2)), so its tensor, row offset, column and LDS column are fixed; per
+    // tile only the tile's base, the row limit and the stage change
+    constexpr int NIWQ = Q4 ? QR::NIW : 1;
+    uint32_t rq_off[NIWQ], rq_col[NIWQ], rq_lds[NIWQ], rq_m32[NIWQ];
+    uint64_t rq_m64[NIWQ];          // all ones for a V transfer: selects V's base and limit
+#pragma unroll
+    for (int m = 0; m < NIWQ; ++m) {
         const int i = min(wave + kNW * m, 2 * QR::NX - 1);
-        if (i < QR::NX)
-            dma_raw(false, n + 4, sk4, i);
-        else
-            dma_raw(true, n + 2, sv2, i - QR::NX);
+        const bool v = i >= QR::NX;
+        const int x = v ? i - QR::NX : i, sl = 64 * x + lane;
+        rq_off[m] = (uint32_t)(sl / QR::CPR) * growq;
+        rq_col[m] = 12u * (uint32_t)(sl % QR::CPR);
+        rq_lds[m] = __builtin_amdgcn_readfirstlane(
+            lds_addr(lds + RAW0 + (v ? QR::KR * QR::RAWT : 0)) + (uint32_t)(1024 * x));
+        rq_m32[m] = v ? ~0u : 0u;
+        rq_m64[m] = v ? ~(uint64_t)0 : (uint64_t)0;
+    }
+    // the last row of the last tile (rows past it repeat it)
+    const uint32_t lastq =
+        nb > 0 ? (uint32_t)min((int64_t)kBN - 1, (int64_t)sk - 1 - (int64_t)(t0 + nb - 1) * kBN) : 0u;
+    // iteration n's raw tiles: K(n+4) in page / tile slot sk4, V(n+2) in sv2; bases, row
+    // limits and stage offsets, formed once and picked per transfer without a branch
+    struct RawIt {
+        uint64_t kb, vb;
+        uint32_t kl, vl, ks, vs;
+    };
+    auto raw_it = [&](int n, int sk4, int sv2) INL {
+        RawIt r;
+        r.kb = (uint64_t)(kq + (int64_t)sk4 * kBN * growq);
+        r.vb = (uint64_t)(vq + (int64_t)sv2 * kBN * growq);
+        r.kl = (n + 4 >= nb - 1 ? lastq : (uint32_t)(kBN - 1)) * growq;
+        r.vl = (n + 2 >= nb - 1 ? lastq : (uint32_t)(kBN - 1)) * growq;
+        r.ks = (uint32_t)(((n + 4) & (QR::KR - 1)) * QR::RAWT);
+        r.vs = (uint32_t)(((n + 2) % QR::VR) * QR::RAWT);
+        return r;
+    };
+    auto dma_q4 = [&](const RawIt &r, int m) INL {
+        const uint64_t base = r.kb ^ ((r.kb ^ r.vb) & rq_m64[m]);
+        dma12c((const uint8_t *)base, rq_off[m], r.kl ^ ((r.kl ^ r.vl) & rq_m32[m]), rq_col[m],
+               rq_lds[m], r.ks ^ ((r.ks ^ r.vs) & rq_m32[m]));
     };
     // mixed caches: this wave's m-th transfer, the TK of K(n+4) then the TV of V(n+2); the raw
     // tensor's NX wave-wide transfers are dealt to the waves (surplus ones repeat the last)
@@ -894,6 +941,9 @@ __global__ __launch_bounds__(kNT, 1) void prefill16_kernel(Prefill16Params p)
     auto tile = [&](int n, f32x16 *s0, f32x16 *s1c, f32x16 *s1n) INL {
         const uint8_t *vs = vstage(n - 1), *ks = kstage(n + 1);
         const int sk4 = slot(n + LK), sv2 = slot(n + LV);   // where this iteration's DMA reads
+        RawIt rit{};
+        if constexpr (Q4)
+            rit = raw_it(n, sk4, sv2);                   // (LK = 4, LV = 2 here)
         u32x4 fb[kRead + 1];
         auto units = [&](auto sc_) INL {          // the softmax units of slot sc_
             constexpr int sl = decltype(sc_)::value;
@@ -931,7 +981,7 @@ __global__ __launch_bounds__(kNT, 1) void prefill16_kernel(Prefill16Params p)
             units(std::integral_constant<int, NM + i>{});
             if constexpr (Q4) {
                 if constexpr ((i & 3) == 1 && (i >> 2) < QR::NIW)
-                    dma_q4(n, i >> 2, sk4, sv2);
+                    dma_q4(rit, i >> 2);
             } else if constexpr (ANYQ) {
                 if constexpr ((i & 3) == 1 && (i >> 2) < TI)
                     dma_mixed(n, i >> 2, sk4, sv2);
