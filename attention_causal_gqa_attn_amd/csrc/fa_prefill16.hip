@@ -623,8 +623,9 @@ __global__ __launch_bounds__(kNT, 1) void prefill16_kernel(Prefill16Params p)
         const int tl = n + (is_v ? LV : LK);
         const uint32_t lim = tl >= nb - 1 ? tail_lim : ~0u;
         const uint32_t st = (uint32_t)((is_v ? FSK + (tl & (FSV - 1)) : (tl & (FSK - 1))) * G::TILE);
-        const uint8_t *src = PAGED ? (is_v ? vg : kg) + (int64_t)(is_v ? sv2 : sk4) * tstep
-                                   : (is_v ? vcur : kcur);
+        const uint8_t *src = PAGED || ANYQ
+                                 ? (is_v ? vg : kg) + (int64_t)(is_v ? sv2 : sk4) * tstep
+                                 : (is_v ? vcur : kcur);
         dma16c(src, is_v ? voff[ii] : koff[ii], lim, lwave[ii], st);
     };
     // after iteration n's transfers: the tiles of iteration n + 1
@@ -701,18 +702,38 @@ __global__ __launch_bounds__(kNT, 1) void prefill16_kernel(Prefill16Params p)
     };
     // mixed caches: this wave's m-th transfer, the TK of K(n+4) then the TV of V(n+2); the raw
     // tensor's NX wave-wide transfers are dealt to the waves (surplus ones repeat the last)
+    // (the raw tensor's transfer mr moves column min(wave + 4 mr, NX - 1): fixed row offset,
+    // column and LDS column, as for two raw tensors; the 16-bit tensor's go as dma_fast)
+    constexpr int NRAW = ANYQ && !Q4 ? QR::NIW1 : 1;
+    uint32_t mr_off[NRAW], mr_col[NRAW], mr_lds[NRAW];
+#pragma unroll
+    for (int mr = 0; mr < NRAW; ++mr) {
+        const int sl = 64 * min(wave + kNW * mr, QR::NX - 1) + lane;
+        mr_off[mr] = (uint32_t)(sl / QR::CPR) * growq;
+        mr_col[mr] = 12u * (uint32_t)(sl % QR::CPR);
+        mr_lds[mr] = __builtin_amdgcn_readfirstlane(
+            lds_addr(lds + RAW0) + (uint32_t)(1024 * min(wave + kNW * mr, QR::NX - 1)));
+    }
     auto dma_mixed = [&](int n, int m, int sk4, int sv2) INL {
         if (m < TK) {
-            if constexpr (QK)
-                dma_raw(false, n + 4, sk4, min(wave + kNW * m, QR::NX - 1));
-            else
-                dma_one(false, (n + 4) & (FSK - 1), n + 4, sk4, m);
+            if constexpr (QK) {
+                const int tl = n + 4;
+                dma12c(kq + (int64_t)sk4 * kBN * growq, mr_off[m],
+                       (tl >= nb - 1 ? lastq : (uint32_t)(kBN - 1)) * growq, mr_col[m], mr_lds[m],
+                       (uint32_t)((tl & (QR::KR - 1)) * QR::RAWT));
+            } else {
+                dma_fast(n, m, sk4, sv2);
+            }
         } else {
             const int mv = m - TK;
-            if constexpr (QV)
-                dma_raw(true, n + 2, sv2, min(wave + kNW * mv, QR::NX - 1));
-            else
-                dma_one(true, FSK + ((n + 2) & (FSV - 1)), n + 2, sv2, mv);
+            if constexpr (QV) {
+                const int tl = n + 2;
+                dma12c(vq + (int64_t)sv2 * kBN * growq, mr_off[mv],
+                       (tl >= nb - 1 ? lastq : (uint32_t)(kBN - 1)) * growq, mr_col[mv],
+                       mr_lds[mv], (uint32_t)((tl % QR::VR) * QR::RAWT));
+            } else {
+                dma_fast(n, G::NDMA + mv, sk4, sv2);
+            }
         }
     };
     // This thread's (key row, block) item of a tile: at D = 128 one K and one V item, wave w
