@@ -748,6 +748,9 @@ __global__ __launch_bounds__(kNT, 1) void prefill16_kernel(Prefill16Params p)
         const uint8_t *sa = raw + 16 * (dq_row * QR::CPR + (3 * dq_blk) / 2);
         return RawBlock{*(const u32x4 *)sa, *(const u32x4 *)(sa + 16)};
     };
+    // the item's f16 rows, in two halves: code dwords 2 h, 2 h + 1 into the chunks 4 blk + h
+    // (low nibbles) and 4 blk + 2 + h (high nibbles), each half's stores issued before the next
+    // half is unpacked (1.9 % faster at 2K x 16K than all unpacks first)
     auto dq_store = [&](const RawBlock &rb, uint8_t *dst, bool is_v) INL {
         const u32x4 &A = rb.A, &Bq = rb.Bq;
         uint32_t dbits, codes[4];
@@ -765,16 +768,16 @@ __global__ __launch_bounds__(kNT, 1) void prefill16_kernel(Prefill16Params p)
             codes[3] = __builtin_amdgcn_alignbit(Bq[1], Bq[0], 16);
         }
         const uint32_t d2 = dbits * 0x10001u;
-        uint32_t lo[4][2], hi[4][2];
-#pragma unroll
-        for (int gg = 0; gg < 4; ++gg)
-            q4_unpack_row(codes[gg], d2, lo[gg], hi[gg]);
         const int sw = is_v ? G::swv(dq_row) : G::swk(dq_row);
         uint8_t *rp = dst + dq_row * G::ROW;
-        *(u32x4 *)(rp + 16 * ((4 * dq_blk + 0) ^ sw)) = (u32x4){lo[0][0], lo[0][1], lo[1][0], lo[1][1]};
-        *(u32x4 *)(rp + 16 * ((4 * dq_blk + 1) ^ sw)) = (u32x4){lo[2][0], lo[2][1], lo[3][0], lo[3][1]};
-        *(u32x4 *)(rp + 16 * ((4 * dq_blk + 2) ^ sw)) = (u32x4){hi[0][0], hi[0][1], hi[1][0], hi[1][1]};
-        *(u32x4 *)(rp + 16 * ((4 * dq_blk + 3) ^ sw)) = (u32x4){hi[2][0], hi[2][1], hi[3][0], hi[3][1]};
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+            uint32_t lo[2][2], hi[2][2];
+            q4_unpack_row(codes[2 * h2], d2, lo[0], hi[0]);
+            q4_unpack_row(codes[2 * h2 + 1], d2, lo[1], hi[1]);
+            *(u32x4 *)(rp + 16 * ((4 * dq_blk + h2) ^ sw)) = (u32x4){lo[0][0], lo[0][1], lo[1][0], lo[1][1]};
+            *(u32x4 *)(rp + 16 * ((4 * dq_blk + 2 + h2) ^ sw)) = (u32x4){hi[0][0], hi[0][1], hi[1][0], hi[1][1]};
+        }
     };
     auto dequant_k = [&](int tl) INL {
         if (D == 128 || wave < 2)
@@ -966,6 +969,30 @@ __global__ __launch_bounds__(kNT, 1) void prefill16_kernel(Prefill16Params p)
         if constexpr (Q4)
             rit = raw_it(n, sk4, sv2);                   // (LK = 4, LV = 2 here)
         u32x4 fb[kRead + 1];
+        // Both caches q4_0 at D = 128: K(n+2) and V(n) are dequantized inside half 2, the raw
+        // blocks read in slot NM + 4 and K's and V's f16 rows written in slots NM + 14 and
+        // NM + 26 (into the stages of K(n) and V(n-2), read in iteration n-1; the raw tiles
+        // landed before the barrier). Timed on an MI355X against the end of the tile and four
+        // other placements: 1.8-1.9 % faster at 2K x 16K, 3-4 % for 256 queries; half 1 was
+        // slower, and with one q4_0 cache the end of the tile stays (0.6 % faster there).
+        constexpr bool DQS = Q4 && D == 128;
+        constexpr int DQL = NM + 4, DQK = NM + 14, DQV = NM + 26;
+        RawBlock dqk{}, dqv{};
+        auto dq_at = [&](auto sl_) INL {
+            constexpr int sl = decltype(sl_)::value;
+            if constexpr (DQS) {
+                if constexpr (sl == DQL) {
+                    if constexpr (QK)
+                        dqk = dq_load(rawk(n + 2));
+                    if constexpr (QV)
+                        dqv = dq_load(rawv(n));
+                }
+                if constexpr (QK && sl == DQK)
+                    dq_store(dqk, kstage(n + 2), false);
+                if constexpr (QV && sl == DQV)
+                    dq_store(dqv, vstage(n), true);
+            }
+        };
         auto units = [&](auto sc_) INL {          // the softmax units of slot sc_
             constexpr int sl = decltype(sc_)::value;
             static_for<PL::sc.first[sl], PL::sc.first[sl + 1]>([&](auto ic) INL {
@@ -988,6 +1015,7 @@ __global__ __launch_bounds__(kNT, 1) void prefill16_kernel(Prefill16Params p)
                 mask(1, s1c, n);
             }
             units(ic);
+            dq_at(ic);
             if constexpr (FAST16 && kDmaMode == 2 && (i & 3) == 1 && (i >> 2) < G::NDMA)
                 dma_fast(n, i >> 2, sk4, sv2);        // K(n+LK)
             __builtin_amdgcn_sched_barrier(0);
@@ -1000,6 +1028,7 @@ __global__ __launch_bounds__(kNT, 1) void prefill16_kernel(Prefill16Params p)
                 fb[(f + kRead) % (kRead + 1)] = kread(ks, f + kRead);
             s_slot(i, fb[f % (kRead + 1)], s0, s1n);
             units(std::integral_constant<int, NM + i>{});
+            dq_at(std::integral_constant<int, NM + i>{});
             if constexpr (Q4) {
                 if constexpr ((i & 3) == 1 && (i >> 2) < QR::NIW)
                     dma_q4(rit, i >> 2);
@@ -1022,7 +1051,7 @@ __global__ __launch_bounds__(kNT, 1) void prefill16_kernel(Prefill16Params p)
         // the first of the new (half 1 of the next tile)
         apply_rescale(0);
         apply_rescale(1);
-        if constexpr (ANYQ) {
+        if constexpr (ANYQ && !DQS) {
             // K(n+2) and V(n) into the stages of K(n) and V(n-2), read in iteration n-1 (at the
             // end of the tile, where the last score MFMAs are still executing)
             __builtin_amdgcn_sched_barrier(0);
