@@ -206,6 +206,31 @@ def draw_f32(w: Workload, seed: Optional[int] = None):
     return q, k, v
 
 
+def normal_f16(shape, seed: int, chunk: int = 1 << 26) -> np.ndarray:
+    """N(0,1) values rounded to float16, drawn in float32 chunks from numpy's PCG64 (for caches
+    too large to hold in float32 at once)."""
+    rng = np.random.default_rng(seed)
+    out = np.empty(int(np.prod(shape)), np.float16)
+    for s in range(0, out.size, chunk):
+        n = min(chunk, out.size - s)
+        out[s:s + n] = rng.standard_normal(n, dtype=np.float32)
+    return out.reshape(shape)
+
+
+def random_q4_0(n_blocks: int, seed: int) -> np.ndarray:
+    """q4_0 blocks [n_blocks, 18] for caches too large to quantize: uniform random 4-bit codes
+    and scales d = f16 of U(0.25, 0.4), the range max|x|/8 takes for 32 N(0,1) values."""
+    rng = np.random.default_rng(seed)
+    out = np.empty((n_blocks, Q4_0_BYTES), np.uint8)
+    step = 1 << 24
+    for s in range(0, n_blocks, step):
+        n = min(step, n_blocks - s)
+        d = rng.uniform(0.25, 0.4, n).astype(np.float16)
+        out[s:s + n, :2] = d.view(np.uint8).reshape(n, 2)
+        out[s:s + n, 2:] = rng.integers(0, 256, (n, 16), dtype=np.uint8)
+    return out
+
+
 def generate(w: Workload, seed: Optional[int] = None) -> Inputs:
     q, k, v = draw_f32(w, seed)
     return Inputs(w, encode(q, w.q_dtype), encode(k, w.kv), encode(v, w.kv))
