@@ -41,10 +41,44 @@ def test_f16_cache_beyond_4gib():
     qpd = torch.from_numpy(qp).cuda()
     pre = fa.prefill(qpd, kd, vd, causal=True, offset=Sk - Sq, scale=scale)
     spl = fa.prefill_split(qpd, kd, vd, causal=True, offset=Sk - Sq, scale=scale)
+    # the same bytes as a pool of 64-key pages, dealt to the two sequences in shuffled order
+    # (the paged prefill takes 4096 of them per sequence, its documented limit, from anywhere
+    # in the pool)
+    n_pages = B * Sk // 64
+    half = n_pages // 2
+    table = np.random.default_rng(208).permutation(n_pages).astype(np.int32)
+    table = np.ascontiguousarray(table[:2 * half].reshape(2, half))
+    lens = np.array([64 * half - 5, 64 * half - 37], np.int32)
+    tpre = np.ascontiguousarray(table[:, :4096])
+    lpre = np.array([64 * 4096 - 5, 64 * 4096 - 37], np.int32)
+    pk = kd.reshape(-1)[:n_pages * 64 * Hkv * D].view(n_pages, 64, Hkv, D)
+    pv = vd.reshape(-1)[:n_pages * 64 * Hkv * D].view(n_pages, 64, Hkv, D)
+    tab_d, lens_d = torch.from_numpy(table).cuda(), torch.from_numpy(lens).cuda()
+    pdec = fa.decode_paged(torch.from_numpy(qd).cuda(), pk, pv, tab_d, lens_d, causal=True,
+                           scale=scale)
+    ppre = fa.prefill_paged(qpd, pk, pv, torch.from_numpy(tpre).cuda(),
+                            torch.from_numpy(lpre).cuda(), causal=True, scale=scale)
     torch.cuda.synchronize()
     dec, pre, spl = to_host(dec), to_host(pre), to_host(spl)
-    del kd, vd
+    pdec, ppre = to_host(pdec), to_host(ppre)
+    del kd, vd, pk, pv
     rows = [i * Hq + h for i in (0, Sq - 1) for h in (0, 13, 31)]
+    hk = k.reshape(-1)[:n_pages * 64 * Hkv * D].reshape(n_pages, 64, Hkv, D)
+    hv = v.reshape(-1)[:n_pages * 64 * Hkv * D].reshape(n_pages, 64, Hkv, D)
+    for b in range(B):
+        n = int(lens[b])
+        kb = hk[table[b]].reshape(-1, Hkv, D)[None, :n]
+        vb = hv[table[b]].reshape(-1, Hkv, D)[None, :n]
+        ref = oracle.attention(qd[b:b + 1], kb, vb, q_dtype="f16", kv_dtype="f16", causal=True,
+                               offset=n - 1, scale=scale)
+        _check(f"paged decode sequence {b}", pdec[b:b + 1], ref, TOL["f16"])
+        n = int(lpre[b])
+        kb = hk[tpre[b]].reshape(-1, Hkv, D)[None, :n]
+        vb = hv[tpre[b]].reshape(-1, Hkv, D)[None, :n]
+        ref = oracle.attention(qp[b:b + 1], kb, vb, q_dtype="f16", kv_dtype="f16", causal=True,
+                               offset=n - Sq, scale=scale, rows=rows)
+        _check(f"paged prefill sequence {b}", ppre[b].reshape(Sq * Hq, D)[rows], ref, TOL["f16"])
+        del kb, vb
     for b in range(B):
         ref = oracle.attention(qd[b:b + 1], k[b:b + 1], v[b:b + 1], q_dtype="f16",
                                kv_dtype="f16", causal=True, offset=Sk - 1, scale=scale)
