@@ -207,23 +207,28 @@ int orc_quantize_q4_0(const void *x, int x_dtype, int64_t n_blocks, uint8_t *blo
     return ORC_OK;
 }
 
-/* Widen `rows` rows of D elements stored as `dtype` into a new f32 buffer. */
+/* Widen `rows` rows of D elements stored as `dtype` into a new f32 buffer. Every element is
+ * widened on its own, so splitting the loop over threads changes no value. */
 static float *upcast_rows(const void *src, int dtype, int64_t rows, int D)
 {
     float *dst = (float *)malloc(sizeof(float) * (size_t)rows * (size_t)D);
     if (!dst)
         return NULL;
+    const int64_t n = rows * D;
     if (dtype == ORC_F16) {
         const uint16_t *s = (const uint16_t *)src;
-        for (int64_t i = 0; i < rows * D; ++i)
+#pragma omp parallel for schedule(static)
+        for (int64_t i = 0; i < n; ++i)
             dst[i] = half_bits_to_float(s[i]);
     } else if (dtype == ORC_BF16) {
         const uint16_t *s = (const uint16_t *)src;
-        for (int64_t i = 0; i < rows * D; ++i)
+#pragma omp parallel for schedule(static)
+        for (int64_t i = 0; i < n; ++i)
             dst[i] = bf16_bits_to_float(s[i]);
     } else {
         const uint8_t *s = (const uint8_t *)src;
         const int nb = D / 32;
+#pragma omp parallel for schedule(static)
         for (int64_t r = 0; r < rows; ++r)
             for (int b = 0; b < nb; ++b)
                 q4_0_block_to_float(s + (r * nb + b) * 18, dst + r * D + 32 * b);
