@@ -1264,6 +1264,95 @@ __global__ __launch_bounds__(256) void decode_merge4_kernel(DecodeParams p)
         op[lane] = (uint16_t)(pack2<BF>(o[0] * inv, 0.0f) & 0xFFFFu);
 }
 
+// 65 to 16 NW splits: NW waves per (b, KV head, row), wave w holding splits w, w + NW, ...
+// (16 per lane), so every split's row is again loaded in one round. A wave combines its own
+// splits against its own largest frame (lanes 0..15 hold their frames and sums); the waves'
+// partial rows, frames and sums then meet in LDS and are combined the same way (log-sum-exp
+// of the waves' states, the merge applied twice).
+template <int D, bool BF, int NW>
+__global__ __launch_bounds__(64 * NW) void decode_mergew_kernel(DecodeParams p)
+{
+    constexpr int E = D / 64;
+    __shared__ float part[NW][D];
+    __shared__ float wfl[NW][2];
+    const AttnArgs &a = p.a;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    int rest = blockIdx.x;
+    const int rr = rest % p.rows;
+    rest /= p.rows;
+    const int kvh = rest % a.Hkv;
+    const int b = rest / a.Hkv;
+    const int stride = p.rows * (D + 2);
+    const float *base = p.part + ((int64_t)b * a.Hkv + kvh) * p.n_split * stride + rr * (D + 2);
+    const int ns = p.n_split;
+    const int su = wave + NW * min(lane, 15);        // lane u < 16: split wave + NW u
+    const bool on = lane < 16 && su < ns;
+    const f32x2 fl = *(const f32x2 *)(base + (int64_t)min(su, ns - 1) * stride + D);
+    float x[16][E];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+        const float *src = base + (int64_t)min(wave + NW * u, ns - 1) * stride + E * lane;
+        if constexpr (E == 2) {
+            const f32x2 v2 = *(const f32x2 *)src;
+            x[u][0] = v2[0];
+            x[u][1] = v2[1];
+        } else {
+            x[u][0] = *src;
+        }
+    }
+    const float f = on ? fl[0] : -INFINITY;
+    const float Fw = wave_max(f);
+    const float w = (Fw == -INFINITY || !on) ? 0.0f : exp2_fast(f - Fw);
+    const float Lw = wave_sum(w * (on ? fl[1] : 0.0f));
+    float o[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+        o[e] = 0.0f;
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+        const float wu = __builtin_bit_cast(
+            float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), u));
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+            o[e] += wu * x[u][e];
+    }
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+        part[wave][E * lane + e] = o[e];
+    if (lane == 0) {
+        wfl[wave][0] = Fw;
+        wfl[wave][1] = Lw;
+    }
+    __syncthreads();
+    if (wave > 0)
+        return;
+    float F = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < NW; ++v)
+        F = fmaxf(F, wfl[v][0]);
+    float L = 0.0f;
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+        o[e] = 0.0f;
+#pragma unroll
+    for (int v = 0; v < NW; ++v) {
+        const float c = (F == -INFINITY || wfl[v][0] == -INFINITY) ? 0.0f
+                                                                    : exp2_fast(wfl[v][0] - F);
+        L += c * wfl[v][1];
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+            o[e] += c * part[v][E * lane + e];
+    }
+    const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+    const int qi = rr / a.G, hl = rr % a.G;
+    uint16_t *op = (uint16_t *)a.o + (((int64_t)b * a.Sq + qi) * a.Hq + kvh * a.G + hl) * D;
+    if constexpr (E == 2)
+        *(uint32_t *)(op + 2 * lane) = pack2<BF>(o[0] * inv, o[1] * inv);
+    else
+        op[lane] = (uint16_t)(pack2<BF>(o[0] * inv, 0.0f) & 0xFFFFu);
+}
+
 template <int D, int KV>
 hipError_t launch(const DecodeParams &p, int64_t n_wg, hipStream_t stream)
 {
@@ -1293,6 +1382,12 @@ hipError_t launch(const DecodeParams &p, int64_t n_wg, hipStream_t stream)
     if (p.n_split <= 64)
         hipLaunchKernelGGL((decode_merge4_kernel<D, KV == KV_BF16>), dim3((unsigned)n_rows),
                            dim3(256), 0, stream, p);
+    else if (p.n_split <= 128)
+        hipLaunchKernelGGL((decode_mergew_kernel<D, KV == KV_BF16, 8>), dim3((unsigned)n_rows),
+                           dim3(512), 0, stream, p);
+    else if (p.n_split <= 256)
+        hipLaunchKernelGGL((decode_mergew_kernel<D, KV == KV_BF16, 16>), dim3((unsigned)n_rows),
+                           dim3(1024), 0, stream, p);
     else
         hipLaunchKernelGGL((decode_merge_kernel<D, KV == KV_BF16>), dim3((unsigned)n_rows),
                            dim3(64), 0, stream, p);

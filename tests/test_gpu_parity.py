@@ -321,11 +321,18 @@ DECODE = [
     wl("decode_q4_0_mha_noncausal", 1, 4, 4, 1, 130, 128, "q4_0", False, 0, seed=53),
     wl("decode_q4_0_sq4_g1", 1, 2, 2, 4, 700, 128, "q4_0", True, 690, seed=54),
     wl("decode_q4_0_before_keys", 1, 8, 2, 1, 300, 128, "q4_0", True, -5, seed=55),
-    # one KV head: more than 64 splits, the merge kernel's looped path
+    # one KV head, 157 splits: the 16-wave merge (129-256 splits)
     wl("decode_many_splits", 1, 4, 1, 1, 10000, 128, "f16", True, 9999, seed=56),
-    # head-group q4_0 kernel with 157 splits per head group: the merge kernel's looped path
-    # behind that kernel, ragged last split
+    # head-group q4_0 kernel with 157 splits per head group: the 16-wave merge behind that
+    # kernel, ragged last split
     wl("decode_q4_0_many_splits", 1, 32, 8, 1, 20000, 128, "q4_0", True, 19999, seed=57),
+    # 125 splits: the 8-wave merge (65-128 splits); bf16 the same way
+    wl("decode_merge8_f16", 1, 8, 4, 1, 8000, 128, "f16", True, 7999, seed=59),
+    wl("decode_merge8_bf16", 1, 8, 4, 1, 8000, 128, "bf16", True, 7999, seed=60),
+    # 141 splits of 8 rows at D = 64 (one element per lane in the merge)
+    wl("decode_merge16_d64_sq2", 1, 8, 2, 2, 9000, 64, "f16", True, 8998, seed=62),
+    # 512 splits: the looped merge (more than 256 splits)
+    wl("decode_merge_looped_d64", 1, 4, 1, 1, 40000, 64, "f16", True, 39999, seed=63),
     # 1100 head groups of one split each (a large batch of short sequences), D = 64
     wl("decode_q4_0_large_batch", 1100, 16, 4, 1, 100, 64, "q4_0", True, 99, seed=58),
 ]
