@@ -459,6 +459,16 @@ def main():
     leg("decode_f16_standard")(lambda: fa.standard_attention(
         dq, dkf, dvf, causal=True, offset=wd.causal_offset, scale=wd.scale, out=do7,
         workspace=std_ws, stream=stream))
+    # one sequence of the decode cache (a batch-1 step): its key ranges fill the chip by
+    # themselves, 256 per head group, so the merge combines more than 64 splits per row
+    dq1, dk1, dv1 = dq[:1], dk[:1], dv[:1]
+    ws1 = torch.empty(max(fa.decode_workspace_bytes(1, wd.Hq, wd.Hkv, wd.Sq, wd.Sk, wd.D), 16),
+                      dtype=torch.uint8, device=dev)
+    do8 = torch.empty_like(dq1)
+    b1bytes = dk1.numel() + dv1.numel() + 2 * dq1.numel() * 2
+    leg("decode_q4_0_b1")(lambda: fa.decode(dq1, dk1, dv1, causal=True, offset=wd.causal_offset,
+                                            scale=wd.scale, out=do8, workspace=ws1,
+                                            stream=stream))
     w64 = wp.with_(D=64)
     x64 = W.generate(w64)
     q64, k64, v64 = to_dev(x64.q, "f16"), to_dev(x64.k, "f16"), to_dev(x64.v, "f16")
@@ -666,6 +676,10 @@ def main():
                               what="4 x 1 query against 32768 keys, f16 K and V (split + merge)"),
         "decode_f16_standard": hbm_leg(fbytes, "decode_f16_standard",
                                        what="fa_standard_attention on the f16 decode shape"),
+        "decode_q4_0_b1": hbm_leg(b1bytes, "decode_q4_0_b1",
+                                  what="1 x 1 query against 32768 q4_0 keys (the decode "
+                                       "workload's first sequence: 256 key ranges per head "
+                                       "group, merged by the 16-wave merge)"),
         "quantize_q4_0": hbm_leg(wbytes, "quantize_q4_0",
                                  what="fa_quantize_q4_0 of f16 K and V [1, 16384, 8, 128] (two "
                                       "launches)"),
