@@ -288,8 +288,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--calibrate-copy", action="store_true")
-    # leave out the prefill sweep, whose f16 legs run the headline prefill's kernel at other
-    # sizes: a kernel-trace profile of the run then averages only the headline launches
+    # leave out the prefill sweep and the batch-1 decode, which run the headline kernels at
+    # other sizes: a kernel-trace profile of the run then averages only the headline launches
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--gate", action="store_true",
                     help="exit with status 1 if the prefill or decode falls below its floor")
@@ -460,15 +460,18 @@ def main():
         dq, dkf, dvf, causal=True, offset=wd.causal_offset, scale=wd.scale, out=do7,
         workspace=std_ws, stream=stream))
     # one sequence of the decode cache (a batch-1 step): its key ranges fill the chip by
-    # themselves, 256 per head group, so the merge combines more than 64 splits per row
+    # themselves, 256 per head group, so the merge combines more than 64 splits per row. A
+    # sweep leg (the same kernels at another grid, kept out of the --no-sweep runs that the
+    # per-kernel profiles average)
     dq1, dk1, dv1 = dq[:1], dk[:1], dv[:1]
-    ws1 = torch.empty(max(fa.decode_workspace_bytes(1, wd.Hq, wd.Hkv, wd.Sq, wd.Sk, wd.D), 16),
-                      dtype=torch.uint8, device=dev)
-    do8 = torch.empty_like(dq1)
     b1bytes = dk1.numel() + dv1.numel() + 2 * dq1.numel() * 2
-    leg("decode_q4_0_b1")(lambda: fa.decode(dq1, dk1, dv1, causal=True, offset=wd.causal_offset,
-                                            scale=wd.scale, out=do8, workspace=ws1,
-                                            stream=stream))
+    if not args.no_sweep:
+        ws1 = torch.empty(max(fa.decode_workspace_bytes(1, wd.Hq, wd.Hkv, wd.Sq, wd.Sk, wd.D),
+                              16), dtype=torch.uint8, device=dev)
+        do8 = torch.empty_like(dq1)
+        leg("decode_q4_0_b1")(lambda: fa.decode(dq1, dk1, dv1, causal=True,
+                                                offset=wd.causal_offset, scale=wd.scale,
+                                                out=do8, workspace=ws1, stream=stream))
     w64 = wp.with_(D=64)
     x64 = W.generate(w64)
     q64, k64, v64 = to_dev(x64.q, "f16"), to_dev(x64.k, "f16"), to_dev(x64.v, "f16")
@@ -676,10 +679,10 @@ def main():
                               what="4 x 1 query against 32768 keys, f16 K and V (split + merge)"),
         "decode_f16_standard": hbm_leg(fbytes, "decode_f16_standard",
                                        what="fa_standard_attention on the f16 decode shape"),
-        "decode_q4_0_b1": hbm_leg(b1bytes, "decode_q4_0_b1",
-                                  what="1 x 1 query against 32768 q4_0 keys (the decode "
-                                       "workload's first sequence: 256 key ranges per head "
-                                       "group, merged by the 16-wave merge)"),
+        "decode_q4_0_b1": None if args.no_sweep else hbm_leg(
+            b1bytes, "decode_q4_0_b1",
+            what="1 x 1 query against 32768 q4_0 keys (the decode workload's first sequence: "
+                 "256 key ranges per head group, merged by the 16-wave merge)"),
         "quantize_q4_0": hbm_leg(wbytes, "quantize_q4_0",
                                  what="fa_quantize_q4_0 of f16 K and V [1, 16384, 8, 128] (two "
                                       "launches)"),
