@@ -1471,7 +1471,12 @@ constexpr int kSplitBias = 3;
 // kCUs CUs in one round (parts = kCUs / units), merged by a second kernel. Timed on an MI355X at
 // 8-128 units and 2K-16K keys against runs sized for two or four rounds (512 or 1024
 // workgroups): one round was fastest at every shape (e.g. 1024 queries x 16K keys: 267 us
-// against 278 and 307; 64 queries: 78 against 130). With more units than that, pairing.
+// against 278 and 307; 64 queries: 78 against 130). With more units than that and at most
+// kCUs, pairing. With more than kCUs units the workgroups run in several rounds, and the
+// hardware's dispatch of the later rounds onto the CUs that free up (heaviest units first)
+// already evens the load: nothing is paired. Timed on an MI355X against pairing there: 4096
+// queries x 4096 keys 143 against 163 us, 3072 x 3072 94 against 120, two sequences of
+// 2048 x 2048 83 against 105, 8192 x 8192 508 against 544.
 constexpr int64_t kCUs = 256;          // compute units of the gfx950 part (MI355X)
 constexpr int64_t kMinRunTiles = 4;
 constexpr int64_t kMaxParts = 64;
@@ -1535,7 +1540,7 @@ PrefillSplit prefill_split_plan(const AttnArgs &a0)
             return finish(sp);
         }
     }
-    if (!a.causal)
+    if (!a.causal || n_units > kCUs)
         return finish(sp);
     int64_t total = 0;
     for (int q = 0; q < g.n_qblk; ++q)

@@ -100,7 +100,9 @@ int fa_prefill(const void *q, const void *k, const void *v, void *o,
  * its mirror block n-1-q, a light unit, runs the remaining tiles after its own unit. The grid
  * stays one workgroup per unit. The later of a split unit's two parts to finish merges them
  * (log-sum-exp of the two partial softmax states) and writes the unit's rows. No workgroup
- * waits for another.
+ * waits for another. Pairing applies up to 256 units (one workgroup per CU); with more, the
+ * workgroups run in several rounds whose dispatch onto the CUs that free up already evens the
+ * load, and nothing is paired.
  * With at most 128 units, half the 256 CUs (a short chunk of queries against many keys, or a
  * small batch), most CUs would idle while each unit's workgroup runs all of its tiles, so
  * instead every unit's tiles are cut into runs of at least 4 tiles, as many runs per unit as

@@ -749,6 +749,30 @@ def test_prefill_split_matches_oracle(w):
             w.name)
 
 
+# more than 256 units (several rounds of workgroups): nothing is paired, so fa_prefill_split
+# is fa_prefill (with a q4_0 cache of 16+ query blocks per KV head, on its f16 copy): the same
+# bits, and sampled rows against the oracle
+SPLIT_ROUNDS = [wl("rounds_4k_f16", 1, 32, 8, 4096, 4096, 128, "f16", True, 0, seed=117),
+                wl("rounds_b2_q4_0", 2, 32, 8, 2048, 2048, 128, "q4_0", True, 0, seed=118)]
+
+
+@pytest.mark.parametrize("w", SPLIT_ROUNDS, ids=[w.name for w in SPLIT_ROUNDS])
+def test_prefill_split_several_rounds(w):
+    say(f"prefill_split {w}")
+    nbytes = fa.fa_prefill_workspace_bytes(w.B, w.Hq, w.Hkv, w.Sq, w.Sk, w.D, int(w.causal),
+                                           w.causal_offset, w.kv_code)
+    deq = (w.B * w.Sk * w.Hkv * w.D * 2 * 2) if w.kv == "q4_0" else 0
+    assert nbytes == (0 if deq == 0 else 4096 + deq), nbytes      # counters and copies only
+    x = W.generate(w)
+    q, k, v = device_inputs(w, x)
+    plain = fa.prefill(q, k, v, causal=True, offset=w.causal_offset, scale=w.scale)
+    split = fa.prefill_split(q, k, v, causal=True, offset=w.causal_offset, scale=w.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(plain.view(torch.int16), split.view(torch.int16))
+    rows = np.random.default_rng(w.seed).choice(w.B * w.Sq * w.Hq, 512, replace=False)
+    compare(w, to_host(split).reshape(-1, w.D)[rows], oracle_out(w, x, rows=rows), w.name)
+
+
 # key split (at most 128 units): a short chunk of queries against many keys; every unit's
 # tiles are cut into runs of their own workgroups and a merge kernel combines them
 SPLIT_PARTS = [
