@@ -333,6 +333,11 @@ DECODE = [
     wl("decode_merge16_d64_sq2", 1, 8, 2, 2, 9000, 64, "f16", True, 8998, seed=62),
     # 512 splits: the looped merge (more than 256 splits)
     wl("decode_merge_looped_d64", 1, 4, 1, 1, 40000, 64, "f16", True, 39999, seed=63),
+    # 5-16 rows per KV head (the q4_0 kernel that dequantizes into f16 tiles): GQA 8 (8 rows),
+    # 4 queries of GQA 4 (16 rows), 3 queries of GQA 4 (12 rows, ragged causal)
+    wl("decode_q4_0_g8", 2, 64, 8, 1, 5000, 128, "q4_0", True, 4999, seed=64),
+    wl("decode_q4_0_sq4_g4", 2, 32, 8, 4, 3000, 128, "q4_0", True, 2996, seed=65),
+    wl("decode_q4_0_sq3_g4_d64", 1, 16, 4, 3, 2100, 64, "q4_0", True, 2050, seed=66),
     # 1100 head groups of one split each (a large batch of short sequences), D = 64
     wl("decode_q4_0_large_batch", 1100, 16, 4, 1, 100, 64, "q4_0", True, 99, seed=58),
 ]
