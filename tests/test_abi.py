@@ -147,13 +147,19 @@ def test_prefill_workspace_bytes():
     assert fa.fa_prefill_workspace_bytes(1, 32, 8, 2048, 16384, 128, 0, 0, 0) == 0
     assert fa.fa_prefill_workspace_bytes(1, 2, 2, 128, 128, 64, 1, 0, 0) == 0
     assert fa.fa_prefill_workspace_bytes(0, 32, 8, 2048, 16384, 128, 1, 14336, 0) == 0
-    # more split units than the 4096 counter bytes hold (64 sequences x 8 KV heads x 12
-    # blocks = 6144): no split, the call is fa_prefill
+    # more than 256 units (one workgroup per CU): the workgroups run in several rounds, whose
+    # dispatch already evens the load, and nothing is paired (the call is fa_prefill); a q4_0
+    # cache of 16+ query blocks per KV head is still copied first. 10 or 64 sequences of the
+    # 2048-query chunk (2560, 16384 units), 4096 x 4096 keys (512 units)
+    assert fa.fa_prefill_workspace_bytes(10, 32, 8, 2048, 16384, 128, 1, 14336, 0) == 0
     assert fa.fa_prefill_workspace_bytes(64, 32, 8, 2048, 16384, 128, 1, 14336, 0) == 0
     assert fa.fa_prefill_workspace_bytes(64, 32, 8, 2048, 16384, 128, 1, 14336, 2) == \
         4096 + 2 * 64 * copy
-    assert fa.fa_prefill_workspace_bytes(10, 32, 8, 2048, 16384, 128, 1, 14336, 0) == \
-        4096 + 960 * 2 * 4 * 64 * 132 * 4
+    assert fa.fa_prefill_workspace_bytes(1, 32, 8, 4096, 4096, 128, 1, 0, 0) == 0
+    assert fa.fa_prefill_workspace_bytes(1, 32, 8, 4096, 4096, 128, 1, 0, 2) == \
+        4096 + 2 * 4096 * 8 * 128 * 2
+    # 256 units (2048 x 2048, one round) are still paired
+    assert fa.fa_prefill_workspace_bytes(1, 32, 8, 2048, 2048, 128, 1, 0, 0) > 4096
     # invalid sizes give 0 too
     assert fa.fa_prefill_workspace_bytes(1, 30, 8, 2048, 16384, 128, 1, 14336, 0) == 0
     assert fa.fa_prefill_workspace_bytes(1, 32, 8, 2048, 16384, 96, 1, 14336, 0) == 0
