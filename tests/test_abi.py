@@ -214,6 +214,12 @@ def test_decode_workspace_bound():
     assert fa.fa_decode_workspace_bytes(4, 32, 8, 1, 0, 128) == 4 * 8 * 1 * 4 * 130 * 4
     assert fa.fa_decode_workspace_bytes(0, 32, 8, 1, 100, 128) == 0
     assert fa.fa_decode_workspace_bytes(1, 32, 8, 1, 100, 96) == 0
+    # one sequence fills the 512 workgroups alone: 256 splits per (b, KV head) of 2 tiles each
+    # (the 16-wave merge, 129-256 splits); two sequences 128 (the 8-wave merge); one KV head of
+    # a 16-bit cache at 40000 keys 512 (the looped merge)
+    assert fa.fa_decode_workspace_bytes(1, 32, 8, 1, 32768, 128) == 1 * 8 * 256 * 4 * 130 * 4
+    assert fa.fa_decode_workspace_bytes(2, 32, 8, 1, 32768, 128) == 2 * 8 * 128 * 4 * 130 * 4
+    assert fa.fa_decode_workspace_bytes(1, 4, 1, 1, 40000, 64) == 1 * 1 * 512 * 4 * 66 * 4
     # a workspace one byte short of the bound is refused for the largest causal offsets too
     for off in (4095, 100000):
         assert decode(workspace_bytes=fa.fa_decode_workspace_bytes(4, 32, 8, 1, 4096, 128) - 1,
